@@ -1,0 +1,274 @@
+"""ctypes binding of libaggemm.so: argument marshalling only.
+
+Every step of the operation runs in the library's HIP kernels; this module
+turns torch tensors into device pointers and sizes, passes the current
+stream, and raises on a non-zero status.  The library must have been built
+(``python -m communication_gemm_amd.build``); importing this module without
+it fails loudly, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libaggemm.so")
+
+AGG_OK, AGG_E_INVALID, AGG_E_UNSUPPORTED, AGG_E_NOMEM, AGG_E_HIP, AGG_E_TIMEOUT = range(6)
+MODE_PIPELINED, MODE_COMPUTE_ONLY, MODE_SEQUENTIAL, MODE_COPY_ONLY = range(4)
+LINKS_PARALLEL, LINKS_SERIAL = range(2)
+MAX_SHARDS = 64
+
+
+class AggError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class Options(ctypes.Structure):
+    """Mirror of ``struct agg_options`` in include/aggemm.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("local_shard", ctypes.c_int),
+        ("send_order", ctypes.POINTER(ctypes.c_int)),
+        ("mode", ctypes.c_int),
+        ("link_gbps", ctypes.c_double),
+        ("link_model", ctypes.c_int),
+        ("producer_wgs", ctypes.c_int),
+        ("consumer_wgs", ctypes.c_int),
+        ("tile", ctypes.c_int),
+        ("acc_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("timeout_ms", ctypes.c_double),
+        ("debug_drop_chunk", ctypes.c_int),
+        ("consumer_events", ctypes.c_void_p * 2),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``struct agg_plan_info``."""
+
+    _fields_ = [
+        ("shard_rows", ctypes.c_int64),
+        ("chunk_rows", ctypes.c_int),
+        ("chunks_per_source", ctypes.c_int),
+        ("tile_m", ctypes.c_int),
+        ("tile_n", ctypes.c_int),
+        ("m_tiles_per_shard", ctypes.c_int),
+        ("n_tiles", ctypes.c_int),
+        ("total_tiles", ctypes.c_int64),
+        ("total_chunks", ctypes.c_int64),
+        ("consumer_wgs", ctypes.c_int),
+        ("producer_wgs", ctypes.c_int),
+    ]
+
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "ag_gemm_options_init": (None, [ctypes.POINTER(Options)]),
+    "ag_gemm_f16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]),
+    "ag_gemm_f16_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.POINTER(Options)]),
+    "ag_gemm_i8_dequant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int, ctypes.c_void_p]),
+    "ag_gemm_i8_dequant_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.POINTER(Options)]),
+    "ag_gemm_pick_chunk_rows": (ctypes.c_int, [ctypes.c_int64]),
+    "ag_gemm_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_int]),
+    "ag_gemm_workspace_reset": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t,
+                                               ctypes.c_void_p]),
+    "ag_gemm_check": (ctypes.c_int, [ctypes.c_void_p]),
+    "ag_gemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ag_gemm_release": (None, []),
+    "ag_gemm_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.POINTER(Options), ctypes.c_int,
+                                    ctypes.POINTER(PlanInfo), ctypes.c_void_p,
+                                    ctypes.c_void_p]),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m communication_gemm_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.ag_gemm_status_string(int(status)).decode()
+
+
+def _raise(status: int, what: str):
+    if status:
+        raise AggError(status, what)
+
+
+def options(**kw) -> Options:
+    """An agg_options with the library's defaults, then ``kw`` applied.
+
+    ``send_order`` may be a sequence of ints; ``consumer_events`` a pair of
+    torch.cuda.Event objects; ``acc_out``/``workspace`` torch tensors.
+    """
+    o = Options()
+    lib.ag_gemm_options_init(ctypes.byref(o))
+    keep = []
+    for k, v in kw.items():
+        if v is None:
+            continue
+        if k == "send_order":
+            arr = (ctypes.c_int * len(v))(*[int(x) for x in v])
+            keep.append(arr)
+            o.send_order = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int))
+        elif k == "consumer_events":
+            o.consumer_events[0] = ctypes.c_void_p(v[0].cuda_event)
+            o.consumer_events[1] = ctypes.c_void_p(v[1].cuda_event)
+        elif k in ("acc_out", "workspace"):
+            setattr(o, k, v.data_ptr() if hasattr(v, "data_ptr") else int(v))
+            if k == "workspace" and hasattr(v, "numel"):
+                o.workspace_bytes = v.numel() * v.element_size()
+        else:
+            setattr(o, k, v)
+    o._keep = keep   # keep ctypes arrays alive with the struct
+    return o
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _shard_ptrs(shards, dtype, K):
+    import torch
+    if not shards:
+        raise ValueError("need at least one shard")
+    if len(shards) > MAX_SHARDS:
+        raise ValueError(f"at most {MAX_SHARDS} shards")
+    S = shards[0].shape[0]
+    for t in shards:
+        if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"shards must be contiguous 2-D {dtype} CUDA tensors")
+        if tuple(t.shape) != (S, K):
+            raise ValueError("all shards must be S x K")
+    return (ctypes.c_void_p * len(shards))(*[t.data_ptr() for t in shards]), S
+
+
+def _check_out(C, shape, dtype):
+    if C.dtype != dtype or not C.is_cuda or not C.is_contiguous() or tuple(C.shape) != shape:
+        raise ValueError(f"output must be a contiguous {dtype} CUDA tensor of shape {shape}")
+
+
+def ag_gemm_f16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None):
+    """C[M, N] (fp32) = concat(shards)[M, K] (fp16) x B[K, N] (fp16)."""
+    import torch
+    if B.dtype != torch.float16 or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
+        raise ValueError("B must be a contiguous 2-D fp16 CUDA tensor")
+    K, N = B.shape
+    table, S = _shard_ptrs(shards, torch.float16, K)
+    M = S * len(shards)
+    _check_out(C, (M, N), torch.float32)
+    st = _stream_handle(stream)
+    if opts is None:
+        rc = lib.ag_gemm_f16(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
+                             int(chunk_rows), st)
+    else:
+        rc = lib.ag_gemm_f16_ex(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
+                                int(chunk_rows), st, ctypes.byref(opts))
+    _raise(rc, "ag_gemm_f16")
+    return C
+
+
+def ag_gemm_i8_dequant(shards, B, bias, scale, C, chunk_rows: int = 0, stream=None,
+                       opts: Options | None = None):
+    """C[M, N] (fp16) = fp16(fp32(concat(shards) x B + bias) * scale)."""
+    import torch
+    if B.dtype != torch.int8 or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
+        raise ValueError("B must be a contiguous 2-D int8 CUDA tensor")
+    K, N = B.shape
+    table, S = _shard_ptrs(shards, torch.int8, K)
+    M = S * len(shards)
+    if bias.dtype != torch.int32 or tuple(bias.shape) != (N,) or not bias.is_cuda:
+        raise ValueError("bias must be an int32 CUDA tensor of shape (N,)")
+    if scale.dtype != torch.float32 or tuple(scale.shape) != (N,) or not scale.is_cuda:
+        raise ValueError("scale must be a float32 CUDA tensor of shape (N,)")
+    _check_out(C, (M, N), torch.float16)
+    st = _stream_handle(stream)
+    if opts is None:
+        rc = lib.ag_gemm_i8_dequant(table, len(shards), B.data_ptr(), bias.data_ptr(),
+                                    scale.data_ptr(), C.data_ptr(), M, K, N,
+                                    int(chunk_rows), st)
+    else:
+        rc = lib.ag_gemm_i8_dequant_ex(table, len(shards), B.data_ptr(), bias.data_ptr(),
+                                       scale.data_ptr(), C.data_ptr(), M, K, N,
+                                       int(chunk_rows), st, ctypes.byref(opts))
+    _raise(rc, "ag_gemm_i8_dequant")
+    return C
+
+
+def pick_chunk_rows(shard_rows: int) -> int:
+    return lib.ag_gemm_pick_chunk_rows(int(shard_rows))
+
+
+def workspace_bytes(n_shards: int, M: int, K: int, elt_bytes: int) -> int:
+    return lib.ag_gemm_workspace_bytes(int(n_shards), int(M), int(K), int(elt_bytes))
+
+
+def workspace_reset(ws, stream=None):
+    rc = lib.ag_gemm_workspace_reset(ctypes.c_void_p(ws.data_ptr()),
+                                     ws.numel() * ws.element_size(), _stream_handle(stream))
+    _raise(rc, "ag_gemm_workspace_reset")
+
+
+def check(stream=None) -> int:
+    """Synchronise and return the status of the calls since the last check."""
+    return lib.ag_gemm_check(_stream_handle(stream))
+
+
+def release():
+    lib.ag_gemm_release()
+
+
+def plan(kind: str, n_shards: int, M: int, K: int, N: int, chunk_rows: int = 0,
+         opts: Options | None = None, num_cus: int = 256, orders: bool = False):
+    """Host-only schedule query: (PlanInfo, tile_order or None, chunk_order or None)."""
+    import numpy as np
+    info = PlanInfo()
+    k = {"f16": 0, "i8": 1}[kind]
+    o = ctypes.byref(opts) if opts is not None else None
+    rc = lib.ag_gemm_plan(k, n_shards, M, K, N, chunk_rows, o, num_cus, ctypes.byref(info),
+                          None, None)
+    _raise(rc, "ag_gemm_plan")
+    if not orders:
+        return info, None, None
+    tiles = np.zeros((info.total_tiles, 4), np.int32)
+    chunks = np.zeros((max(info.total_chunks, 0), 2), np.int32)
+    rc = lib.ag_gemm_plan(k, n_shards, M, K, N, chunk_rows, o, num_cus, ctypes.byref(info),
+                          tiles.ctypes.data, chunks.ctypes.data if chunks.size else None)
+    _raise(rc, "ag_gemm_plan")
+    return info, tiles, chunks

@@ -1,0 +1,393 @@
+// api.cpp -- the C ABI: argument checks, per-device state (side stream,
+// events, workspace, counter bookkeeping) and the launch sequence of one
+// call (PTO-ISA AllGather+GEMM README: the host enqueues the communication
+// kernel and the compute kernel on two streams, then waits for both).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+
+#include "aggemm.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace agg {
+namespace {
+
+// Counter bookkeeping of one workspace: the value every counter holds once
+// all calls issued on it have finished, the last call's epoch and the last
+// epoch whose outcome ag_gemm_check() has reported.
+struct Track {
+    uint32_t base[kMaxShards];
+    uint32_t tickets;          // producer tickets handed out so far
+    uint32_t epoch;
+    uint32_t checked;
+    int device;
+};
+
+struct Device {
+    bool ready = false;
+    int num_cus = 0;
+    double clock_hz = 0;       // rate of the device's constant clock
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    char* ws = nullptr;        // internal workspace
+    size_t ws_bytes = 0;
+    Track track{};
+    int occ[2][4] = {{0}};
+};
+
+std::mutex g_mu;
+std::map<int, Device> g_dev;
+std::map<void*, Track> g_user_ws;   // caller-owned workspaces, by address
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int device_state(Device** out)
+{
+    int id = 0;
+    if (hipGetDevice(&id) != hipSuccess) return AGG_E_HIP;
+    Device& d = g_dev[id];
+    if (!d.ready) {
+        int cus = 0, khz = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess)
+            return AGG_E_HIP;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, id) != hipSuccess)
+            return AGG_E_HIP;
+        if (hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) != hipSuccess)
+            return AGG_E_HIP;
+        if (hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&d.join, hipEventDisableTiming) != hipSuccess)
+            return AGG_E_HIP;
+        d.num_cus = cus;
+        d.clock_hz = (khz > 0 ? khz : 100000) * 1000.0;
+        memset(&d.track, 0, sizeof d.track);
+        d.track.device = id;
+        d.ready = true;
+    }
+    *out = &d;
+    return AGG_OK;
+}
+
+int occupancy(Device& d, int kind, int tile)
+{
+    int& o = d.occ[kind][tile & 3];
+    if (!o) o = consumer_occupancy(kind, tile);
+    return o;
+}
+
+// The internal workspace, grown on demand.  Growing frees the old one,
+// which waits for work still using it.
+int internal_workspace(Device& d, size_t need, hipStream_t st, char** ws, Track** tr)
+{
+    if (d.ws_bytes < need) {
+        if (d.ws) {
+            if (hipDeviceSynchronize() != hipSuccess) return AGG_E_HIP;
+            (void)hipFree(d.ws);
+            d.ws = nullptr;
+            d.ws_bytes = 0;
+        }
+        size_t bytes = need + (need >> 3);   // some headroom against regrowth
+        if (hipMalloc(&d.ws, bytes) != hipSuccess) {
+            d.ws = nullptr;
+            (void)hipGetLastError();
+            return AGG_E_NOMEM;
+        }
+        d.ws_bytes = bytes;
+        if (launch_header_reset(reinterpret_cast<uint32_t*>(d.ws), st) != hipSuccess)
+            return AGG_E_HIP;
+        uint32_t keep = d.track.epoch;
+        memset(&d.track, 0, sizeof d.track);
+        d.track.epoch = keep;
+        d.track.checked = keep;
+    }
+    *ws = d.ws;
+    *tr = &d.track;
+    return AGG_OK;
+}
+
+struct Call {
+    Kind kind;
+    const void* const* shards;
+    int n;
+    const void* B;
+    const int32_t* bias;
+    const float* scale;
+    void* C;
+    int64_t M, K, N;
+    int chunk_rows;
+    hipStream_t st;
+    const agg_options* opt;
+};
+
+int run(const Call& c)
+{
+    agg_options def;
+    ag_gemm_options_init(&def);
+    const agg_options* opt = c.opt ? c.opt : &def;
+
+    // pointer checks first: they need no device
+    if (!c.shards || c.n < 1) return AGG_E_INVALID;
+    if (c.n > kMaxShards) return AGG_E_UNSUPPORTED;
+    if (c.M < 0 || c.K < 0 || c.N < 0) return AGG_E_INVALID;
+    const bool empty = c.M == 0 || c.N == 0;
+    if (!empty) {
+        if (c.K > 0) {
+            for (int i = 0; i < c.n; ++i) {
+                if (!c.shards[i]) return AGG_E_INVALID;
+                if (!aligned(c.shards[i], 16)) return AGG_E_UNSUPPORTED;
+            }
+            if (!c.B) return AGG_E_INVALID;
+            if (!aligned(c.B, 16)) return AGG_E_UNSUPPORTED;
+        }
+        if (!c.C) return AGG_E_INVALID;
+        if (!aligned(c.C, 16)) return AGG_E_UNSUPPORTED;
+        if (c.kind == kI8) {
+            if (!c.bias || !c.scale) return AGG_E_INVALID;
+            if (!aligned(c.bias, 4) || !aligned(c.scale, 4)) return AGG_E_UNSUPPORTED;
+            if (opt->acc_out && !aligned(opt->acc_out, 16)) return AGG_E_UNSUPPORTED;
+        }
+    }
+
+    // every argument check runs before the first HIP call
+    Plan p;
+    int rc = make_plan(c.kind, c.n, c.M, c.K, c.N, c.chunk_rows, opt, 0, &p);
+    if (rc) return rc;
+    if (empty) return AGG_OK;   // nothing to compute or move
+
+    std::lock_guard<std::mutex> lock(g_mu);
+    Device* d = nullptr;
+    rc = device_state(&d);
+    if (rc) return rc;
+    rc = make_plan(c.kind, c.n, c.M, c.K, c.N, c.chunk_rows, opt, d->num_cus, &p);
+    if (rc) return rc;
+
+    const int kind = c.kind == kF16 ? 0 : 1;
+    const bool run_producer = p.mode != AGG_MODE_COMPUTE_ONLY && c.n > 1 && c.K > 0;
+    const bool run_consumer = p.mode != AGG_MODE_COPY_ONLY;
+
+    // workspace
+    char* ws = nullptr;
+    Track* tr = nullptr;
+    if (opt->workspace) {
+        auto it = g_user_ws.find(opt->workspace);
+        if (it == g_user_ws.end() || opt->workspace_bytes < p.ws_bytes) return AGG_E_INVALID;
+        ws = static_cast<char*>(opt->workspace);
+        tr = &it->second;
+    } else {
+        rc = internal_workspace(*d, p.ws_bytes, c.st, &ws, &tr);
+        if (rc) return rc;
+    }
+    const uint32_t epoch = ++tr->epoch;
+    const double timeout_ms = opt->timeout_ms > 0 ? opt->timeout_ms : 2000.0;
+    const uint64_t limit = (uint64_t)(timeout_ms * 1e-3 * d->clock_hz);
+    uint32_t* header = reinterpret_cast<uint32_t*>(ws);
+
+    const Schedule& s = p.sched;
+    const size_t slot = ((size_t)s.S * (size_t)s.K * p.elt + 255) & ~(size_t)255;
+    ConsumerArgs ca;
+    memset(&ca, 0, sizeof ca);
+    ProducerArgs pa;
+    memset(&pa, 0, sizeof pa);
+    ca.s = s;
+    pa.s = s;
+    for (int i = 0; i < c.n; ++i) {
+        const char* src = static_cast<const char*>(c.shards[i]);
+        char* dst = s.slot[i] >= 0 ? ws + kHeaderBytes + slot * (size_t)s.slot[i] : nullptr;
+        ca.a[i] = (i == s.local) ? src : dst;
+        pa.src[i] = src;
+        pa.dst[i] = dst;
+        ca.base[i] = tr->base[i];
+        pa.base[i] = tr->base[i];
+    }
+    ca.B = static_cast<const char*>(c.B);
+    ca.C = c.C;
+    ca.counters = header;
+    ca.err = header + kErrorOffset / 4;
+    ca.epoch = epoch;
+    // the consumer waits on counters only while a producer runs beside it
+    ca.no_wait = !(p.mode == AGG_MODE_PIPELINED && run_producer);
+    ca.limit = limit;
+    ca.bias = c.bias;
+    ca.scale = c.scale;
+    ca.acc_out = opt->acc_out;
+    pa.counters = header;
+    pa.err = header + kErrorOffset / 4;
+    pa.clock = reinterpret_cast<uint64_t*>(ws + kClockOffset);
+    pa.ticket = reinterpret_cast<uint32_t*>(ws + kTicketOffset);
+    pa.ticket_base = tr->tickets;
+    pa.epoch = epoch;
+    pa.elt = p.elt;
+    pa.drop = p.drop_chunk;
+    pa.ticks_per_byte = p.link_gbps > 0 ? d->clock_hz / (p.link_gbps * 1e9) : 0.0;
+    pa.limit = limit;
+
+    int occ = occupancy(*d, kind, p.shape.id);
+    if (occ < 1) return AGG_E_HIP;
+    int cwgs = p.consumer_wgs;
+    if (!opt->consumer_wgs && cwgs > d->num_cus * occ) cwgs = d->num_cus * occ;
+    // While the consumer waits on counters the producer must find room on
+    // some CU: keep a few consumer slots free so it always can.
+    const bool concurrent = p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer;
+    const int reserve = 16;
+    if (concurrent && cwgs > d->num_cus * occ - reserve)
+        cwgs = d->num_cus * occ - reserve > 0 ? d->num_cus * occ - reserve : 1;
+
+    hipEvent_t* cev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opt->consumer_events));
+    auto consumer = [&](hipStream_t st) -> hipError_t {
+        hipError_t e = hipSuccess;
+        if (cev[0]) e = hipEventRecord(cev[0], st);
+        if (e == hipSuccess)
+            e = (c.kind == kF16) ? launch_consumer_f16(ca, p.shape.id, cwgs, st)
+                                 : launch_consumer_i8(ca, p.shape.id, cwgs, st);
+        if (e == hipSuccess && cev[1]) e = hipEventRecord(cev[1], st);
+        return e;
+    };
+
+    hipError_t e = hipSuccess;
+    if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer) {
+        e = hipEventRecord(d->fork, c.st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
+        if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
+        if (e == hipSuccess) e = consumer(c.st);
+        if (e == hipSuccess) e = hipEventRecord(d->join, d->side);
+        if (e == hipSuccess) e = hipStreamWaitEvent(c.st, d->join, 0);
+    } else {
+        if (run_producer) e = launch_producer(pa, p.producer_wgs, c.st);
+        if (e == hipSuccess && run_consumer) e = consumer(c.st);
+    }
+    if (e != hipSuccess) return AGG_E_HIP;
+    if (run_producer) {
+        for (int i = 0; i < c.n; ++i)
+            if (i != s.local) tr->base[i] += (uint32_t)s.cps;
+        // every producer workgroup takes one ticket past the last position
+        tr->tickets += (uint32_t)(total_chunks(s) + p.producer_wgs);
+    }
+    return AGG_OK;
+}
+
+int check_track(Track& t, uint32_t* header, hipStream_t st)
+{
+    uint32_t err = 0;
+    if (hipMemcpy(&err, header + kErrorOffset / 4, sizeof err, hipMemcpyDeviceToHost) != hipSuccess)
+        return AGG_E_HIP;
+    int rc = AGG_OK;
+    if (err && (int32_t)(err - t.checked) > 0) {
+        rc = AGG_E_TIMEOUT;
+        // a failed call leaves counters short: start over from zero
+        if (launch_header_reset(header, st) != hipSuccess) return AGG_E_HIP;
+        if (hipStreamSynchronize(st) != hipSuccess) return AGG_E_HIP;
+        memset(t.base, 0, sizeof t.base);
+        t.tickets = 0;
+    }
+    t.checked = t.epoch;
+    return rc;
+}
+
+}  // namespace
+}  // namespace agg
+
+using namespace agg;
+
+extern "C" {
+
+int ag_gemm_f16(const void* const* shards, int n_shards, const void* B, float* C,
+                int64_t M, int64_t K, int64_t N, int chunk_rows, void* stream)
+{
+    return ag_gemm_f16_ex(shards, n_shards, B, C, M, K, N, chunk_rows, stream, nullptr);
+}
+
+int ag_gemm_f16_ex(const void* const* shards, int n_shards, const void* B, float* C,
+                   int64_t M, int64_t K, int64_t N, int chunk_rows, void* stream,
+                   const agg_options* opt)
+{
+    Call c{kF16, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
+           static_cast<hipStream_t>(stream), opt};
+    return run(c);
+}
+
+int ag_gemm_i8_dequant(const int8_t* const* shards, int n_shards, const int8_t* B,
+                       const int32_t* bias, const float* scale, void* C, int64_t M,
+                       int64_t K, int64_t N, int chunk_rows, void* stream)
+{
+    return ag_gemm_i8_dequant_ex(shards, n_shards, B, bias, scale, C, M, K, N,
+                                 chunk_rows, stream, nullptr);
+}
+
+int ag_gemm_i8_dequant_ex(const int8_t* const* shards, int n_shards, const int8_t* B,
+                          const int32_t* bias, const float* scale, void* C, int64_t M,
+                          int64_t K, int64_t N, int chunk_rows, void* stream,
+                          const agg_options* opt)
+{
+    Call c{kI8, reinterpret_cast<const void* const*>(shards), n_shards, B, bias, scale,
+           C, M, K, N, chunk_rows, static_cast<hipStream_t>(stream), opt};
+    return run(c);
+}
+
+int ag_gemm_workspace_reset(void* workspace, size_t bytes, void* stream)
+{
+    if (!workspace || bytes < (size_t)kHeaderBytes) return AGG_E_INVALID;
+    if (!aligned(workspace, 256)) return AGG_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return AGG_E_HIP;
+    if (launch_header_reset(static_cast<uint32_t*>(workspace),
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+        return AGG_E_HIP;
+    Track t;
+    memset(&t, 0, sizeof t);
+    t.device = dev;
+    g_user_ws[workspace] = t;
+    return AGG_OK;
+}
+
+int ag_gemm_check(void* stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(st) != hipSuccess) return AGG_E_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return AGG_E_HIP;
+    // work on the side stream is joined into the caller's stream, but a
+    // copy-only call may have been the last thing on it
+    auto it = g_dev.find(dev);
+    int rc = AGG_OK;
+    if (it != g_dev.end() && it->second.ready) {
+        Device& d = it->second;
+        if (hipStreamSynchronize(d.side) != hipSuccess) return AGG_E_HIP;
+        if (d.ws) {
+            int r = check_track(d.track, reinterpret_cast<uint32_t*>(d.ws), st);
+            if (r) rc = r;
+        }
+    }
+    for (auto& kv : g_user_ws) {
+        if (kv.second.device != dev) continue;
+        int r = check_track(kv.second, static_cast<uint32_t*>(kv.first), st);
+        if (r && !rc) rc = r;
+    }
+    return rc;
+}
+
+void ag_gemm_release(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (auto& kv : g_dev) {
+        Device& d = kv.second;
+        if (!d.ready) continue;
+        (void)hipSetDevice(kv.first);
+        (void)hipDeviceSynchronize();
+        if (d.ws) (void)hipFree(d.ws);
+        if (d.fork) (void)hipEventDestroy(d.fork);
+        if (d.join) (void)hipEventDestroy(d.join);
+        if (d.side) (void)hipStreamDestroy(d.side);
+    }
+    g_dev.clear();
+    g_user_ws.clear();
+    (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// kernels.hpp -- arguments and launchers of the device kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "schedule.hpp"
+
+namespace agg {
+
+// Chunk producer: copies every remote shard's chunks into its workspace
+// slot, then releases them one by one on the shard's counter.
+struct ProducerArgs {
+    Schedule s;
+    const char* src[kMaxShards];   // shard base pointers
+    char* dst[kMaxShards];         // workspace slot of each remote shard
+    uint32_t* counters;            // header base; counter of shard i at i * 32
+    uint32_t* err;
+    uint64_t* clock;               // pacing origin slot
+    uint32_t* ticket;              // hands out producer positions in order
+    uint32_t ticket_base;          // its value at the start of the call
+    uint32_t base[kMaxShards];     // counter values at the start of the call
+    uint32_t epoch;
+    int elt;                       // bytes per element
+    int64_t drop;                  // producer position whose release is withheld
+    double ticks_per_byte;         // pacing; 0 = unpaced
+    uint64_t limit;                // wait limit in clock ticks
+};
+
+// Persistent consumer GEMM.
+struct ConsumerArgs {
+    Schedule s;
+    const char* a[kMaxShards];     // rows of each shard: local in place, remote in the workspace
+    const char* B;
+    void* C;
+    uint32_t* counters;
+    uint32_t* err;
+    uint32_t base[kMaxShards];
+    uint32_t epoch;
+    int no_wait;                   // compute-only mode: take every chunk as ready
+    uint64_t limit;
+    // int8 path
+    const int32_t* bias;
+    const float* scale;
+    int32_t* acc_out;
+};
+
+hipError_t launch_producer(const ProducerArgs& a, int wgs, hipStream_t st);
+hipError_t launch_consumer_f16(const ConsumerArgs& a, int tile_id, int wgs,
+                               hipStream_t st);
+hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs,
+                              hipStream_t st);
+hipError_t launch_header_reset(uint32_t* header, hipStream_t st);
+
+// Workgroups of a consumer tile shape that fit on one CU at once.
+int consumer_occupancy(int kind, int tile_id);
+
+}  // namespace agg

@@ -1,0 +1,248 @@
+// plan.cpp -- argument checks, chunk size choice and the shared schedule.
+// Host code only; no HIP calls, so it is testable without a GPU.
+#include "plan.hpp"
+
+#include <math.h>
+#include <string.h>
+
+namespace agg {
+
+namespace {
+
+// Output tiles the consumer kernels are instantiated for.  All use 4 waves
+// (one per SIMD) of 64 lanes; the big tile is what keeps the MFMA pipes fed
+// at large shapes, the small ones give enough tiles to fill 256 CUs and to
+// stream at small shapes.
+const TileShape kF16Shapes[] = {
+    {1, 256, 256, 256},
+    {2, 128, 128, 256},
+    {3, 64, 64, 256},
+};
+const TileShape kI8Shapes[] = {
+    {1, 256, 256, 256},
+    {2, 128, 128, 256},
+    {3, 64, 64, 256},
+};
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+const TileShape* tile_shapes(Kind kind, int* count)
+{
+    if (kind == kF16) {
+        *count = (int)(sizeof(kF16Shapes) / sizeof(kF16Shapes[0]));
+        return kF16Shapes;
+    }
+    *count = (int)(sizeof(kI8Shapes) / sizeof(kI8Shapes[0]));
+    return kI8Shapes;
+}
+
+int pick_chunk_rows(int64_t S)
+{
+    if (S < 1) return 0;
+    int64_t cr = S / 64;          // ceil(S / cr) then lies in [64, 127]
+    if (cr < 1) cr = 1;
+    if (cr > (int64_t)0x7fffffff) cr = 0x7fffffff;
+    return (int)cr;
+}
+
+static size_t slot_bytes(int64_t S, int64_t K, int elt)
+{
+    size_t b = (size_t)S * (size_t)K * (size_t)elt;
+    return (b + 255) & ~(size_t)255;
+}
+
+size_t workspace_bytes(int n_shards, int64_t M, int64_t K, int elt)
+{
+    if (n_shards < 1 || n_shards > kMaxShards || M < 0 || K < 0 || elt < 1 ||
+        M % n_shards)
+        return 0;
+    int64_t S = M / n_shards;
+    return (size_t)kHeaderBytes + (size_t)(n_shards - 1) * slot_bytes(S, K, elt);
+}
+
+int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
+              int chunk_rows, const agg_options* opt, int num_cus, Plan* out)
+{
+    agg_options def;
+    ag_gemm_options_init(&def);
+    if (!opt) opt = &def;
+    if (opt->struct_size < sizeof(agg_options)) return AGG_E_INVALID;
+    if (n_shards < 1) return AGG_E_INVALID;
+    if (n_shards > kMaxShards) return AGG_E_UNSUPPORTED;
+    if (M < 0 || K < 0 || N < 0) return AGG_E_INVALID;
+    if (M % n_shards) return AGG_E_INVALID;
+    const int64_t S = M / n_shards;
+    if (chunk_rows < 0 || (S > 0 && chunk_rows > S)) return AGG_E_INVALID;
+    const int kvec = (kind == kF16) ? 8 : 16;   // elements per 16-byte load
+    if (K % kvec || N % 8) return AGG_E_UNSUPPORTED;
+    if (opt->local_shard < 0 || opt->local_shard >= n_shards) return AGG_E_INVALID;
+    if (opt->mode < AGG_MODE_PIPELINED || opt->mode > AGG_MODE_COPY_ONLY)
+        return AGG_E_INVALID;
+    if (!(opt->link_gbps >= 0.0) || isinf(opt->link_gbps)) return AGG_E_INVALID;
+    if (opt->link_model != AGG_LINKS_PARALLEL && opt->link_model != AGG_LINKS_SERIAL)
+        return AGG_E_INVALID;
+    if (opt->producer_wgs < 0 || opt->consumer_wgs < 0) return AGG_E_INVALID;
+    if (!(opt->timeout_ms >= 0.0)) return AGG_E_INVALID;
+    if (num_cus <= 0) num_cus = 256;
+    // Row and element offsets are formed in 64-bit; per-tile loop counters
+    // in 32-bit.
+    if (S > (1LL << 30) || K > (1LL << 30) || N > (1LL << 30))
+        return AGG_E_UNSUPPORTED;
+
+    Plan p;
+    memset(&p, 0, sizeof p);
+    Schedule& s = p.sched;
+    s.n_shards = n_shards;
+    s.local = opt->local_shard;
+    s.link_model = opt->link_model;
+    s.S = S;
+    s.K = K;
+    s.N = N;
+    s.cr = chunk_rows ? chunk_rows : pick_chunk_rows(S);
+    if (s.cr < 1) s.cr = 1;
+    s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
+
+    // send order: a permutation of the remote shards
+    for (int i = 0; i < kMaxShards; ++i) { s.order[i] = -1; s.slot[i] = -1; }
+    s.order[0] = s.local;
+    bool seen[kMaxShards] = {false};
+    seen[s.local] = true;
+    for (int q = 1; q < n_shards; ++q) {
+        int id = opt->send_order ? opt->send_order[q - 1]
+                                 : (s.local + q) % n_shards;
+        if (id < 0 || id >= n_shards || seen[id]) return AGG_E_INVALID;
+        seen[id] = true;
+        s.order[q] = id;
+        s.slot[id] = q - 1;
+    }
+
+    // output tile
+    int count = 0;
+    const TileShape* shapes = tile_shapes(kind, &count);
+    const TileShape* pick = nullptr;
+    if (opt->tile) {
+        for (int i = 0; i < count; ++i)
+            if (shapes[i].id == opt->tile) pick = &shapes[i];
+        if (!pick) return AGG_E_INVALID;
+    } else {
+        // the largest tile that still gives every CU two or more tiles
+        for (int i = 0; i < count && !pick; ++i) {
+            int64_t tiles = (int64_t)n_shards * cdiv(S, shapes[i].tm) *
+                            cdiv(N, shapes[i].tn);
+            if (tiles >= 2LL * num_cus) pick = &shapes[i];
+        }
+        if (!pick) pick = &shapes[count - 1];
+    }
+    p.shape = *pick;
+    s.tm = pick->tm;
+    s.tn = pick->tn;
+    s.mt = (int)cdiv(S, s.tm);
+    s.nt = (int)cdiv(N, s.tn);
+
+    int64_t tiles = total_tiles(s);
+    int64_t chunks = total_chunks(s);
+    int cw = opt->consumer_wgs ? opt->consumer_wgs : num_cus;
+    if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
+    if (cw < 1) cw = 1;
+    int pw = opt->producer_wgs ? opt->producer_wgs : (num_cus + 1) / 2;
+    if (pw > chunks) pw = (int)(chunks > 0 ? chunks : 1);
+    if (pw < 1) pw = 1;
+    p.consumer_wgs = cw;
+    p.producer_wgs = pw;
+    p.mode = opt->mode;
+    p.link_gbps = opt->link_gbps;
+    p.elt = (kind == kF16) ? 2 : 1;
+    p.M = M;
+    p.ws_bytes = workspace_bytes(n_shards, M, K, p.elt);
+    p.drop_chunk = opt->debug_drop_chunk;
+    *out = p;
+    return AGG_OK;
+}
+
+}  // namespace agg
+
+extern "C" {
+
+void ag_gemm_options_init(agg_options* opt)
+{
+    if (!opt) return;
+    memset(opt, 0, sizeof *opt);
+    opt->struct_size = sizeof(agg_options);
+    opt->local_shard = 0;
+    opt->send_order = nullptr;
+    opt->mode = AGG_MODE_PIPELINED;
+    opt->link_gbps = 0.0;
+    opt->link_model = AGG_LINKS_PARALLEL;
+    opt->debug_drop_chunk = -1;
+}
+
+int ag_gemm_pick_chunk_rows(int64_t shard_rows)
+{
+    return agg::pick_chunk_rows(shard_rows);
+}
+
+size_t ag_gemm_workspace_bytes(int n_shards, int64_t M, int64_t K, int elt_bytes)
+{
+    return agg::workspace_bytes(n_shards, M, K, elt_bytes);
+}
+
+const char* ag_gemm_status_string(int status)
+{
+    switch (status) {
+    case AGG_OK: return "ok";
+    case AGG_E_INVALID: return "invalid argument";
+    case AGG_E_UNSUPPORTED: return "unsupported shape or alignment";
+    case AGG_E_NOMEM: return "out of device memory";
+    case AGG_E_HIP: return "HIP runtime error";
+    case AGG_E_TIMEOUT: return "counter wait timed out";
+    default: return "unknown status";
+    }
+}
+
+int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
+                 int chunk_rows, const agg_options* opt, int num_cus,
+                 agg_plan_info* info, int32_t* tile_order, int32_t* chunk_order)
+{
+    if (kind != 0 && kind != 1) return AGG_E_INVALID;
+    agg::Plan p;
+    int rc = agg::make_plan(kind == 0 ? agg::kF16 : agg::kI8, n_shards, M, K,
+                            N, chunk_rows, opt, num_cus, &p);
+    if (rc) return rc;
+    const agg::Schedule& s = p.sched;
+    if (info) {
+        info->shard_rows = s.S;
+        info->chunk_rows = s.cr;
+        info->chunks_per_source = s.cps;
+        info->tile_m = s.tm;
+        info->tile_n = s.tn;
+        info->m_tiles_per_shard = s.mt;
+        info->n_tiles = s.nt;
+        info->total_tiles = agg::total_tiles(s);
+        info->total_chunks = agg::total_chunks(s);
+        info->consumer_wgs = p.consumer_wgs;
+        info->producer_wgs = p.producer_wgs;
+    }
+    if (tile_order) {
+        int64_t T = agg::total_tiles(s);
+        for (int64_t i = 0; i < T; ++i) {
+            agg::TileRef t = agg::tile_at(s, i);
+            tile_order[4 * i + 0] = t.shard;
+            tile_order[4 * i + 1] = t.m;
+            tile_order[4 * i + 2] = t.n;
+            tile_order[4 * i + 3] = t.need;
+        }
+    }
+    if (chunk_order) {
+        int64_t C = agg::total_chunks(s);
+        for (int64_t i = 0; i < C; ++i) {
+            agg::ChunkRef c = agg::chunk_at(s, i);
+            chunk_order[2 * i + 0] = c.shard;
+            chunk_order[2 * i + 1] = c.j;
+        }
+    }
+    return AGG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// plan.hpp -- host-side argument checks and planning (no HIP calls).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "aggemm.h"
+#include "schedule.hpp"
+
+namespace agg {
+
+enum Kind { kF16 = 0, kI8 = 1 };
+
+struct TileShape {
+    int id;         // 1-based id accepted by agg_options.tile
+    int tm, tn;     // output tile
+    int threads;    // workgroup size
+};
+
+// Output tiles the consumer kernels are built for, per path.
+const TileShape* tile_shapes(Kind kind, int* count);
+
+struct Plan {
+    Schedule sched;
+    TileShape shape;
+    int mode;
+    double link_gbps;
+    int consumer_wgs;
+    int producer_wgs;
+    int elt;            // bytes per A element
+    int64_t M;
+    size_t ws_bytes;    // workspace bytes this call needs
+    int drop_chunk;
+};
+
+// Validate arguments and build the plan.  num_cus: CUs of the target device.
+int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
+              int chunk_rows, const agg_options* opt, int num_cus, Plan* out);
+
+int pick_chunk_rows(int64_t shard_rows);
+size_t workspace_bytes(int n_shards, int64_t M, int64_t K, int elt);
+
+}  // namespace agg

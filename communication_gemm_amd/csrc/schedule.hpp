@@ -1,0 +1,163 @@
+// schedule.hpp -- the one schedule that drives both the chunk producer and
+// the persistent consumer GEMM (PTO-ISA AllGather+GEMM README, optimisation
+// notes: the communication side sends chunks in the order the compute side
+// consumes them; the local row-group is computed first with no wait).
+//
+// Everything here is plain integer arithmetic usable on the host (planning,
+// tests) and on the device (kernels map their position to work with it).
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define AGG_HD __host__ __device__ inline
+#else
+#define AGG_HD inline
+#endif
+
+namespace agg {
+
+constexpr int kMaxShards = 64;
+
+// Workspace header: one 32-bit counter per source shard, each on its own
+// 128-byte line, then the error word, the pacing origin and the producer's
+// ticket counter.
+constexpr int kCounterStride = 128;                       // bytes
+constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
+constexpr int kClockOffset = kErrorOffset + kCounterStride; // uint64
+constexpr int kTicketOffset = kClockOffset + kCounterStride; // uint32
+constexpr int kHeaderBytes = 16384;
+
+struct Schedule {
+    int n_shards;
+    int local;             // shard read in place
+    int link_model;        // 0 = parallel links, 1 = one serial link
+    int cr;                // rows per chunk
+    int cps;               // chunks per source
+    int tm, tn;            // output tile
+    int mt;                // m-tiles per shard
+    int nt;                // n-tiles
+    int64_t S, K, N;
+    int order[kMaxShards]; // order[0] = local, order[1..n-1] = send order
+    int slot[kMaxShards];  // workspace slot of each shard (-1: local)
+};
+
+AGG_HD int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Chunks of a source that must be released before m-tile `m` can start:
+// the chunk holding the tile's last row, and all before it.
+AGG_HD int need_chunks(const Schedule& s, int m)
+{
+    int64_t last = (int64_t)(m + 1) * s.tm;
+    if (last > s.S) last = s.S;
+    return (int)cdiv(last, s.cr);
+}
+
+AGG_HD int64_t total_tiles(const Schedule& s)
+{
+    return (int64_t)s.n_shards * s.mt * s.nt;
+}
+
+AGG_HD int64_t total_chunks(const Schedule& s)
+{
+    return (int64_t)(s.n_shards - 1) * s.cps;
+}
+
+struct TileRef {
+    int shard;   // source shard of the A rows
+    int m;       // m-tile within the shard
+    int n;       // n-tile
+    int need;    // counter value to wait for (0 = local, no wait)
+};
+
+// Consumer position p -> tile.  Local tiles first; then remote tiles in
+// arrival order: with parallel links every source delivers its rows at the
+// same time, so tiles go m-tile by m-tile across sources; with one serial
+// link sources arrive one after the other.
+AGG_HD TileRef tile_at(const Schedule& s, int64_t p)
+{
+    TileRef t;
+    int64_t local_tiles = (int64_t)s.mt * s.nt;
+    if (p < local_tiles) {
+        t.shard = s.local;
+        t.m = (int)(p / s.nt);
+        t.n = (int)(p % s.nt);
+        t.need = 0;
+        return t;
+    }
+    int64_t q = p - local_tiles;
+    int remotes = s.n_shards - 1;
+    int src;
+    if (s.link_model == 0) {
+        int64_t per_m = (int64_t)remotes * s.nt;
+        t.m = (int)(q / per_m);
+        int64_t r = q % per_m;
+        src = (int)(r / s.nt);
+        t.n = (int)(r % s.nt);
+    } else {
+        int64_t per_src = (int64_t)s.mt * s.nt;
+        src = (int)(q / per_src);
+        int64_t r = q % per_src;
+        t.m = (int)(r / s.nt);
+        t.n = (int)(r % s.nt);
+    }
+    t.shard = s.order[1 + src];
+    t.need = need_chunks(s, t.m);
+    return t;
+}
+
+struct ChunkRef {
+    int shard;   // source shard
+    int src;     // its position in the send order (0-based over remotes)
+    int j;       // chunk index within the shard
+};
+
+// Producer position c -> chunk, in the order the consumer needs them.
+AGG_HD ChunkRef chunk_at(const Schedule& s, int64_t c)
+{
+    ChunkRef r;
+    int remotes = s.n_shards - 1;
+    if (s.link_model == 0) {
+        // group g = chunks first needed by m-tile g, every source in send
+        // order, chunks ascending inside a source
+        int prev = 0;
+        for (int g = 0; g < s.mt; ++g) {
+            int cur = need_chunks(s, g);
+            int64_t gs = cur - prev;
+            int64_t span = gs * remotes;
+            if (c < span) {
+                r.src = (int)(c / gs);
+                r.j = prev + (int)(c % gs);
+                r.shard = s.order[1 + r.src];
+                return r;
+            }
+            c -= span;
+            prev = cur;
+        }
+        r.src = -1; r.j = -1; r.shard = -1;   // out of range
+        return r;
+    }
+    r.src = (int)(c / s.cps);
+    r.j = (int)(c % s.cps);
+    r.shard = s.order[1 + r.src];
+    return r;
+}
+
+// Rows of chunk j: [j*cr, min((j+1)*cr, S)).
+AGG_HD int64_t chunk_row_end(const Schedule& s, int j)
+{
+    int64_t e = (int64_t)(j + 1) * s.cr;
+    return e < s.S ? e : s.S;
+}
+
+// Bytes that must have crossed the emulated link before chunk (src, j) may
+// be released: its own source's rows up to the chunk's end (parallel
+// links), or everything sent before it on the one link (serial).
+AGG_HD int64_t paced_bytes(const Schedule& s, const ChunkRef& r, int elt)
+{
+    int64_t rows = chunk_row_end(s, r.j);
+    if (s.link_model != 0) rows += (int64_t)r.src * s.S;
+    return rows * s.K * elt;
+}
+
+}  // namespace agg

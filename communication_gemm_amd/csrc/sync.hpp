@@ -1,0 +1,105 @@
+// sync.hpp -- device-side counter primitives for chunk readiness.
+//
+// A source's counter only grows: the producer adds one per chunk, in chunk
+// order, after the chunk's stores (PTO-ISA AllGather+GEMM README: the
+// communication side atomically increments a per-source summary counter
+// after each chunk; the compute side blocks until the counter reaches the
+// value it expects).  Counters are never reset between calls: each call
+// waits for base + n, the base carried over from the calls before it, and
+// values are compared modulo 2^32 (the Pallas collective matmul page waits
+// on a semaphore whose expected value grows with the step for the same
+// reason).
+//
+// gfx950 has no compare-and-block on memory inside a kernel, so the waiting
+// side polls with one lane, sleeps between polls and gives up after a time
+// limit, leaving an error mark instead of hanging.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace agg {
+
+__device__ inline uint64_t ticks()
+{
+    return __builtin_amdgcn_s_memrealtime();   // constant-rate clock
+}
+
+__device__ inline uint32_t load_agent(const uint32_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline bool reached(uint32_t value, uint32_t target)
+{
+    return (int32_t)(value - target) >= 0;
+}
+
+// Mark the call `epoch` as failed (the error word keeps the largest
+// failing epoch).
+__device__ inline void raise_error(uint32_t* err, uint32_t epoch)
+{
+    __hip_atomic_fetch_max(err, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll *ctr until it reaches `target` (mod 2^32).  On success the caller's
+// later loads see everything released before the counter got there.
+// Returns the value seen, or target - 1 after a time-out or after another
+// workgroup of the same call failed.
+__device__ inline uint32_t acquire_wait(const uint32_t* ctr, uint32_t target,
+                                        uint32_t* err, uint32_t epoch,
+                                        uint64_t limit)
+{
+    uint32_t v = load_agent(ctr);
+    if (!reached(v, target)) {
+        const uint64_t t0 = ticks();
+        uint32_t spins = 0;
+        do {
+            __builtin_amdgcn_s_sleep(2);
+            if ((++spins & 31u) == 0) {
+                if (reached(load_agent(err), epoch)) return target - 1;
+                if (ticks() - t0 > limit) {
+                    raise_error(err, epoch);
+                    return target - 1;
+                }
+            }
+            v = load_agent(ctr);
+        } while (!reached(v, target));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return v;
+}
+
+// Release one more chunk: every lane has already fenced its own stores.
+__device__ inline void release_add(uint32_t* ctr)
+{
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Pacing origin shared by all producer workgroups of one call: the first
+// one to arrive stamps the clock, tagged with the call's epoch.
+__device__ inline uint64_t pacing_origin(uint64_t* slot, uint32_t epoch)
+{
+    const uint64_t mask = (1ull << 40) - 1;
+    const uint64_t tag = (uint64_t)(epoch & 0xffffffu);
+    uint64_t now = ticks() & mask;
+    uint64_t mine = (tag << 40) | now;
+    uint64_t cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        if ((cur >> 40) == tag) return cur & mask;
+        if (__hip_atomic_compare_exchange_strong(slot, &cur, mine, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return now;
+    }
+}
+
+// Sleep until the 40-bit clock has advanced `delta` past `origin`.
+__device__ inline void wait_until(uint64_t origin, uint64_t delta)
+{
+    const uint64_t mask = (1ull << 40) - 1;
+    while (((ticks() - origin) & mask) < delta)
+        __builtin_amdgcn_s_sleep(1);
+}
+
+}  // namespace agg

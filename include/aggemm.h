@@ -1,0 +1,206 @@
+/*
+ * aggemm.h -- streamed AllGather + GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libaggemm.so.  No C++ or torch types cross this boundary: data
+ * arguments are plain device pointers, sizes are int64_t, a stream is a
+ * hipStream_t passed as void* (NULL = the default stream).
+ *
+ * The operation (PTO-ISA AllGather+GEMM README, "compute function"; the
+ * Triton-distributed AllGather GEMM tutorial's reference function):
+ *
+ *   A = [A_0; A_1; ...; A_{n-1}]       row blocks stacked in shard order,
+ *                                       shard s = rows [s*S, (s+1)*S), S = M/n
+ *   C = A x B                           B: K x N, replicated
+ *
+ * computed as a stream: the shards other than the local one reach a
+ * workspace chunk by chunk (a chunk = chunk_rows consecutive rows of one
+ * shard, all of K), each chunk released by a monotonic per-source counter;
+ * the GEMM starts on the local shard, which needs no wait, and consumes the
+ * remote chunks in the order they are sent (PTO-ISA README, "streaming
+ * pipeline" and "optimisation notes").  On one GPU every shard is a local
+ * allocation; a producer kernel on a side stream plays the links.
+ *
+ * Result: C rows [s*S, (s+1)*S) = A_s x B for every shard s, whatever the
+ * local shard, the send order, the chunk size, the mode or the pacing.
+ *
+ * Return values: AGG_OK (0) or a positive agg_status.  Argument errors are
+ * reported synchronously and nothing is enqueued.  Kernel time-outs (a
+ * counter that never reaches its value) are reported by ag_gemm_check().
+ * Faults of asynchronous work surface at stream synchronisation, as in HIP.
+ *
+ * Threading: calls that use the library's internal workspace on one device
+ * must be issued from one host thread at a time and are ordered on their
+ * streams; two calls in flight on different streams of one device would
+ * share the workspace and race.
+ */
+#ifndef AGGEMM_H
+#define AGGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum agg_status {
+    AGG_OK = 0,
+    AGG_E_INVALID = 1,      /* null pointer, bad size, bad permutation ...   */
+    AGG_E_UNSUPPORTED = 2,  /* K or N not a multiple of the vector width,
+                               misaligned pointer, too many shards          */
+    AGG_E_NOMEM = 3,        /* workspace allocation failed                   */
+    AGG_E_HIP = 4,          /* a HIP call failed while enqueueing            */
+    AGG_E_TIMEOUT = 5       /* a counter wait exceeded its limit (reported
+                               by ag_gemm_check)                             */
+};
+
+/* What one call runs (PTO-ISA README, "benchmark and output"). */
+enum agg_mode {
+    AGG_MODE_PIPELINED = 0,    /* producer and consumer run concurrently     */
+    AGG_MODE_COMPUTE_ONLY = 1, /* consumer only; every chunk taken as ready,
+                                  remote rows read from the workspace as the
+                                  previous call on it left them              */
+    AGG_MODE_SEQUENTIAL = 2,   /* producer finishes, then the consumer runs  */
+    AGG_MODE_COPY_ONLY = 3     /* producer only; C is not written            */
+};
+
+/* How the emulated links are paced when link_gbps > 0. */
+enum agg_link_model {
+    AGG_LINKS_PARALLEL = 0,  /* one link per source, all in parallel (full
+                                mesh): chunk j of every source is released
+                                no earlier than t0 + bytes(chunks 0..j)/rate */
+    AGG_LINKS_SERIAL = 1     /* one link shared by all sources in send order */
+};
+
+#define AGG_MAX_SHARDS 64
+
+typedef struct agg_options {
+    uint32_t struct_size;   /* sizeof(agg_options); set by ag_gemm_options_init */
+    int local_shard;        /* shard read in place, never waited on (default 0) */
+    const int *send_order;  /* HOST array of the n-1 remote shard ids in send
+                               order, or NULL for local+1, local+2, ... mod n */
+    int mode;               /* enum agg_mode (default PIPELINED)              */
+    double link_gbps;       /* per-link pacing in GB/s (1e9 B/s); 0 = none    */
+    int link_model;         /* enum agg_link_model (default PARALLEL)         */
+    int producer_wgs;       /* producer workgroups; 0 = automatic            */
+    int consumer_wgs;       /* consumer workgroups; 0 = automatic            */
+    int tile;               /* consumer tile shape id; 0 = automatic          */
+    int32_t *acc_out;       /* int8 path only: optional DEVICE int32 [M, N]
+                               receiving A x B + bias before the dequant     */
+    void *workspace;        /* optional caller-owned DEVICE workspace, made
+                               ready once by ag_gemm_workspace_reset()       */
+    size_t workspace_bytes; /* its size (>= ag_gemm_workspace_bytes(...))    */
+    double timeout_ms;      /* bound on every counter wait; 0 = 2000 ms      */
+    int debug_drop_chunk;   /* test hook: index (in send order) of a chunk
+                               whose release is withheld; -1 = off           */
+    void *consumer_events[2]; /* optional hipEvent_t pair recorded right
+                                 before and after the consumer kernel, on
+                                 the stream it runs on                       */
+} agg_options;
+
+/* Fill *opt with the defaults above. */
+void ag_gemm_options_init(agg_options *opt);
+
+/*
+ * fp16 x fp16 -> fp32 streamed AllGather + GEMM.
+ *   shards     HOST array of n_shards DEVICE pointers, each an fp16 [S, K]
+ *              row-major block (S = M / n_shards), 16-byte aligned.
+ *   B          DEVICE fp16 [K, N] row-major, 16-byte aligned.
+ *   C          DEVICE fp32 [M, N] row-major, fully overwritten; must not
+ *              alias any input.
+ *   chunk_rows rows per chunk; 0 = ag_gemm_pick_chunk_rows(S).
+ * Requires K % 8 == 0 and N % 8 == 0 (AGG_E_UNSUPPORTED otherwise).
+ * Inputs are read only; the caller owns every buffer.
+ * PTO-ISA AllGather+GEMM README, "spec" table: A M x K fp16 (split on M
+ * across ranks), B K x N fp16 (replicated), C M x N fp32.
+ */
+int ag_gemm_f16(const void *const *shards, int n_shards, const void *B,
+                float *C, int64_t M, int64_t K, int64_t N, int chunk_rows,
+                void *stream);
+int ag_gemm_f16_ex(const void *const *shards, int n_shards, const void *B,
+                   float *C, int64_t M, int64_t K, int64_t N, int chunk_rows,
+                   void *stream, const agg_options *opt);
+
+/*
+ * int8 x int8 -> int32, + bias, x per-channel scale -> fp16
+ * (catccos AllGatherMatmulDequant design doc, sections 1.2 and 2.2):
+ *   v = A x B + bias[n]        exact int32
+ *   C = fp16_rne(fp32_rne(v) * scale[n])
+ *   shards  HOST array of n_shards DEVICE int8 [S, K] row-major blocks.
+ *   B       DEVICE int8 [K, N] row-major.
+ *   bias    DEVICE int32 [N];  scale DEVICE fp32 [N] (per output channel).
+ *   C       DEVICE fp16 [M, N] row-major, fully overwritten.
+ * Requires K % 16 == 0 and N % 8 == 0.  The caller guarantees that every
+ * |v| < 2^31 (int32 accumulation does not saturate).
+ */
+int ag_gemm_i8_dequant(const int8_t *const *shards, int n_shards,
+                       const int8_t *B, const int32_t *bias,
+                       const float *scale, void *C, int64_t M, int64_t K,
+                       int64_t N, int chunk_rows, void *stream);
+int ag_gemm_i8_dequant_ex(const int8_t *const *shards, int n_shards,
+                          const int8_t *B, const int32_t *bias,
+                          const float *scale, void *C, int64_t M, int64_t K,
+                          int64_t N, int chunk_rows, void *stream,
+                          const agg_options *opt);
+
+/*
+ * Rows per chunk so that each source has 64 to 127 chunks: max(1, S / 64)
+ * (PTO-ISA README, "dynamic chunk size": 64-128 chunks per source).
+ * Returns 0 for S < 1.
+ */
+int ag_gemm_pick_chunk_rows(int64_t shard_rows);
+
+/* Bytes of workspace one call needs: a counter header plus one slot of
+ * S x K elements for every remote shard. 0 on invalid sizes. */
+size_t ag_gemm_workspace_bytes(int n_shards, int64_t M, int64_t K,
+                               int elt_bytes);
+
+/* Make a caller-owned workspace ready (zeroes its counter header on
+ * `stream`); needed once after allocating it. */
+int ag_gemm_workspace_reset(void *workspace, size_t bytes, void *stream);
+
+/*
+ * Synchronise `stream` and report whether the calls issued since the last
+ * check on this device timed out (AGG_E_TIMEOUT) or failed in HIP
+ * (AGG_E_HIP).  Clears the recorded error and re-arms the counters.
+ */
+int ag_gemm_check(void *stream);
+
+/* Human-readable text for an agg_status value. */
+const char *ag_gemm_status_string(int status);
+
+/* Free the internal workspaces and side streams of every device. */
+void ag_gemm_release(void);
+
+/* ---- planning queries (host only, no GPU needed) ----------------------- */
+
+typedef struct agg_plan_info {
+    int64_t shard_rows;     /* S */
+    int chunk_rows;         /* rows per chunk */
+    int chunks_per_source;  /* ceil(S / chunk_rows) */
+    int tile_m, tile_n;     /* consumer output tile */
+    int m_tiles_per_shard;  /* ceil(S / tile_m) */
+    int n_tiles;            /* ceil(N / tile_n) */
+    int64_t total_tiles;    /* n_shards * m_tiles_per_shard * n_tiles */
+    int64_t total_chunks;   /* (n_shards - 1) * chunks_per_source */
+    int consumer_wgs;       /* persistent consumer grid */
+    int producer_wgs;       /* producer grid */
+} agg_plan_info;
+
+/*
+ * The schedule one call would run, for inspection and tests.
+ *   kind: 0 = fp16 path, 1 = int8 path; num_cus: CUs of the device to plan
+ *   for (0 = 256).  tile_order (nullable, capacity total_tiles * 4 int32):
+ *   per consumer position: shard, m-tile, n-tile, counter value waited for
+ *   (0 for the local shard).  chunk_order (nullable, capacity total_chunks
+ *   * 2 int32): per producer position: shard, chunk index.
+ */
+int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
+                 int chunk_rows, const agg_options *opt, int num_cus,
+                 agg_plan_info *info, int32_t *tile_order,
+                 int32_t *chunk_order);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AGGEMM_H */

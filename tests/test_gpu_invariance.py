@@ -1,0 +1,128 @@
+"""Schedule invariance, ordering and failure handling on the GPU.
+
+Chunking cuts A along M only and never changes the order of the K sum, so
+the HIP output must be bit-identical whatever the chunk size, local shard,
+send order, link pacing, link model, producer width or mode (the gathered
+result is the same C: PTO-ISA AllGather+GEMM README, "compute function").
+A consumer that read a chunk before its release would see the NaN planted
+in the workspace.  A withheld release must end in a reported time-out, not
+a hang.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import check_f16, dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def agg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import communication_gemm_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def data():
+    shards, B = synth.make_f16(4 * 512, 1024, 768, 4, "normal", 50000)
+    return [dev(s, torch) for s in shards], dev(B, torch), shards, B
+
+
+def call(agg, data, chunk_rows=0, **kw):
+    ts, B = data[0], data[1]
+    C = torch.full((ts[0].shape[0] * len(ts), B.shape[1]), float("nan"), device="cuda")
+    agg.ag_gemm_f16(ts, B, C, chunk_rows, opts=agg.options(**kw))
+    rc = agg.check()
+    assert rc == 0, agg.status_string(rc)
+    return C
+
+
+@pytest.fixture(scope="module")
+def ref(agg, data, orc):
+    C = call(agg, data)
+    Co, So = orc.ag_gemm_f16(data[2], data[3])
+    check_f16(C.cpu().numpy(), Co, So, "reference call")
+    return C
+
+
+@pytest.mark.parametrize("kw", [
+    dict(chunk_rows=1), dict(chunk_rows=16), dict(chunk_rows=100), dict(chunk_rows=512),
+    dict(local_shard=2), dict(local_shard=3, send_order=[1, 0, 2]),
+    dict(send_order=[3, 2, 1]),
+    dict(link_model=1), dict(link_model=1, send_order=[2, 3, 1]),
+    dict(link_gbps=50.0), dict(link_gbps=20.0, link_model=1),
+    dict(producer_wgs=1), dict(producer_wgs=3), dict(consumer_wgs=7),
+    dict(mode=2),
+])
+def test_bitwise_invariant(agg, data, ref, kw):
+    kw = dict(kw)
+    cr = kw.pop("chunk_rows", 0)
+    C = call(agg, data, cr, **kw)
+    assert torch.equal(C, ref), kw
+
+
+def test_compute_only_after_copy_only(agg, data, ref):
+    ts, B = data[0], data[1]
+    C = torch.full_like(ref, float("nan"))
+    agg.ag_gemm_f16(ts, B, C, opts=agg.options(mode=3))       # copy only
+    agg.ag_gemm_f16(ts, B, C, opts=agg.options(mode=1))       # compute only
+    assert agg.check() == 0
+    assert torch.equal(C, ref)
+
+
+def test_repeated_calls_reuse_counters(agg, data, ref):
+    # counters are never reset between calls: each call waits for base + n
+    for i in range(20):
+        C = call(agg, data, [0, 7, 64][i % 3])
+        assert torch.equal(C, ref)
+
+
+def test_nan_poisoned_caller_workspace(agg, data, ref):
+    ts, B = data[0], data[1]
+    M, K = ts[0].shape[0] * len(ts), ts[0].shape[1]
+    nbytes = agg.workspace_bytes(len(ts), M, K, 2)
+    ws = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
+    for it in range(3):
+        ws.fill_(float("nan"))                 # slots hold NaN until released
+        agg.workspace_reset(ws)
+        C = torch.full_like(ref, float("nan"))
+        agg.ag_gemm_f16(ts, B, C, 8, opts=agg.options(workspace=ws, link_gbps=100.0))
+        assert agg.check() == 0
+        assert torch.equal(C, ref), f"iteration {it}"
+
+
+def test_unregistered_workspace_rejected(agg, data):
+    ts, B = data[0], data[1]
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    C = torch.empty((ts[0].shape[0] * len(ts), B.shape[1]), device="cuda")
+    with pytest.raises(agg.AggError) as e:
+        agg.ag_gemm_f16(ts, B, C, opts=agg.options(workspace=ws))
+    assert e.value.status == agg.AGG_E_INVALID
+
+
+def test_withheld_chunk_times_out_then_recovers(agg, data, ref):
+    ts, B = data[0], data[1]
+    C = torch.zeros_like(ref)
+    agg.ag_gemm_f16(ts, B, C, opts=agg.options(debug_drop_chunk=5, timeout_ms=50.0))
+    assert agg.check() == agg.AGG_E_TIMEOUT
+    # the next call starts from re-armed counters and is exact again
+    assert torch.equal(call(agg, data), ref)
+
+
+def test_i8_invariant_across_schedules(agg, orc):
+    shards, Bn, bias, scale = synth.make_i8(3 * 256, 512, 256, 3, 51000)
+    ts = [dev(s, torch) for s in shards]
+    B, tb, tsc = dev(Bn, torch), dev(bias, torch), dev(scale, torch)
+    outs = []
+    for kw, cr in [(dict(), 0), (dict(local_shard=1, send_order=[0, 2]), 5),
+                   (dict(link_model=1, link_gbps=30.0), 64), (dict(mode=2), 3)]:
+        C = torch.empty((768, 256), dtype=torch.float16, device="cuda")
+        agg.ag_gemm_i8_dequant(ts, B, tb, tsc, C, cr, opts=agg.options(**kw))
+        assert agg.check() == 0
+        outs.append(C)
+    for C in outs[1:]:
+        assert torch.equal(C, outs[0])

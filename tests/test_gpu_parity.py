@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Bar (fp16 path): |C_gpu - C_oracle| <= 5e-4 * sum_k |a_ik b_kj| per element.
+Bar (int8 path): int32 accumulators bit-exact; fp16 output within 1 ulp.
+Small cases are compared element by element in full; the full-size
+workloads on sampled rows (every shard's edges and chunk edges).
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import REL, check_f16, check_i8, dev, sample_rows
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def agg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import communication_gemm_amd as m
+    return m
+
+
+def run_f16(agg, shards, B, chunk_rows=0, opts=None):
+    ts = [dev(s, torch) for s in shards]
+    tB = dev(B, torch)
+    M = sum(s.shape[0] for s in shards)
+    C = torch.full((M, B.shape[1]), float("nan"), dtype=torch.float32, device="cuda")
+    agg.ag_gemm_f16(ts, tB, C, chunk_rows, opts=opts)
+    rc = agg.check()
+    assert rc == 0, agg.status_string(rc)
+    return C.cpu().numpy()
+
+
+def run_i8(agg, shards, B, bias, scale, chunk_rows=0, opts_kw=None):
+    ts = [dev(s, torch) for s in shards]
+    M = sum(s.shape[0] for s in shards)
+    N = B.shape[1]
+    acc = torch.full((M, N), -1, dtype=torch.int32, device="cuda")
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    opts = agg.options(acc_out=acc, **(opts_kw or {}))
+    agg.ag_gemm_i8_dequant(ts, dev(B, torch), dev(bias, torch), dev(scale, torch), C,
+                           chunk_rows, opts=opts)
+    rc = agg.check()
+    assert rc == 0, agg.status_string(rc)
+    return acc.cpu().numpy(), C.cpu().numpy()
+
+
+# ---------------------------------------------------------------- fp16 path
+
+def test_case1_full(agg, orc):
+    c = synth.CASES[1]
+    shards, B = synth.make_case(c)
+    C = run_f16(agg, shards, B, c.chunk_rows)
+    Co, So = orc.ag_gemm_f16(shards, B)
+    check_f16(C, Co, So, c.name)
+
+
+def test_case2_full(agg, orc):
+    c = synth.CASES[2]
+    shards, B = synth.make_case(c)
+    C = run_f16(agg, shards, B, c.chunk_rows)
+    Co, So = orc.ag_gemm_f16(shards, B)
+    check_f16(C, Co, So, c.name)
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_large_cases_sampled_rows(agg, orc, cid):
+    c = synth.CASES[cid]
+    shards, B = synth.make_case(c)
+    opts = agg.options(link_gbps=c.link_gbps) if c.link_gbps else None
+    C = run_f16(agg, shards, B, c.chunk_rows, opts)
+    assert np.isfinite(C).all()
+    rows = sample_rows(c.M, c.n_shards, agg.pick_chunk_rows(c.shard_rows))
+    Co, So = orc.ag_gemm_f16(shards, B, rows=rows)
+    check_f16(C[rows], Co, So, c.name)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("n,S,K,N,cr", [
+    (3, 100, 296, 168, 7),     # ragged rows, k tail, n tail, ragged last chunk
+    (2, 300, 520, 264, 0),
+    (4, 33, 8, 8, 5),          # K and N of a single vector
+])
+def test_ragged_shapes(agg, orc, tile, n, S, K, N, cr):
+    shards, B = synth.make_f16(n * S, K, N, n, "normal", 31000 + S)
+    C = run_f16(agg, shards, B, cr, agg.options(tile=tile))
+    Co, So = orc.ag_gemm_f16(shards, B)
+    check_f16(C, Co, So, f"tile {tile} n={n} S={S} K={K} N={N}")
+
+
+def test_single_shard_and_many_shards(agg, orc):
+    shards, B = synth.make_f16(96, 64, 32, 1, "normal", 32000)
+    C = run_f16(agg, shards, B)
+    Co, So = orc.ag_gemm_f16(shards, B)
+    check_f16(C, Co, So, "one shard")
+    shards, B = synth.make_f16(64 * 3, 32, 16, 64, "normal", 32001)
+    C = run_f16(agg, shards, B, 1)
+    Co, So = orc.ag_gemm_f16(shards, B)
+    check_f16(C, Co, So, "64 shards")
+
+
+def test_k_zero_gives_zeros(agg):
+    ts = [torch.empty((16, 0), dtype=torch.float16, device="cuda") for _ in range(2)]
+    B = torch.empty((0, 24), dtype=torch.float16, device="cuda")
+    C = torch.full((32, 24), 7.0, device="cuda")
+    agg.ag_gemm_f16(ts, B, C)
+    assert agg.check() == 0
+    assert (C == 0).all()
+
+
+def test_closed_form_all_ones(agg):
+    K = 4096
+    ts = [torch.ones((256, K), dtype=torch.float16, device="cuda") for _ in range(4)]
+    B = torch.ones((K, 512), dtype=torch.float16, device="cuda")
+    C = torch.empty((1024, 512), device="cuda")
+    agg.ag_gemm_f16(ts, B, C)
+    assert agg.check() == 0
+    assert (C == K).all()
+
+
+# ---------------------------------------------------------------- int8 path
+
+def test_i8_small_full(agg, orc):
+    shards, B, bias, scale = synth.make_i8(2 * 192, 27392 // 8, 264, 2, 40000)
+    acc, D = run_i8(agg, shards, B, bias, scale)
+    ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale)
+    check_i8(acc, D, ao, Do, "int8 small")
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_i8_ragged(agg, orc, tile):
+    shards, B, bias, scale = synth.make_i8(3 * 77, 16 * 37, 8 * 19, 3, 41000 + tile)
+    acc, D = run_i8(agg, shards, B, bias, scale, 9, dict(tile=tile))
+    ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale)
+    check_i8(acc, D, ao, Do, f"int8 ragged tile {tile}")
+
+
+def test_i8_debug_mode_all_ones(agg):
+    K, N = 27392, 256
+    ts = [torch.ones((128, K), dtype=torch.int8, device="cuda") for _ in range(2)]
+    B = torch.ones((K, N), dtype=torch.int8, device="cuda")
+    bias = torch.arange(N, dtype=torch.int32, device="cuda") - 128
+    scale = torch.full((N,), 5e-4, dtype=torch.float32, device="cuda")
+    C = torch.empty((256, N), dtype=torch.float16, device="cuda")
+    acc = torch.empty((256, N), dtype=torch.int32, device="cuda")
+    agg.ag_gemm_i8_dequant(ts, B, bias, scale, C, opts=agg.options(acc_out=acc))
+    assert agg.check() == 0
+    want = (K + bias).cpu().numpy()
+    assert (acc.cpu().numpy() == want[None, :]).all()
+    wantD = (want.astype(np.float32) * np.float32(5e-4)).astype(np.float16)
+    assert np.array_equal(C.cpu().numpy().view(np.uint16),
+                          np.broadcast_to(wantD.view(np.uint16), (256, N)))
+
+
+def test_case5_sampled_rows(agg, orc):
+    c = synth.CASES[5]
+    shards, B, bias, scale = synth.make_case(c)
+    acc, D = run_i8(agg, shards, B, bias, scale)
+    rows = sample_rows(c.M, c.n_shards, agg.pick_chunk_rows(c.shard_rows), extra=6)
+    ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale, rows=rows)
+    check_i8(acc[rows], D[rows], ao, Do, c.name)

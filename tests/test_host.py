@@ -1,0 +1,207 @@
+"""Host-side checks of the C-ABI library: it loads, exports what the header
+declares, plans the shared schedule correctly and rejects bad arguments
+before touching the GPU.  No kernel runs here.
+
+Schedule properties follow the PTO-ISA AllGather+GEMM README ("optimisation
+notes"): the local row-group first with no wait, remote chunks sent in the
+order they are consumed, 64-128 chunks per source, per-source monotonic
+counters.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import communication_gemm_amd as agg
+from communication_gemm_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "aggemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ag_gemm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(_native.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_native.EXPORTS), "binding and header disagree"
+
+
+def test_options_struct_matches_header_defaults():
+    o = agg.options()
+    assert o.struct_size == ctypes.sizeof(_native.Options)
+    assert o.local_shard == 0 and o.mode == agg.MODE_PIPELINED
+    assert o.debug_drop_chunk == -1 and o.link_gbps == 0.0
+
+
+def test_status_strings():
+    for s in range(6):
+        assert agg.status_string(s)
+    assert "timed out" in agg.status_string(agg.AGG_E_TIMEOUT)
+
+
+def test_pick_chunk_rows_exhaustive():
+    S = np.arange(1, 65537)
+    cr = np.array([agg.pick_chunk_rows(int(s)) for s in S])
+    assert (cr >= 1).all()
+    nchunks = -(-S // cr)
+    assert ((nchunks >= 64) & (nchunks <= 128))[S >= 64].all()
+    assert (cr[S < 64] == 1).all()
+    # chunks tile the shard exactly: the last one is non-empty
+    last = S - (nchunks - 1) * cr
+    assert ((last >= 1) & (last <= cr)).all()
+    assert agg.pick_chunk_rows(0) == 0
+
+
+def test_workspace_bytes():
+    assert agg.workspace_bytes(8, 8192, 4096, 2) == 16384 + 7 * 1024 * 4096 * 2
+    assert agg.workspace_bytes(1, 100, 64, 2) == 16384
+    assert agg.workspace_bytes(3, 100, 64, 2) == 0        # M % n != 0
+    assert agg.workspace_bytes(2, 2, 8, 1) == 16384 + 256  # slots rounded to 256 B
+
+
+def _check_schedule(n, M, K, N, cr=0, **kw):
+    opts = agg.options(**kw)
+    info, tiles, chunks = agg.plan("f16", n, M, K, N, cr, opts, orders=True)
+    S = M // n
+    local = kw.get("local_shard", 0)
+    order = kw.get("send_order") or [(local + q) % n for q in range(1, n)]
+    L = info.m_tiles_per_shard * info.n_tiles
+    # every output tile exactly once
+    keys = {tuple(t[:3]) for t in tiles}
+    assert len(keys) == len(tiles) == n * L
+    # local tiles first, never waited on
+    assert (tiles[:L, 0] == local).all() and (tiles[:L, 3] == 0).all()
+    assert (tiles[L:, 0] != local).all() and (tiles[L:, 3] > 0).all()
+    # a remote tile waits for the chunk holding its last row
+    for sh, m, _, need in tiles[L:]:
+        last_row = min((m + 1) * info.tile_m, S)
+        assert need == -(-last_row // info.chunk_rows)
+    # every remote chunk sent exactly once, in chunk order within a source
+    assert len({tuple(c) for c in chunks}) == len(chunks) == (n - 1) * info.chunks_per_source
+    for s in order:
+        js = chunks[chunks[:, 0] == s, 1]
+        assert (np.diff(js) == 1).all() and js[0] == 0
+    # send order = consumption order: the producer position by which a
+    # remote tile's data is complete never decreases along the tile list
+    pos = {tuple(c): i for i, c in enumerate(chunks)}
+    ready = [pos[(sh, need - 1)] for sh, _, _, need in tiles[L:]]
+    assert all(a <= b for a, b in zip(ready, ready[1:]))
+    return info, tiles, chunks
+
+
+@pytest.mark.parametrize("n,M,K,N,cr", [
+    (2, 256, 256, 128, 32), (2, 2048, 2048, 1024, 0), (4, 4096, 4096, 4096, 0),
+    (8, 8192, 4096, 4096, 0), (3, 300, 296, 168, 7), (5, 5 * 1000, 64, 8, 0),
+    (1, 64, 64, 64, 0)])
+def test_schedule_parallel_links(n, M, K, N, cr):
+    if n == 1:
+        info, tiles, chunks = agg.plan("f16", n, M, K, N, cr, orders=True)
+        assert info.total_chunks == 0 and (tiles[:, 3] == 0).all()
+        return
+    _check_schedule(n, M, K, N, cr)
+
+
+def test_schedule_serial_link_is_source_major():
+    info, tiles, chunks = _check_schedule(4, 4096, 4096, 4096, 0,
+                                          link_model=agg.LINKS_SERIAL, send_order=[3, 1, 2])
+    L = info.m_tiles_per_shard * info.n_tiles
+    srcs = tiles[L:, 0]
+    assert list(dict.fromkeys(srcs.tolist())) == [3, 1, 2]
+    assert list(dict.fromkeys(chunks[:, 0].tolist())) == [3, 1, 2]
+    assert (np.diff(srcs) != 0).sum() == 2
+
+
+def test_schedule_parallel_links_go_m_tile_by_m_tile():
+    info, tiles, _ = _check_schedule(4, 4096, 4096, 4096, 0, local_shard=2)
+    L = info.m_tiles_per_shard * info.n_tiles
+    assert (np.diff(tiles[L:, 1]) >= 0).all()          # m-tiles never go back
+    first = tiles[L:L + 3 * info.n_tiles]
+    assert list(dict.fromkeys(first[:, 0].tolist())) == [3, 0, 1]
+
+
+def test_schedule_chunk_larger_than_tile():
+    # chunks of 100 rows, tiles of 64 rows: several tiles per chunk
+    _check_schedule(2, 800, 64, 64, 100, tile=3)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(local_shard=4), agg.AGG_E_INVALID),
+    (dict(local_shard=-1), agg.AGG_E_INVALID),
+    (dict(send_order=[1, 1, 2]), agg.AGG_E_INVALID),
+    (dict(send_order=[0, 1, 2]), agg.AGG_E_INVALID),     # contains the local shard
+    (dict(send_order=[1, 2, 7]), agg.AGG_E_INVALID),
+    (dict(mode=9), agg.AGG_E_INVALID),
+    (dict(link_model=3), agg.AGG_E_INVALID),
+    (dict(link_gbps=-1.0), agg.AGG_E_INVALID),
+    (dict(tile=17), agg.AGG_E_INVALID),
+])
+def test_plan_rejects_bad_options(kw, status):
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 4, 1024, 64, 64, 0, agg.options(**kw))
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("kind,n,M,K,N,cr,status", [
+    ("f16", 0, 64, 64, 64, 0, agg.AGG_E_INVALID),
+    ("f16", 65, 65, 64, 64, 0, agg.AGG_E_UNSUPPORTED),
+    ("f16", 3, 100, 64, 64, 0, agg.AGG_E_INVALID),        # M % n
+    ("f16", 2, 64, 60, 64, 0, agg.AGG_E_UNSUPPORTED),     # K % 8
+    ("f16", 2, 64, 64, 60, 0, agg.AGG_E_UNSUPPORTED),     # N % 8
+    ("i8", 2, 64, 72, 64, 0, agg.AGG_E_UNSUPPORTED),      # K % 16
+    ("f16", 2, 64, 64, 64, 33, agg.AGG_E_INVALID),        # chunk > S
+    ("f16", 2, 64, 64, 64, -1, agg.AGG_E_INVALID),
+    ("f16", 2, -64, 64, 64, 0, agg.AGG_E_INVALID),
+])
+def test_plan_rejects_bad_sizes(kind, n, M, K, N, cr, status):
+    with pytest.raises(agg.AggError) as e:
+        agg.plan(kind, n, M, K, N, cr)
+    assert e.value.status == status
+
+
+# ---- the real entry points return argument errors before any HIP call ----
+
+FAKE = 0x10000   # a 16-byte aligned address that is never dereferenced
+
+
+def _f16(table, n, B, C, M, K, N, cr=0, opts=None):
+    t = (ctypes.c_void_p * max(n, 1))(*table) if table is not None else None
+    if opts is None:
+        return _native.lib.ag_gemm_f16(t, n, B, C, M, K, N, cr, None)
+    return _native.lib.ag_gemm_f16_ex(t, n, B, C, M, K, N, cr, None, ctypes.byref(opts))
+
+
+def test_entry_point_argument_errors():
+    lib = _native.lib
+    assert _f16(None, 2, FAKE, FAKE, 64, 64, 64) == agg.AGG_E_INVALID
+    assert _f16([FAKE, 0], 2, FAKE, FAKE, 64, 64, 64) == agg.AGG_E_INVALID
+    assert _f16([FAKE, FAKE + 8], 2, FAKE, FAKE, 64, 64, 64) == agg.AGG_E_UNSUPPORTED
+    assert _f16([FAKE, FAKE], 2, FAKE + 2, FAKE, 64, 64, 64) == agg.AGG_E_UNSUPPORTED
+    assert _f16([FAKE, FAKE], 2, FAKE, 0, 64, 64, 64) == agg.AGG_E_INVALID
+    assert _f16([FAKE, FAKE], 2, FAKE, FAKE, 63, 64, 64) == agg.AGG_E_INVALID
+    assert _f16([FAKE, FAKE], 2, FAKE, FAKE, 64, 12, 64) == agg.AGG_E_UNSUPPORTED
+    assert _f16([FAKE, FAKE], 2, FAKE, FAKE, 64, 64, 64, 40) == agg.AGG_E_INVALID
+    bad = agg.options(send_order=[0])
+    assert _f16([FAKE, FAKE], 2, FAKE, FAKE, 64, 64, 64, 0, bad) == agg.AGG_E_INVALID
+    short = agg.options()
+    short.struct_size = 8
+    assert _f16([FAKE, FAKE], 2, FAKE, FAKE, 64, 64, 64, 0, short) == agg.AGG_E_INVALID
+    t = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    # int8: bias and scale are required
+    assert lib.ag_gemm_i8_dequant(t, 2, FAKE, None, FAKE, FAKE, 64, 64, 64, 0, None) == agg.AGG_E_INVALID
+    assert lib.ag_gemm_i8_dequant(t, 2, FAKE, FAKE, FAKE + 2, FAKE, 64, 64, 64, 0, None) == agg.AGG_E_UNSUPPORTED
+    assert lib.ag_gemm_workspace_reset(None, 1 << 20, None) == agg.AGG_E_INVALID
+
+
+def test_empty_problems_are_no_ops():
+    # M = 0 or N = 0: nothing to move or compute, nothing enqueued
+    assert _f16([0, 0], 2, 0, 0, 0, 64, 64) == agg.AGG_OK
+    assert _f16([FAKE, FAKE], 2, FAKE, 0, 64, 64, 0) == agg.AGG_OK
