@@ -25,6 +25,7 @@ struct Track {
     uint32_t epoch;
     uint32_t checked;
     int device;
+    bool used;                 // a call ran on it since the last check
 };
 
 struct Device {
@@ -181,6 +182,7 @@ int run(const Call& c)
         if (rc) return rc;
     }
     const uint32_t epoch = ++tr->epoch;
+    tr->used = true;
     const double timeout_ms = opt->timeout_ms > 0 ? opt->timeout_ms : 2000.0;
     const uint64_t limit = (uint64_t)(timeout_ms * 1e-3 * d->clock_hz);
     uint32_t* header = reinterpret_cast<uint32_t*>(ws);
@@ -283,6 +285,7 @@ int check_track(Track& t, uint32_t* header, hipStream_t st)
         t.tickets = 0;
     }
     t.checked = t.epoch;
+    t.used = false;
     return rc;
 }
 
@@ -357,13 +360,15 @@ int ag_gemm_check(void* stream)
     if (it != g_dev.end() && it->second.ready) {
         Device& d = it->second;
         if (hipStreamSynchronize(d.side) != hipSuccess) return AGG_E_HIP;
-        if (d.ws) {
+        if (d.ws && d.track.used) {
             int r = check_track(d.track, reinterpret_cast<uint32_t*>(d.ws), st);
             if (r) rc = r;
         }
     }
+    // only workspaces that calls used since the last check: one the caller
+    // has freed since then is never touched again
     for (auto& kv : g_user_ws) {
-        if (kv.second.device != dev) continue;
+        if (kv.second.device != dev || !kv.second.used) continue;
         int r = check_track(kv.second, static_cast<uint32_t*>(kv.first), st);
         if (r && !rc) rc = r;
     }

@@ -156,13 +156,16 @@ size_t ag_gemm_workspace_bytes(int n_shards, int64_t M, int64_t K,
                                int elt_bytes);
 
 /* Make a caller-owned workspace ready (zeroes its counter header on
- * `stream`); needed once after allocating it. */
+ * `stream`); needed once after allocating it.  Call ag_gemm_check() after
+ * the last call that used it before freeing it. */
 int ag_gemm_workspace_reset(void *workspace, size_t bytes, void *stream);
 
 /*
- * Synchronise `stream` and report whether the calls issued since the last
- * check on this device timed out (AGG_E_TIMEOUT) or failed in HIP
- * (AGG_E_HIP).  Clears the recorded error and re-arms the counters.
+ * Synchronise `stream` and the library's side stream and report whether
+ * the calls issued since the last check on this device timed out
+ * (AGG_E_TIMEOUT) or failed in HIP (AGG_E_HIP).  Looks only at workspaces
+ * used since the last check; clears the recorded error and re-arms the
+ * counters of a workspace whose call failed.
  */
 int ag_gemm_check(void *stream);
 
