@@ -21,7 +21,6 @@ namespace {
 // epoch whose outcome ag_gemm_check() has reported.
 struct Track {
     uint32_t base[kMaxShards];
-    uint32_t tickets;          // producer tickets handed out so far
     uint32_t epoch;
     uint32_t checked;
     int device;
@@ -37,7 +36,7 @@ struct Device {
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
-    int occ[2][4] = {{0}};
+    int occ[2][8] = {{0}};
 };
 
 std::mutex g_mu;
@@ -74,7 +73,7 @@ int device_state(Device** out)
 
 int occupancy(Device& d, int kind, int tile)
 {
-    int& o = d.occ[kind][tile & 3];
+    int& o = d.occ[kind][tile & 7];
     if (!o) o = consumer_occupancy(kind, tile);
     return o;
 }
@@ -97,7 +96,7 @@ int internal_workspace(Device& d, size_t need, hipStream_t st, char** ws, Track*
             return AGG_E_NOMEM;
         }
         d.ws_bytes = bytes;
-        if (launch_header_reset(reinterpret_cast<uint32_t*>(d.ws), st) != hipSuccess)
+        if (launch_header_reset(reinterpret_cast<uint32_t*>(d.ws), kHeaderBytes, st) != hipSuccess)
             return AGG_E_HIP;
         uint32_t keep = d.track.epoch;
         memset(&d.track, 0, sizeof d.track);
@@ -207,6 +206,7 @@ int run(const Call& c)
     ca.B = static_cast<const char*>(c.B);
     ca.C = c.C;
     ca.counters = header;
+    ca.flags = header + kFlagOffset / 4;
     ca.err = header + kErrorOffset / 4;
     ca.epoch = epoch;
     // the consumer waits on counters only while a producer runs beside it
@@ -216,10 +216,9 @@ int run(const Call& c)
     ca.scale = c.scale;
     ca.acc_out = opt->acc_out;
     pa.counters = header;
+    pa.flags = header + kFlagOffset / 4;
     pa.err = header + kErrorOffset / 4;
     pa.clock = reinterpret_cast<uint64_t*>(ws + kClockOffset);
-    pa.ticket = reinterpret_cast<uint32_t*>(ws + kTicketOffset);
-    pa.ticket_base = tr->tickets;
     pa.epoch = epoch;
     pa.elt = p.elt;
     pa.drop = p.drop_chunk;
@@ -229,13 +228,11 @@ int run(const Call& c)
     int occ = occupancy(*d, kind, p.shape.id);
     if (occ < 1) return AGG_E_HIP;
     int cwgs = p.consumer_wgs;
-    if (!opt->consumer_wgs && cwgs > d->num_cus * occ) cwgs = d->num_cus * occ;
-    // While the consumer waits on counters the producer must find room on
-    // some CU: keep a few consumer slots free so it always can.
-    const bool concurrent = p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer;
-    const int reserve = 16;
-    if (concurrent && cwgs > d->num_cus * occ - reserve)
-        cwgs = d->num_cus * occ - reserve > 0 ? d->num_cus * occ - reserve : 1;
+    // a persistent grid larger than what can be resident at once gains
+    // nothing, and its waiting workgroups would sit in front of the producer
+    if (cwgs > d->num_cus * occ) cwgs = d->num_cus * occ;
+    // No slots are held back for the producer: every consumer kernel leaves
+    // room for producer waves on each CU even at full occupancy.
 
     hipEvent_t* cev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opt->consumer_events));
     auto consumer = [&](hipStream_t st) -> hipError_t {
@@ -250,10 +247,12 @@ int run(const Call& c)
 
     hipError_t e = hipSuccess;
     if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer) {
+        // the consumer goes first so that its persistent workgroups are all
+        // resident; the producer's small workgroups fit beside them
         e = hipEventRecord(d->fork, c.st);
+        if (e == hipSuccess) e = consumer(c.st);
         if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
         if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
-        if (e == hipSuccess) e = consumer(c.st);
         if (e == hipSuccess) e = hipEventRecord(d->join, d->side);
         if (e == hipSuccess) e = hipStreamWaitEvent(c.st, d->join, 0);
     } else {
@@ -264,8 +263,6 @@ int run(const Call& c)
     if (run_producer) {
         for (int i = 0; i < c.n; ++i)
             if (i != s.local) tr->base[i] += (uint32_t)s.cps;
-        // every producer workgroup takes one ticket past the last position
-        tr->tickets += (uint32_t)(total_chunks(s) + p.producer_wgs);
     }
     return AGG_OK;
 }
@@ -279,10 +276,9 @@ int check_track(Track& t, uint32_t* header, hipStream_t st)
     if (err && (int32_t)(err - t.checked) > 0) {
         rc = AGG_E_TIMEOUT;
         // a failed call leaves counters short: start over from zero
-        if (launch_header_reset(header, st) != hipSuccess) return AGG_E_HIP;
+        if (launch_header_reset(header, kHeaderBytes, st) != hipSuccess) return AGG_E_HIP;
         if (hipStreamSynchronize(st) != hipSuccess) return AGG_E_HIP;
         memset(t.base, 0, sizeof t.base);
-        t.tickets = 0;
     }
     t.checked = t.epoch;
     t.used = false;
@@ -336,7 +332,7 @@ int ag_gemm_workspace_reset(void* workspace, size_t bytes, void* stream)
     std::lock_guard<std::mutex> lock(g_mu);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return AGG_E_HIP;
-    if (launch_header_reset(static_cast<uint32_t*>(workspace),
+    if (launch_header_reset(static_cast<uint32_t*>(workspace), kHeaderBytes,
                             static_cast<hipStream_t>(stream)) != hipSuccess)
         return AGG_E_HIP;
     Track t;

@@ -10,19 +10,24 @@
 // last row; what a workgroup has already seen of a counter is remembered,
 // so most tiles pass without touching it.
 //
-// Tile main loop (PTO-ISA README: continuous K accumulation, two-level
-// double buffering): 4 waves, each owning a (BM/2) x (BN/2) block of
-// 32x32 MFMA accumulators kept in registers for the whole K loop; A and B
-// k-slices are staged in LDS, double buffered, the next slice's HBM loads
-// (16 bytes per lane) in flight while the current one is multiplied.
+// Tile main loop (PTO-ISA README: continuous K accumulation, multi-level
+// buffering): 4 waves, each owning a (BM/2) x (BN/2) block of 32x32 MFMA
+// accumulators kept in registers for the whole K loop.  K is walked in
+// slices of SB bytes per row; NS slices live in an LDS ring, NS-1 of them
+// in flight from HBM while the oldest is multiplied.  Inside a slice the
+// operand reads of MFMA step s+1 are issued before the MFMAs of step s, and
+// the last step's MFMAs run across the barrier that publishes the next
+// slice.
 //
-// LDS layout: every operand row holds one k-slice of 128 bytes as eight
-// 16-byte pieces; piece p of row r is stored at position p ^ swz(r), which
-// keeps both the row-wise 16-byte stores and the column-wise MFMA operand
-// reads free of bank conflicts.  A is stored as it lies in memory (row =
-// output row, k along the row); B is stored transposed (row = output
-// column, k along the row), because an MFMA operand lane holds consecutive
-// k of one column.  The transpose happens in registers on the way in.
+// HBM -> LDS moves use the gfx950 direct global-to-LDS load (16 bytes per
+// lane, written lane by lane at the instruction's LDS base), so no
+// registers stage the tiles.  Each slice's loads go through buffer
+// descriptors that end where the matrix does, and a lane whose piece lies
+// beyond K or N gets an out-of-range offset: such loads return zeros.  A is stored as it lies in memory
+// (row = output row, k along the row); B is stored row-major too (row = k)
+// and read with the LDS transpose loads, which hand each lane consecutive k
+// of one column.  16-byte pieces are XOR-swizzled per row, the swizzle
+// applied by choosing which global piece each lane fetches.
 #include "kernels.hpp"
 #include "sync.hpp"
 
@@ -34,24 +39,30 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx16 __attribute__((ext_vector_type(16)));
+typedef int intx2 __attribute__((ext_vector_type(2)));
+typedef short short4_ __attribute__((ext_vector_type(4)));
+#define LDS_PTR __attribute__((address_space(3)))
+#define GLB_PTR __attribute__((address_space(1)))
 
 constexpr int kThreads = 256;   // 4 waves
-constexpr int kRowBytes = 128;  // one k-slice of one operand row in LDS
-
-__device__ __forceinline__ int swz(int r) { return (r + (r >> 3)) & 7; }
-
-__device__ __forceinline__ int lds_off(int row, int piece)
-{
-    return row * kRowBytes + ((piece ^ swz(row)) << 4);
-}
+constexpr int kLdsBytes = 163840;
+// Buffer descriptor word 3 for untyped 32-bit accesses, and an offset no
+// buffer of this code reaches (range checks return zero for it).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // ---- element traits ---------------------------------------------------
+//
+// Both paths move 16-byte pieces: 8 fp16 or 16 int8 values along K.  One
+// MFMA step consumes 32 bytes of K per row (two pieces).  Inside every
+// 16-lane group, lane i of a b16 transpose load receives element i % 4 of
+// the 8 bytes loaded by lane 4e + i/4 (e = 0..3), and of a b8 transpose
+// load byte i % 8 of lane 2e + i/8 (e = 0..7).
 
 struct F16 {
     static constexpr int kElt = 2;        // bytes per element
-    static constexpr int kBK = 64;        // k per slice (128 bytes)
-    static constexpr int kBRows = 8;      // B rows (k) per transposed block
     typedef floatx16 Acc;
+    typedef float Out;                    // element of C
 
     __device__ static Acc zero() { Acc z; for (int i = 0; i < 16; ++i) z[i] = 0.f; return z; }
 
@@ -61,47 +72,43 @@ struct F16 {
             __builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0, 0);
     }
 
-    // One B block: k rows [k, k+8) x columns [n, n+8) -> eight 16-byte
-    // column pieces (8 k values of one column each).
-    __device__ static void load_b(const char* __restrict__ B, int64_t N, int64_t K,
-                                  int64_t k, int64_t n, uint4 (&raw)[8])
+    // B piece swizzle: spreads the 4-row x 32-byte footprint of a transpose
+    // load group, and the second group 8 rows further, over all banks.
+    __device__ static int swz_b(int k) { return 2 * ((k & 3) + 4 * ((k >> 3) & 1)); }
+
+    // B operand of 32 columns, MFMA step kk of the slice: 8 values
+    // k = 16kk + 8(lane/32) + 0..7 from two b16 transpose loads.  b_offset
+    // gives the lane's address of the first load (step 0, half 0) within a
+    // stage's B part; the other loads of the slice are 4 and 16 rows on,
+    // which the swizzle leaves unchanged (it only looks at k % 4 and
+    // k / 8 % 2 of rows 0..15 of a group).
+    template <int LB>
+    __device__ static int b_offset(int lane, int n_base)
     {
-        const bool ncol = n < N;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (ncol && k + r < K)
-                raw[r] = *reinterpret_cast<const uint4*>(B + ((k + r) * N + n) * 2);
-            else
-                raw[r] = make_uint4(0, 0, 0, 0);
-        }
+        const int g = lane >> 4, jj = lane & 15;
+        const int n = n_base + 16 * (g & 1) + 4 * (jj & 3);      // first of 4 halves
+        const int k = 8 * (g >> 1) + (jj >> 2);
+        const int phys = (n >> 3) ^ (swz_b(k) & (LB / 16 - 1));
+        return k * LB + phys * 16 + (n & 7) * 2;
     }
 
-    __device__ static void transpose_b(const uint4 (&raw)[8], uint4 (&col)[8])
+    template <int LB>
+    __device__ static uint4 read_b(const char* p, int kk)
     {
-        // raw[r] holds columns 0..7 of row r as 4 words of 2 halves;
-        // col[c] must hold rows 0..7 of column c.
+        short4_ v[2];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            uint32_t w[4];
-#pragma unroll
-            for (int rp = 0; rp < 4; ++rp) {
-                const uint4& x4 = raw[2 * rp];
-                const uint4& y4 = raw[2 * rp + 1];
-                uint32_t x = (c >> 1) == 0 ? x4.x : (c >> 1) == 1 ? x4.y : (c >> 1) == 2 ? x4.z : x4.w;
-                uint32_t y = (c >> 1) == 0 ? y4.x : (c >> 1) == 1 ? y4.y : (c >> 1) == 2 ? y4.z : y4.w;
-                w[rp] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u))
-                                : ((x & 0xffffu) | (y << 16));
-            }
-            col[c] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        for (int h = 0; h < 2; ++h)
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_PTR short4_*)(p + (16 * kk + 4 * h) * LB));
+        uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
 };
 
 struct I8 {
     static constexpr int kElt = 1;
-    static constexpr int kBK = 128;
-    static constexpr int kBRows = 16;
     typedef intx16 Acc;
+    typedef _Float16 Out;
 
     __device__ static Acc zero() { Acc z; for (int i = 0; i < 16; ++i) z[i] = 0; return z; }
 
@@ -111,179 +118,397 @@ struct I8 {
             __builtin_bit_cast(intx4, a), __builtin_bit_cast(intx4, b), c, 0, 0, 0);
     }
 
-    // One B block: k rows [k, k+16) x columns [n, n+8), as 16 pieces of 8
-    // bytes, kept two rows per uint4 (raw[q] = rows 2q, 2q+1).
-    __device__ static void load_b(const char* __restrict__ B, int64_t N, int64_t K,
-                                  int64_t k, int64_t n, uint4 (&raw)[8])
+    // an 8-row x 16-byte transpose load group lands on 8 distinct pieces
+    __device__ static int swz_b(int k) { return 2 * (k & 7); }
+
+    // B operand: 16 values k = 32kk + 16(lane/32) + 0..15 from two b8
+    // transpose loads, 8 and 32 rows apart (the swizzle only looks at
+    // k % 8).
+    template <int LB>
+    __device__ static int b_offset(int lane, int n_base)
     {
-        const bool ncol = n < N;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
-            if (ncol && k + 2 * q < K)
-                lo = *reinterpret_cast<const uint2*>(B + (k + 2 * q) * N + n);
-            if (ncol && k + 2 * q + 1 < K)
-                hi = *reinterpret_cast<const uint2*>(B + (k + 2 * q + 1) * N + n);
-            raw[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
+        const int g = lane >> 4, jj = lane & 15;
+        const int n = n_base + 16 * (g & 1) + 8 * (jj & 1);      // first of 8 bytes
+        const int k = 16 * (g >> 1) + (jj >> 1);
+        const int phys = (n >> 4) ^ (swz_b(k) & (LB / 16 - 1));
+        return k * LB + phys * 16 + (n & 15);
     }
 
-    __device__ static uint32_t byte_of(const uint4 (&raw)[8], int r, int c)
+    template <int LB>
+    __device__ static uint4 read_b(const char* p, int kk)
     {
-        // byte c (0..7) of row r (0..15)
-        const uint4& v = raw[r >> 1];
-        uint32_t w;
-        const int wi = ((r & 1) << 1) | (c >> 2);
-        w = wi == 0 ? v.x : wi == 1 ? v.y : wi == 2 ? v.z : v.w;
-        return (w >> ((c & 3) * 8)) & 0xffu;
-    }
-
-    __device__ static void transpose_b(const uint4 (&raw)[8], uint4 (&col)[8])
-    {
+        intx2 v[2];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            uint32_t w[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-                w[d] = byte_of(raw, 4 * d, c) | (byte_of(raw, 4 * d + 1, c) << 8) |
-                       (byte_of(raw, 4 * d + 2, c) << 16) | (byte_of(raw, 4 * d + 3, c) << 24);
-            col[c] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        for (int h = 0; h < 2; ++h)
+            v[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (LDS_PTR intx2*)(p + (32 * kk + 8 * h) * LB));
+        return make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
     }
 };
+
+// The lane index, hidden from the optimiser: addresses derived from it are
+// recomputed where they are used (a few VALU ops beside the MFMAs) instead
+// of being hoisted out of the K loop, where they would pin dozens of
+// registers.
+__device__ __forceinline__ int opaque_lane()
+{
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
+// s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt untouched (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads:
+// those would wait for every load still in flight, including the slices
+// being prefetched.  Callers wait for exactly what the barrier publishes
+// (their own finished loads and LDS reads) before it.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // ---- the tile engine --------------------------------------------------
 
-template <class T, int BM, int BN>
+template <class T, int BM, int BN, int SB, int NS>
 struct Engine {
     static constexpr int kTM = BM / 64;             // 32x32 blocks per wave along M
     static constexpr int kTN = BN / 64;             // ... along N
-    static constexpr int kAVec = BM * 8 / kThreads; // A pieces per lane per slice
-    static constexpr int kBBlk = (BN + kThreads - 1) / kThreads; // B blocks per lane
-    static constexpr int kStage = (BM + BN) * kRowBytes;         // one LDS buffer
-    static_assert(kAVec >= 1, "tile too small");
+    static constexpr int kPieces = SB / 16;         // 16-byte pieces per A row
+    static constexpr int kSteps = SB / 32;          // MFMA steps per slice
+    static constexpr int kBK = SB / T::kElt;        // k per slice
+    static constexpr int kLB = BN * T::kElt;        // bytes per B row in LDS
+    static constexpr int kABytes = BM * SB;         // A part of a stage
+    static constexpr int kBBytes = kBK * kLB;       // B part of a stage
+    static constexpr int kStage = kABytes + kBBytes;
+    static constexpr int kLds = NS * kStage;
+    static constexpr int kAInstr = kABytes / 1024;  // 1 KiB per load instruction
+    static constexpr int kBInstr = kBBytes / 1024;
+    static constexpr int kGroup = (kAInstr + kBInstr) / 4;   // load instructions per wave per slice
+    static_assert(kAInstr % 4 == 0 && kBInstr % 4 == 0, "loads split over 4 waves");
+    static_assert(kSteps % 2 == 0 && NS >= 2 && NS <= 4, "pipeline shape");
+    static_assert(kLds + 1024 <= kLdsBytes, "LDS ring too large");
+    static_assert(kGroup * (NS - 2) < 64, "vmcnt range");
 
-    uint4 a_reg[kAVec];
-    uint4 b_reg[kBBlk][8];
+    static constexpr int kAPer = kAInstr / 4;       // A loads per wave per slice
+    static constexpr int kBPer = kBInstr / 4;       // B loads per wave per slice
 
-    __device__ void gload(const char* __restrict__ arows, int64_t rows_valid,
-                          const char* __restrict__ B, int64_t K, int64_t N,
-                          int64_t n0, int64_t k0)
-    {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int u = 0; u < kAVec; ++u) {
-            const int q = tid + u * kThreads;
-            const int row = q >> 3, piece = q & 7;
-            const int64_t k = k0 + (int64_t)piece * (16 / T::kElt);
-            if (row < rows_valid && k < K)
-                a_reg[u] = *reinterpret_cast<const uint4*>(arows + (row * K + k) * T::kElt);
-            else
-                a_reg[u] = make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kBBlk; ++u) {
-            const int b = tid + u * kThreads;
-            if (b < BN) {
-                const int nb = b % (BN / 8), kb = b / (BN / 8);
-                T::load_b(B, N, K, k0 + (int64_t)kb * T::kBRows, n0 + nb * 8, b_reg[u]);
-            }
-        }
-    }
+    // A piece swizzle: the 16 rows of a quarter-wave reading one piece land
+    // on 16 distinct 16-byte bank groups.  Rows 32 apart share it.
+    __device__ static int swz_a(int r) { return (r / (256 / SB)) % kPieces; }
 
-    __device__ void sstore(char* lds)
-    {
-        const int tid = threadIdx.x;
-        char* As = lds;
-        char* Bs = lds + BM * kRowBytes;
-#pragma unroll
-        for (int u = 0; u < kAVec; ++u) {
-            const int q = tid + u * kThreads;
-            *reinterpret_cast<uint4*>(As + lds_off(q >> 3, q & 7)) = a_reg[u];
-        }
-#pragma unroll
-        for (int u = 0; u < kBBlk; ++u) {
-            const int b = tid + u * kThreads;
-            if (b < BN) {
-                const int nb = b % (BN / 8), kb = b / (BN / 8);
-                uint4 col[8];
-                T::transpose_b(b_reg[u], col);
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    *reinterpret_cast<uint4*>(Bs + lds_off(nb * 8 + c, kb)) = col[c];
-            }
-        }
-    }
+    struct Src {
+        const char* arows;   // first A row of the tile
+        int64_t rows_valid;  // A rows that exist
+        const char* B;
+        int64_t K, N, n0;
+    };
 
-    __device__ void compute(const char* lds, typename T::Acc (&acc)[kTM][kTN])
+    // Per-lane byte offsets, computed once per kernel: where this lane's
+    // pieces come from (relative to a slice's A and B origins) and where its
+    // MFMA operands sit in a stage.  All loads and LDS reads of the K loop
+    // are these plus uniform or immediate offsets.
+    struct Lane {
+        uint32_t a_ld[kAPer];   // A piece of load u: row * K + k, in bytes
+        uint32_t b_ld[kBPer];   // B piece of load u: row * N + n, in bytes
+        uint32_t a_rd[kSteps];  // A operand of step s, block 0
+        uint32_t b_rd[kTN];     // first transpose load of block j (step 0, half 0)
+    };
+
+    __device__ static void lane_offsets(Lane& L, int64_t K, int64_t N)
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
-        const char* As = lds;
-        const char* Bs = lds + BM * kRowBytes;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int piece = 2 * kk + (lane >> 5);
-            uint4 af[kTM], bf[kTN];
+        for (int u = 0; u < kAPer; ++u) {
+            const int q = wave * kAPer + u;
+            const int r = q * (1024 / SB) + lane / kPieces;
+            const int p = (lane % kPieces) ^ swz_a(r);
+            L.a_ld[u] = (uint32_t)(r * K * T::kElt + p * 16);
+        }
 #pragma unroll
-            for (int i = 0; i < kTM; ++i)
-                af[i] = *reinterpret_cast<const uint4*>(As + lds_off(wm + i * 32 + (lane & 31), piece));
+        for (int u = 0; u < kBPer; ++u) {
+            const int q = wave * kBPer + u;
+            const int pos = q * 1024 + lane * 16;
+            const int r = pos / kLB;
+            const int p = ((pos % kLB) >> 4) ^ (T::swz_b(r) & (kLB / 16 - 1));
+            L.b_ld[u] = (uint32_t)(r * N * T::kElt + p * 16);
+        }
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+            const int r = wm + (lane & 31);
+            const int piece = 2 * st + (lane >> 5);
+            L.a_rd[st] = (uint32_t)(r * SB + ((piece ^ swz_a(r)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            L.b_rd[j] = (uint32_t)(kABytes + T::template b_offset<kLB>(lane, wn + j * 32));
+    }
+
+    // Loads of one slice into `stage`.  Rows of A past the tile and rows of
+    // B past K fall outside the buffer ranges and read as zero; on an edge
+    // slice (K not reached by a whole slice, or the tile past N) the lanes
+    // whose piece lies beyond K or N are pushed out of range too.
+    __device__ static void load_slice(char* stage, const Src& src, const Lane& L, int64_t k0)
+    {
+        const int64_t elt = T::kElt;
+        const int64_t a_left = (src.rows_valid * src.K - k0) * elt;
+        const int64_t b_left = ((src.K - k0) * src.N - src.n0) * elt;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(src.arows + k0 * elt), 0, (int)(a_left < 0x7fffffff ? a_left : 0x7fffffff),
+            kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(src.B + (k0 * src.N + src.n0) * elt), 0,
+            (int)(b_left < 0x7fffffff ? b_left : 0x7fffffff), kRsrcWord3);
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const bool edge = k0 + kBK > src.K || src.n0 + BN > src.N;
+        if (!edge) {
+#pragma unroll
+            for (int u = 0; u < kAPer; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (LDS_PTR void*)(stage + (wave * kAPer + u) * 1024), 16, L.a_ld[u], 0,
+                    0, 0);
+#pragma unroll
+            for (int u = 0; u < kBPer; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (LDS_PTR void*)(stage + kABytes + (wave * kBPer + u) * 1024), 16,
+                    L.b_ld[u], 0, 0, 0);
+            return;
+        }
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int u = 0; u < kAPer; ++u) {
+            const int q = wave * kAPer + u;
+            const int r = q * (1024 / SB) + lane / kPieces;
+            const int p = (lane % kPieces) ^ swz_a(r);
+            const bool in = k0 + p * (16 / T::kElt) < src.K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (LDS_PTR void*)(stage + q * 1024), 16, in ? L.a_ld[u] : kOutOfRange, 0, 0,
+                0);
+        }
+#pragma unroll
+        for (int u = 0; u < kBPer; ++u) {
+            const int q = wave * kBPer + u;
+            const int pos = q * 1024 + lane * 16;
+            const int r = pos / kLB;
+            const int p = ((pos % kLB) >> 4) ^ (T::swz_b(r) & (kLB / 16 - 1));
+            const bool in = src.n0 + p * (16 / T::kElt) < src.N;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (LDS_PTR void*)(stage + kABytes + q * 1024), 16,
+                in ? L.b_ld[u] : kOutOfRange, 0, 0, 0);
+        }
+    }
+
+    // Operand fragments of one MFMA step (32 bytes of K): kTM A pieces and
+    // kTN B pieces per lane.
+    struct Step {
+        uint4 a[kTM];
+        uint4 b[kTN];
+    };
+
+    __device__ __forceinline__ static void read_step(const char* st, const Lane& L, int kk,
+                                                     Step& f)
+    {
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+            f.a[i] = *reinterpret_cast<const uint4*>(st + L.a_rd[kk] + i * 32 * SB);
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            f.b[j] = T::template read_b<kLB>(st + L.b_rd[j], kk);
+    }
+
+    __device__ __forceinline__ static void mma_step(const Step& f,
+                                                    typename T::Acc (&acc)[kTM][kTN])
+    {
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
 #pragma unroll
             for (int j = 0; j < kTN; ++j)
-                bf[j] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn + j * 32 + (lane & 31), piece));
+                acc[i][j] = T::mma(f.a[i], f.b[j], acc[i][j]);
+    }
+
+    // Wait until at most `behind` slices of this wave's loads are still in
+    // flight (and every LDS read has returned).
+    __device__ __forceinline__ static void wait_slices(int behind)
+    {
+        if constexpr (NS >= 4) {
+            if (behind >= 2) { wait_vm_lgkm0<2 * kGroup>(); return; }
+        }
+        if constexpr (NS >= 3) {
+            if (behind >= 1) { wait_vm_lgkm0<kGroup>(); return; }
+        }
+        wait_vm_lgkm0<0>();
+    }
+
+    // One k-slice.  On entry f0 holds step 0 of `cur`; on exit it holds
+    // step 0 of `nxt` (when there is a next slice).  `ld` is the stage that
+    // receives slice kt + NS - 1.  The three stages are distinct
+    // (restrict), so the compiler does not make the reads wait for the
+    // loads; the explicit waits below do the ordering that matters.
+    __device__ __attribute__((always_inline)) static void slice(
+        const char* __restrict__ cur, const char* __restrict__ nxt, char* __restrict__ ld,
+        bool load, int64_t k_load, int behind, bool more, const Src& src, const Lane& L,
+        Step& f0, Step& f1, typename T::Acc (&acc)[kTM][kTN])
+    {
+        if (load) load_slice(ld, src, L, k_load);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kTM; ++i)
+        for (int st = 1; st < kSteps; ++st) {
+            read_step(cur, L, st, (st & 1) ? f1 : f0);
+            mma_step((st & 1) ? f0 : f1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the next slice has landed for this wave; every wave is done with
+        // reading `cur`, which a later slice's loads will overwrite
+        wait_slices(behind);
+        bare_barrier();
+        if (more) read_step(nxt, L, 0, f0);
+        mma_step(f1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // The whole K loop of one tile over the NS stages starting at `ring`.
+    // The previous tile left no load in flight (its last slice waited for
+    // all of them) and no LDS read pending (its last barrier came after
+    // them), so the ring can be refilled at once.
+    __device__ __attribute__((always_inline)) static void run(
+        char* ring, int nk, const Src& src, const Lane& L, typename T::Acc (&acc)[kTM][kTN])
+    {
 #pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    acc[i][j] = T::mma(af[i], bf[j], acc[i][j]);
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < nk) load_slice(ring + s * kStage, src, L, (int64_t)s * kBK);
+        // slice 0 has landed; the rest of the prologue may still be loading
+        wait_slices((nk < NS - 1 ? nk : NS - 1) - 1);
+        bare_barrier();
+        Step f0, f1;
+        read_step(ring, L, 0, f0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int l = kt + NS - 1;            // slice to load now
+            // slices still loading once slice kt + 1 has landed
+            const int last = l < nk ? l : nk - 1;
+            const int behind = last - (kt + 1) > 0 ? last - (kt + 1) : 0;
+            slice(ring + (kt % NS) * kStage, ring + ((kt + 1) % NS) * kStage,
+                  ring + (l % NS) * kStage, l < nk, (int64_t)l * kBK, behind, kt + 1 < nk,
+                  src, L, f0, f1, acc);
         }
     }
 };
 
-// Output row of accumulator element r of lane `lane` in a 32x32 block.
-__device__ __forceinline__ int acc_row(int lane, int r)
+// Epilogue.  Accumulator element r of lane l in a 32x32 block belongs to
+// row 8(r/4) + 4(l/32) + r%4 and column l%32, so each store instruction
+// writes two 32-column row segments.  The stores go through a buffer
+// descriptor that starts at the tile's first output row and ends after its
+// last valid row: rows past the shard fall out of range and are dropped,
+// columns past N get an out-of-range lane offset, so no store needs a
+// branch or a 64-bit address.  Offsets stay below 2^31 because a tile
+// spans at most 256 rows of at most 2^20 columns of 4 bytes.
+//
+// fp16 path: the fp32 accumulators are the result (written non-temporal:
+// C is not read again here).  int8 path: the int32 accumulator plus the
+// column's bias (modulo 2^32), optionally kept in acc_out, then scaled in
+// fp32 and rounded to fp16.
+constexpr int kStoreStream = 2;   // non-temporal
+
+// One int32 accumulator, copied out of its AGPR where it is used.  Read
+// through plain code, the accumulators of the whole tile would be given
+// VGPRs where the K loop ends and copied there at once.
+__device__ __forceinline__ uint32_t acc_read(int32_t x)
 {
-    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    uint32_t v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
+    return v;
 }
 
-template <class T, int BM, int BN>
-__device__ __forceinline__ void store_tile(const ConsumerArgs& a, int shard, int m,
-                                           int n, typename T::Acc (&acc)[BM / 64][BN / 64])
+template <class T, int BM, int BN, bool kKeepAcc>
+__device__ __forceinline__ void store_tile_as(const ConsumerArgs& a, int shard, int m, int n,
+                                              typename T::Acc (&acc)[BM / 64][BN / 64])
 {
+    typedef typename T::Out Out;
     const Schedule& s = a.s;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = opaque_lane(), wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
-    const int64_t row0 = (int64_t)m * BM;          // within the shard
-    const int64_t col0 = (int64_t)n * BN;
-    const int64_t out_row0 = (int64_t)shard * s.S; // shard's first row of C
+    const int64_t row0 = (int64_t)m * BM;
+    const int64_t left = s.S - row0;
+    const uint32_t rows = (uint32_t)(left < BM ? left : BM);
+    const int64_t origin = ((int64_t)shard * s.S + row0) * s.N + (int64_t)n * BN;
+    const uint32_t row_out = (uint32_t)s.N * (uint32_t)sizeof(Out);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<Out*>(a.C) + origin, 0, (int)(rows * row_out), kRsrcWord3);
+    __amdgpu_buffer_rsrc_t racc = rc;
+    const uint32_t row_acc = (uint32_t)s.N * 4u;
+    if constexpr (kKeepAcc)
+        racc = __builtin_amdgcn_make_buffer_rsrc(a.acc_out + origin, 0, (int)(rows * row_acc),
+                                                 kRsrcWord3);
+    const uint32_t lrow = (uint32_t)(wm + 4 * (lane >> 5));
+    const int64_t col_lane = (int64_t)n * BN + wn + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < BM / 64; ++i) {
+    for (int j = 0; j < BN / 64; ++j) {
+        const bool in = col_lane + 32 * j < s.N;
+        const uint32_t c = (uint32_t)(wn + (lane & 31) + 32 * j);
+        const uint32_t vo = in ? lrow * row_out + c * (uint32_t)sizeof(Out) : kOutOfRange;
+        const uint32_t vacc = in ? lrow * row_acc + c * 4u : kOutOfRange;
+        int32_t bias = 0;
+        float scale = 0.f;
+        if constexpr (T::kElt == 1) {
+            if (in) {
+                bias = a.bias[col_lane + 32 * j];
+                scale = a.scale[col_lane + 32 * j];
+            }
+        }
 #pragma unroll
-        for (int j = 0; j < BN / 64; ++j) {
-            const int64_t col = col0 + wn + j * 32 + (lane & 31);
-            if (col >= s.N) continue;
+        for (int i = 0; i < BM / 64; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = row0 + wm + i * 32 + acc_row(lane, r);
-                if (row >= s.S) continue;
-                const int64_t idx = (out_row0 + row) * s.N + col;
+                const uint32_t roff = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
                 if constexpr (T::kElt == 2) {
-                    static_cast<float*>(a.C)[idx] = acc[i][j][r];
+                    // the element is copied out first: a bit cast applied
+                    // to a vector element directly reads element 0
+                    const float x = acc[i][j][r];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rc,
+                                                          vo + roff * row_out, 0, kStoreStream);
                 } else {
-                    const int32_t v = (int32_t)((uint32_t)acc[i][j][r] + (uint32_t)a.bias[col]);
-                    if (a.acc_out) a.acc_out[idx] = v;
-                    const float f = (float)v * a.scale[col];
-                    static_cast<_Float16*>(a.C)[idx] = (_Float16)f;
+                    const uint32_t v = acc_read(acc[i][j][r]) + (uint32_t)bias;
+                    if constexpr (kKeepAcc)
+                        __builtin_amdgcn_raw_buffer_store_b32(v, racc, vacc + roff * row_acc,
+                                                              0, kStoreStream);
+                    const _Float16 h = (_Float16)((float)(int32_t)v * scale);
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), rc,
+                                                          vo + roff * row_out, 0, kStoreStream);
                 }
             }
+            // one 32x32 block at a time: the scheduler would otherwise copy
+            // many blocks' accumulators into VGPRs ahead of their stores
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
 template <class T, int BM, int BN>
+__device__ __forceinline__ void store_tile(const ConsumerArgs& a, int shard, int m, int n,
+                                           typename T::Acc (&acc)[BM / 64][BN / 64])
+{
+    if constexpr (T::kElt == 1) {
+        if (a.acc_out) {
+            store_tile_as<T, BM, BN, true>(a, shard, m, n, acc);
+            return;
+        }
+    }
+    store_tile_as<T, BM, BN, false>(a, shard, m, n, acc);
+}
+
+template <class T, int BM, int BN, int SB, int NS>
 __global__ __launch_bounds__(kThreads, 1) void consumer_kernel(ConsumerArgs a)
 {
-    typedef Engine<T, BM, BN> E;
+    typedef Engine<T, BM, BN, SB, NS> E;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ uint32_t seen_sh[kMaxShards];
     __shared__ int ok_sh;
@@ -294,31 +519,51 @@ __global__ __launch_bounds__(kThreads, 1) void consumer_kernel(ConsumerArgs a)
     __syncthreads();
 
     const int64_t tiles = total_tiles(s);
-    const int nk = (int)cdiv(s.K, T::kBK);
-    E eng;
+    const int nk = (int)cdiv(s.K, E::kBK);
+    typename E::Lane L;
+    E::lane_offsets(L, s.K, s.N);
 
     for (int64_t p = blockIdx.x; p < tiles; p += gridDim.x) {
         const TileRef t = tile_at(s, p);
         if (t.need > 0 && !a.no_wait) {
-            if (tid == 0) {
+            // wave 0 waits; the other waves hold at the barrier
+            if (tid < 64) {
+                const uint32_t have = seen_sh[t.shard];
                 int ok = 1;
-                if (seen_sh[t.shard] < (uint32_t)t.need) {
-                    const uint32_t target = a.base[t.shard] + (uint32_t)t.need;
-                    const uint32_t v = acquire_wait(a.counters + t.shard * (kCounterStride / 4),
-                                                    target, a.err, a.epoch, a.limit);
-                    if (reached(v, target)) seen_sh[t.shard] = v - a.base[t.shard];
-                    else ok = 0;
+                if (have < (uint32_t)t.need) {
+                    const uint32_t base = a.base[t.shard];
+                    const uint32_t target = base + (uint32_t)t.need;
+                    uint32_t v = target;
+                    if (tid == 0)
+                        v = poll_until(a.counters + t.shard * (kCounterStride / 4), target,
+                                       a.err, a.epoch, a.limit);
+                    v = __builtin_amdgcn_readfirstlane(v);
+                    if (!reached(v, target)) {
+                        ok = 0;
+                    } else {
+                        // the chunks the counter vouches for carry their
+                        // copier's flag; reading them, then acquiring,
+                        // pairs with each copier's release
+                        const uint32_t upto = v - base;
+                        const uint32_t* fl = a.flags + t.shard * kFlagCap;
+                        bool mine = true;
+                        for (uint32_t c = have + tid; c < upto; c += 64)
+                            mine = mine && poll_flag(fl + c, a.epoch, a.err, a.limit);
+                        ok = __builtin_amdgcn_ballot_w64(!mine) == 0;
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                        if (tid == 0 && ok) seen_sh[t.shard] = upto;
+                    }
                 }
-                ok_sh = ok;
+                if (tid == 0) ok_sh = ok;
             }
             __syncthreads();
             if (!ok_sh) break;   // the call has failed; every lane leaves
         }
 
         const int64_t row0 = (int64_t)t.m * BM;
-        const int64_t rows_valid = s.S - row0;
-        const char* arows = a.a[t.shard] + row0 * s.K * T::kElt;
-        const int64_t n0 = (int64_t)t.n * BN;
+        const int64_t rows = s.S - row0;
+        const typename E::Src src{a.a[t.shard] + row0 * s.K * T::kElt,
+                                  rows < BM ? rows : BM, a.B, s.K, s.N, (int64_t)t.n * BN};
 
         typename T::Acc acc[BM / 64][BN / 64];
 #pragma unroll
@@ -326,85 +571,101 @@ __global__ __launch_bounds__(kThreads, 1) void consumer_kernel(ConsumerArgs a)
 #pragma unroll
             for (int j = 0; j < BN / 64; ++j) acc[i][j] = T::zero();
 
-        if (nk > 0) {
-            eng.gload(arows, rows_valid, a.B, s.K, s.N, n0, 0);
-            eng.sstore(lds);
-            __syncthreads();
-            for (int kt = 0; kt < nk; ++kt) {
-                const int cur = kt & 1;
-                if (kt + 1 < nk)
-                    eng.gload(arows, rows_valid, a.B, s.K, s.N, n0,
-                              (int64_t)(kt + 1) * T::kBK);
-                eng.compute(lds + cur * E::kStage, acc);
-                if (kt + 1 < nk) eng.sstore(lds + (cur ^ 1) * E::kStage);
-                __syncthreads();
-            }
-        }
+        if (nk > 0) E::run(lds, nk, src, L, acc);
         store_tile<T, BM, BN>(a, t.shard, t.m, t.n, acc);
     }
 }
 
-template <class T, int BM, int BN>
-hipError_t launch_one(const ConsumerArgs& a, int wgs, hipStream_t st)
-{
-    const size_t lds = 2 * (size_t)Engine<T, BM, BN>::kStage;
-    auto kern = consumer_kernel<T, BM, BN>;
-    static bool attr_set = false;   // one-time opt-in to > 64 KiB of LDS
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
+// Tile configurations: output tile, slice width (bytes of K per row) and
+// LDS ring depth, by the id the host plans with.  The big tiles walk K in
+// 64-byte slices with four stages (three in flight) or in 128-byte slices
+// with two; the small ones use two 128-byte stages so that several
+// workgroups share a CU.
+template <int ID> struct Cfg;
+template <> struct Cfg<1> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 4; };
+template <> struct Cfg<2> { static constexpr int BM = 128, BN = 128, SB = 128, NS = 2; };
+template <> struct Cfg<3> { static constexpr int BM = 64, BN = 64, SB = 128, NS = 2; };
+template <> struct Cfg<4> { static constexpr int BM = 256, BN = 128, SB = 64, NS = 4; };
+template <> struct Cfg<5> { static constexpr int BM = 128, BN = 256, SB = 64, NS = 4; };
+template <> struct Cfg<6> { static constexpr int BM = 256, BN = 256, SB = 128, NS = 2; };
+template <> struct Cfg<7> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 3; };
+
+template <class T, int ID>
+struct Kern {
+    typedef Cfg<ID> C;
+    typedef Engine<T, C::BM, C::BN, C::SB, C::NS> E;
+    static const void* fn()
+    {
+        return reinterpret_cast<const void*>(consumer_kernel<T, C::BM, C::BN, C::SB, C::NS>);
     }
-    hipLaunchKernelGGL(kern, dim3(wgs), dim3(kThreads), lds, st, a);
-    return hipGetLastError();
+    static hipError_t launch(const ConsumerArgs& a, int wgs, hipStream_t st)
+    {
+        static bool attr_set = false;   // one-time opt-in to > 64 KiB of LDS
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               E::kLds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL((consumer_kernel<T, C::BM, C::BN, C::SB, C::NS>), dim3(wgs),
+                           dim3(kThreads), (size_t)E::kLds, st, a);
+        return hipGetLastError();
+    }
+    static int occupancy()
+    {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn(), kThreads, E::kLds) !=
+            hipSuccess)
+            return 0;
+        return n;
+    }
+};
+
+template <class T>
+hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
+{
+    switch (tile_id) {
+    case 1: return Kern<T, 1>::launch(a, wgs, st);
+    case 2: return Kern<T, 2>::launch(a, wgs, st);
+    case 3: return Kern<T, 3>::launch(a, wgs, st);
+    case 4: return Kern<T, 4>::launch(a, wgs, st);
+    case 5: return Kern<T, 5>::launch(a, wgs, st);
+    case 6: return Kern<T, 6>::launch(a, wgs, st);
+    case 7: return Kern<T, 7>::launch(a, wgs, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class T>
+int occupancy_kind(int tile_id)
+{
+    switch (tile_id) {
+    case 1: return Kern<T, 1>::occupancy();
+    case 2: return Kern<T, 2>::occupancy();
+    case 3: return Kern<T, 3>::occupancy();
+    case 4: return Kern<T, 4>::occupancy();
+    case 5: return Kern<T, 5>::occupancy();
+    case 6: return Kern<T, 6>::occupancy();
+    case 7: return Kern<T, 7>::occupancy();
+    default: return 0;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_consumer_f16(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
 {
-    switch (tile_id) {
-    case 1: return launch_one<F16, 256, 256>(a, wgs, st);
-    case 2: return launch_one<F16, 128, 128>(a, wgs, st);
-    case 3: return launch_one<F16, 64, 64>(a, wgs, st);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_kind<F16>(a, tile_id, wgs, st);
 }
 
 hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
 {
-    switch (tile_id) {
-    case 1: return launch_one<I8, 256, 256>(a, wgs, st);
-    case 2: return launch_one<I8, 128, 128>(a, wgs, st);
-    case 3: return launch_one<I8, 64, 64>(a, wgs, st);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_kind<I8>(a, tile_id, wgs, st);
 }
 
 int consumer_occupancy(int kind, int tile_id)
 {
-    int n = 0;
-    size_t lds = 0;
-    const void* f = nullptr;
-    if (kind == 0) {
-        switch (tile_id) {
-        case 1: f = (const void*)consumer_kernel<F16, 256, 256>; lds = 2 * Engine<F16, 256, 256>::kStage; break;
-        case 2: f = (const void*)consumer_kernel<F16, 128, 128>; lds = 2 * Engine<F16, 128, 128>::kStage; break;
-        case 3: f = (const void*)consumer_kernel<F16, 64, 64>; lds = 2 * Engine<F16, 64, 64>::kStage; break;
-        }
-    } else {
-        switch (tile_id) {
-        case 1: f = (const void*)consumer_kernel<I8, 256, 256>; lds = 2 * Engine<I8, 256, 256>::kStage; break;
-        case 2: f = (const void*)consumer_kernel<I8, 128, 128>; lds = 2 * Engine<I8, 128, 128>::kStage; break;
-        case 3: f = (const void*)consumer_kernel<I8, 64, 64>; lds = 2 * Engine<I8, 64, 64>::kStage; break;
-        }
-    }
-    if (!f) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kThreads, lds) != hipSuccess)
-        return 0;
-    return n;
+    return kind == 0 ? occupancy_kind<F16>(tile_id) : occupancy_kind<I8>(tile_id);
 }
 
 }  // namespace agg

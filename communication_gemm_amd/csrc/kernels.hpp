@@ -15,10 +15,9 @@ struct ProducerArgs {
     const char* src[kMaxShards];   // shard base pointers
     char* dst[kMaxShards];         // workspace slot of each remote shard
     uint32_t* counters;            // header base; counter of shard i at i * 32
+    uint32_t* flags;               // chunk flag matrix: [shard][kFlagCap]
     uint32_t* err;
     uint64_t* clock;               // pacing origin slot
-    uint32_t* ticket;              // hands out producer positions in order
-    uint32_t ticket_base;          // its value at the start of the call
     uint32_t base[kMaxShards];     // counter values at the start of the call
     uint32_t epoch;
     int elt;                       // bytes per element
@@ -34,6 +33,7 @@ struct ConsumerArgs {
     const char* B;
     void* C;
     uint32_t* counters;
+    const uint32_t* flags;         // chunk flag matrix
     uint32_t* err;
     uint32_t base[kMaxShards];
     uint32_t epoch;
@@ -50,7 +50,7 @@ hipError_t launch_consumer_f16(const ConsumerArgs& a, int tile_id, int wgs,
                                hipStream_t st);
 hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs,
                               hipStream_t st);
-hipError_t launch_header_reset(uint32_t* header, hipStream_t st);
+hipError_t launch_header_reset(uint32_t* header, size_t bytes, hipStream_t st);
 
 // Workgroups of a consumer tile shape that fit on one CU at once.
 int consumer_occupancy(int kind, int tile_id);

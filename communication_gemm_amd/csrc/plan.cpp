@@ -9,22 +9,32 @@ namespace agg {
 
 namespace {
 
-// Output tiles the consumer kernels are instantiated for.  All use 4 waves
-// (one per SIMD) of 64 lanes; the big tile is what keeps the MFMA pipes fed
-// at large shapes, the small ones give enough tiles to fill 256 CUs and to
-// stream at small shapes.
+// Output tiles the consumer kernels are instantiated for, largest first.
+// All use 4 waves of 64 lanes.  The big tiles keep the MFMA pipes fed at
+// large shapes; the smaller ones give enough tiles to fill 256 CUs and to
+// follow the chunks as they arrive at smaller shapes.  Every one of these
+// kernels, at its full occupancy, leaves registers, LDS and wave slots for
+// producer waves on each CU (checked against the compiler's resource
+// report by the test suite), so the producer always finds room beside a
+// consumer grid that fills the chip.
 const TileShape kF16Shapes[] = {
-    {1, 256, 256, 256},
-    {2, 128, 128, 256},
-    {3, 64, 64, 256},
+    {1, 256, 256, 256, true},
+    {4, 256, 128, 256, true},
+    {5, 128, 256, 256, true},
+    {2, 128, 128, 256, true},
+    {3, 64, 64, 256, true},
+    {6, 256, 256, 256, false},
+    {7, 256, 256, 256, false},
 };
 const TileShape kI8Shapes[] = {
-    {1, 256, 256, 256},
-    {2, 128, 128, 256},
-    {3, 64, 64, 256},
+    {1, 256, 256, 256, true},
+    {4, 256, 128, 256, true},
+    {5, 128, 256, 256, true},
+    {2, 128, 128, 256, true},
+    {3, 64, 64, 256, true},
+    {6, 256, 256, 256, false},
+    {7, 256, 256, 256, false},
 };
-
-bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
@@ -88,7 +98,10 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (num_cus <= 0) num_cus = 256;
     // Row and element offsets are formed in 64-bit; per-tile loop counters
     // in 32-bit.
-    if (S > (1LL << 30) || K > (1LL << 30) || N > (1LL << 30))
+    // The consumer addresses a tile's A rows, a slice's B rows and a
+    // tile's output rows with 32-bit buffer offsets: 256 rows of K, 128
+    // rows of N and 256 rows of N fp32 values must stay below 2^31 bytes.
+    if (S > (1LL << 30) || K > (1LL << 21) || N > (1LL << 20))
         return AGG_E_UNSUPPORTED;
 
     Plan p;
@@ -103,6 +116,9 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.cr = chunk_rows ? chunk_rows : pick_chunk_rows(S);
     if (s.cr < 1) s.cr = 1;
     s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
+    if (n_shards > 1 && s.cps > kFlagCap) return AGG_E_UNSUPPORTED;
+    // the producer moves a chunk with 32-bit buffer offsets
+    if ((int64_t)s.cr * K * (kind == kF16 ? 2 : 1) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
 
     // send order: a permutation of the remote shards
     for (int i = 0; i < kMaxShards; ++i) { s.order[i] = -1; s.slot[i] = -1; }
@@ -127,13 +143,17 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
             if (shapes[i].id == opt->tile) pick = &shapes[i];
         if (!pick) return AGG_E_INVALID;
     } else {
-        // the largest tile that still gives every CU two or more tiles
+        // the largest tile that still gives every CU two or more tiles,
+        // else the smallest
+        const TileShape* smallest = nullptr;
         for (int i = 0; i < count && !pick; ++i) {
+            if (!shapes[i].auto_pick) continue;
             int64_t tiles = (int64_t)n_shards * cdiv(S, shapes[i].tm) *
                             cdiv(N, shapes[i].tn);
             if (tiles >= 2LL * num_cus) pick = &shapes[i];
+            smallest = &shapes[i];
         }
-        if (!pick) pick = &shapes[count - 1];
+        if (!pick) pick = smallest;
     }
     p.shape = *pick;
     s.tm = pick->tm;
@@ -146,7 +166,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     int cw = opt->consumer_wgs ? opt->consumer_wgs : num_cus;
     if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
     if (cw < 1) cw = 1;
-    int pw = opt->producer_wgs ? opt->producer_wgs : (num_cus + 1) / 2;
+    int pw = opt->producer_wgs ? opt->producer_wgs : num_cus;
     if (pw > chunks) pw = (int)(chunks > 0 ? chunks : 1);
     if (pw < 1) pw = 1;
     p.consumer_wgs = cw;

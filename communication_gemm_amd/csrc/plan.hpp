@@ -15,6 +15,9 @@ struct TileShape {
     int id;         // 1-based id accepted by agg_options.tile
     int tm, tn;     // output tile
     int threads;    // workgroup size
+    // Considered by the automatic choice (the others are alternative
+    // pipelines of the same tile, selected by id only).
+    bool auto_pick;
 };
 
 // Output tiles the consumer kernels are built for, per path.

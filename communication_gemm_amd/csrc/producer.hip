@@ -1,19 +1,30 @@
 // producer.hip -- the chunk producer: plays the links of an AllGather on
 // one GPU.  For every remote shard it moves chunk after chunk (chunk_rows
 // rows x all of K) from the shard into the shard's workspace slot and
-// releases each chunk on the shard's counter (PTO-ISA AllGather+GEMM
-// README: the communication kernel transfers a chunk, then notifies with an
-// atomic add on the per-source counter; several communication blocks per
-// destination; chunks sent in the order they are consumed).
+// publishes it (PTO-ISA AllGather+GEMM README: the communication kernel
+// transfers a chunk, then notifies with an atomic add on the per-source
+// summary counter; several communication blocks per destination; chunks
+// sent in the order they are consumed).
 //
-// Workgroups take producer positions from a ticket counter, in order.
-// Copies proceed in parallel; releases of one source happen in chunk order
-// (a workgroup waits for the source's counter to reach its chunk index
-// before adding one), so a counter value c always means "chunks 0..c-1 are
-// in place".  A workgroup only ever waits for a chunk whose ticket was taken
-// before its own, by a workgroup that is already running, so the producer
-// makes progress however few of its workgroups fit on the GPU at once.
+// Workgroup w copies producer positions w, w + G, w + 2G, ... (send order)
+// in parallel with the others.  A finished chunk is published in two
+// steps, neither of which waits for another workgroup:
+//   * its copier makes the data visible at device scope (release fence)
+//     and stores the call's epoch in the chunk's flag (the chunk flag
+//     matrix);
+//   * the copier then advances the source's summary counter over every
+//     flagged chunk contiguous with it, in one compare-and-swap.
+// So a counter value c means "chunks 0..c-1 are flagged", and the counter
+// moves as soon as the lowest missing chunk lands, whoever copied it.  The
+// consumer waits on the counter, then reads the flags of the chunks it
+// needs and acquires: that pairs with each copier's release directly, so
+// the counter itself carries no data ordering and is updated with relaxed
+// atomics only (no cache maintenance on the counter path).
 //
+// Pacing: with ticks_per_byte > 0 a chunk is not flagged before the
+// emulated link could have carried it (parallel links: its own source's
+// bytes up to and including the chunk; serial link: everything sent before
+// it too), measured from the moment the first producer workgroup started.
 #include "kernels.hpp"
 #include "sync.hpp"
 
@@ -21,28 +32,76 @@ namespace agg {
 
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned int)))) unsigned int v4u32;
+
 constexpr int kProducerThreads = 256;
+constexpr int kRsrcWord3 = 0x00020000;   // untyped 32-bit buffer accesses
+// Cache policy of the copy's stores: device scope (written through to
+// memory), so the release before a chunk's flag has little left to write
+// back.
+constexpr int kStoreDevice = 16;
 constexpr int kUnroll = 8;   // 16-byte vectors in flight per lane
 
+// Copy `bytes` (a multiple of 16, both ends 16-byte aligned) with buffer
+// accesses: lane offsets stay fixed, the step goes into the scalar offset,
+// so eight 16-byte loads per lane are in flight on a handful of registers.
 __device__ __forceinline__ void copy_bytes(char* __restrict__ dst,
                                            const char* __restrict__ src,
                                            int64_t bytes)
 {
-    // bytes is a multiple of 16 and both pointers are 16-byte aligned
-    const int64_t nvec = bytes >> 4;
-    const uint4* s = reinterpret_cast<const uint4*>(src);
-    uint4* d = reinterpret_cast<uint4*>(dst);
-    const int tid = threadIdx.x;
-    const int64_t step = (int64_t)kProducerThreads * kUnroll;
-    int64_t i = tid;
-    for (; i + (kUnroll - 1) * kProducerThreads < nvec; i += step) {
-        uint4 v[kUnroll];
+    const int32_t n = (int32_t)bytes;   // a chunk is far below 2 GiB
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, n, kRsrcWord3);
+    const int32_t lane_off = threadIdx.x * 16;
+    constexpr int32_t kStep = kProducerThreads * 16;          // bytes per sweep
+    int32_t base = 0;
+    for (; base + kUnroll * kStep <= n; base += kUnroll * kStep) {
+        u32x4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = s[i + u * kProducerThreads];
+        for (int u = 0; u < kUnroll; ++u)
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, lane_off, base + u * kStep, 0));
+        // every load is issued before the first store: the compiler would
+        // otherwise pair each load with its store and keep one in flight
+        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]),
+                          "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) d[i + u * kProducerThreads] = v[u];
+        for (int u = 0; u < kUnroll; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[u]), rd,
+                                                   lane_off, base + u * kStep, kStoreDevice);
     }
-    for (; i < nvec; i += kProducerThreads) d[i] = s[i];
+    // the tail: lanes past the end are out of range and do nothing.  The
+    // whole offset goes into the lane offset, which the range check covers
+    for (; base < n; base += kStep) {
+        const int32_t off = base + lane_off;
+        v4u32 t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(t, rd, off, 0, kStoreDevice);
+    }
+}
+
+// Advance the summary counter of one source over the flagged chunks that
+// follow it.  Runs on one lane after that lane's own flag store has been
+// performed at device scope.  Two lanes racing: the compare-and-swap lets
+// one win and the other re-read; a flag stored before a lane reads the
+// counter is seen either by that lane or by the lane that moved the
+// counter past the chunk before it.
+__device__ void advance(uint32_t* ctr, const uint32_t* flags, uint32_t base, int cps,
+                        uint32_t epoch)
+{
+    for (;;) {
+        uint32_t cur = load_agent(ctr);
+        int rel = (int)(cur - base);
+        int k = 0;
+        while (rel + k < cps && load_agent(flags + rel + k) == epoch) ++k;
+        if (k == 0) return;
+        uint32_t want = cur;
+        __hip_atomic_compare_exchange_strong(ctr, &want, cur + (uint32_t)k,
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        // success or not, look again: more chunks may have landed
+    }
 }
 
 }  // namespace
@@ -53,55 +112,62 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     const int64_t total = total_chunks(s);
     const int64_t row_bytes = s.K * a.elt;
     __shared__ uint64_t origin_sh;
-    __shared__ int failed_sh;
+    __shared__ int stop_sh;
 
     if (threadIdx.x == 0) {
         origin_sh = a.ticks_per_byte > 0.0 ? pacing_origin(a.clock, a.epoch) : 0;
-        failed_sh = 0;
+        stop_sh = 0;
     }
     __syncthreads();
 
-    __shared__ int64_t pos_sh;
-    for (;;) {
-        if (threadIdx.x == 0) {
-            uint32_t t = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-            pos_sh = failed_sh ? total : (int64_t)(uint32_t)(t - a.ticket_base);
-        }
-        __syncthreads();
-        const int64_t c = pos_sh;
-        if (c >= total) break;
+    for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
         const ChunkRef r = chunk_at(s, c);
         const int64_t row0 = (int64_t)r.j * s.cr;
         const int64_t rows = chunk_row_end(s, r.j) - row0;
         copy_bytes(a.dst[r.shard] + row0 * row_bytes,
                    a.src[r.shard] + row0 * row_bytes, rows * row_bytes);
-        // each lane makes its own stores visible at device scope before
-        // the single release below
+        // each lane makes its own stores visible at device scope before the
+        // chunk is flagged
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t* ctr = a.counters + r.shard * (kCounterStride / 4);
-            const uint32_t mine = a.base[r.shard] + (uint32_t)r.j;
-            uint32_t seen = acquire_wait(ctr, mine, a.err, a.epoch, a.limit);
-            if (!reached(seen, mine)) {
-                failed_sh = 1;
-            } else {
-                if (a.ticks_per_byte > 0.0) {
-                    double b = (double)paced_bytes(s, r, a.elt);
-                    wait_until(origin_sh, (uint64_t)(b * a.ticks_per_byte));
+        if (threadIdx.x == 0 && c != a.drop) {
+            bool ok = true;
+            if (a.ticks_per_byte > 0.0) {
+                const double b = (double)paced_bytes(s, r, a.elt);
+                const double delta = b * a.ticks_per_byte;
+                // a pace slower than the wait limit is a failed call, not a hang
+                if (delta > (double)a.limit) {
+                    raise_error(a.err, a.epoch);
+                    ok = false;
+                } else {
+                    wait_until(origin_sh, (uint64_t)delta);
                 }
-                if (c != a.drop) release_add(ctr);
+            }
+            if (ok) {
+                uint32_t* flags = a.flags + r.shard * kFlagCap;
+                __hip_atomic_store(flags + r.j, a.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                // the flag store is performed before the counter is read
+                __builtin_amdgcn_s_waitcnt(0);
+                advance(a.counters + r.shard * (kCounterStride / 4), flags,
+                        a.base[r.shard], s.cps, a.epoch);
             }
         }
+        // stop early once a workgroup of this call has failed; one lane
+        // decides for the whole workgroup, so every wave leaves together
+        if (threadIdx.x == 0) stop_sh = reached(load_agent(a.err), a.epoch);
         __syncthreads();
+        if (stop_sh) break;
     }
 }
 
-// Counters, error word and pacing slot to zero; run once per workspace.
-__global__ void header_reset_kernel(uint32_t* header)
+// Zero `bytes` bytes of a workspace header (counters, error word, pacing
+// slot, chunk flags).
+__global__ void header_reset_kernel(uint32_t* header, size_t words)
 {
-    for (int i = threadIdx.x; i < kHeaderBytes / 4; i += blockDim.x) header[i] = 0;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
+         i += (size_t)gridDim.x * blockDim.x)
+        header[i] = 0;
 }
 
 hipError_t launch_producer(const ProducerArgs& a, int wgs, hipStream_t st)
@@ -110,9 +176,9 @@ hipError_t launch_producer(const ProducerArgs& a, int wgs, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_header_reset(uint32_t* header, hipStream_t st)
+hipError_t launch_header_reset(uint32_t* header, size_t bytes, hipStream_t st)
 {
-    hipLaunchKernelGGL(header_reset_kernel, dim3(1), dim3(256), 0, st, header);
+    hipLaunchKernelGGL(header_reset_kernel, dim3(64), dim3(256), 0, st, header, bytes / 4);
     return hipGetLastError();
 }
 

@@ -19,14 +19,18 @@ namespace agg {
 
 constexpr int kMaxShards = 64;
 
-// Workspace header: one 32-bit counter per source shard, each on its own
-// 128-byte line, then the error word, the pacing origin and the producer's
-// ticket counter.
+// Workspace header: one 32-bit summary counter per source shard, each on
+// its own 128-byte line, then the error word, the pacing origin, a page of
+// zeros and the chunk flag matrix (one
+// 32-bit word per source and chunk: the epoch of the call that released
+// it).  The PTO-ISA README keeps the same two structures: per-chunk flags
+// and a per-source summary counter.
 constexpr int kCounterStride = 128;                       // bytes
 constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
 constexpr int kClockOffset = kErrorOffset + kCounterStride; // uint64
-constexpr int kTicketOffset = kClockOffset + kCounterStride; // uint32
-constexpr int kHeaderBytes = 16384;
+constexpr int kFlagOffset = 16384;
+constexpr int kFlagCap = 1024;       // chunks per source the flag matrix holds
+constexpr int kHeaderBytes = kFlagOffset + kMaxShards * kFlagCap * 4;
 
 struct Schedule {
     int n_shards;

@@ -1,10 +1,10 @@
 // sync.hpp -- device-side counter primitives for chunk readiness.
 //
-// A source's counter only grows: the producer adds one per chunk, in chunk
-// order, after the chunk's stores (PTO-ISA AllGather+GEMM README: the
-// communication side atomically increments a per-source summary counter
-// after each chunk; the compute side blocks until the counter reaches the
-// value it expects).  Counters are never reset between calls: each call
+// A source's summary counter only grows: it counts the chunks of the
+// source that are in place, in chunk order (PTO-ISA AllGather+GEMM README:
+// the communication side atomically increments a per-source summary
+// counter after each chunk; the compute side blocks until the counter
+// reaches the value it expects).  Counters are never reset between calls: each call
 // waits for base + n, the base carried over from the calls before it, and
 // values are compared modulo 2^32 (the Pallas collective matmul page waits
 // on a semaphore whose expected value grows with the step for the same
@@ -42,13 +42,12 @@ __device__ inline void raise_error(uint32_t* err, uint32_t epoch)
     __hip_atomic_fetch_max(err, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Poll *ctr until it reaches `target` (mod 2^32).  On success the caller's
-// later loads see everything released before the counter got there.
-// Returns the value seen, or target - 1 after a time-out or after another
-// workgroup of the same call failed.
-__device__ inline uint32_t acquire_wait(const uint32_t* ctr, uint32_t target,
-                                        uint32_t* err, uint32_t epoch,
-                                        uint64_t limit)
+// Poll *ctr until it reaches `target` (mod 2^32).  Relaxed: the caller
+// acquires through the chunk flags afterwards.  Returns the value seen, or
+// target - 1 after a time-out or after another workgroup of the same call
+// failed.
+__device__ inline uint32_t poll_until(const uint32_t* ctr, uint32_t target, uint32_t* err,
+                                      uint32_t epoch, uint64_t limit)
 {
     uint32_t v = load_agent(ctr);
     if (!reached(v, target)) {
@@ -66,14 +65,28 @@ __device__ inline uint32_t acquire_wait(const uint32_t* ctr, uint32_t target,
             v = load_agent(ctr);
         } while (!reached(v, target));
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return v;
 }
 
-// Release one more chunk: every lane has already fenced its own stores.
-__device__ inline void release_add(uint32_t* ctr)
+// Wait (relaxed) until *flag holds `epoch`; false after a time-out or a
+// failure elsewhere in the call.
+__device__ inline bool poll_flag(const uint32_t* flag, uint32_t epoch, uint32_t* err,
+                                 uint64_t limit)
 {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (load_agent(flag) == epoch) return true;
+    const uint64_t t0 = ticks();
+    uint32_t spins = 0;
+    while (load_agent(flag) != epoch) {
+        __builtin_amdgcn_s_sleep(2);
+        if ((++spins & 31u) == 0) {
+            if (reached(load_agent(err), epoch)) return false;
+            if (ticks() - t0 > limit) {
+                raise_error(err, epoch);
+                return false;
+            }
+        }
+    }
+    return true;
 }
 
 // Pacing origin shared by all producer workgroups of one call: the first

@@ -47,7 +47,8 @@ enum agg_status {
     AGG_OK = 0,
     AGG_E_INVALID = 1,      /* null pointer, bad size, bad permutation ...   */
     AGG_E_UNSUPPORTED = 2,  /* K or N not a multiple of the vector width,
-                               misaligned pointer, too many shards          */
+                               misaligned pointer, too many shards, or a
+                               size past the limits below                   */
     AGG_E_NOMEM = 3,        /* workspace allocation failed                   */
     AGG_E_HIP = 4,          /* a HIP call failed while enqueueing            */
     AGG_E_TIMEOUT = 5       /* a counter wait exceeded its limit (reported
@@ -83,7 +84,8 @@ typedef struct agg_options {
     double link_gbps;       /* per-link pacing in GB/s (1e9 B/s); 0 = none    */
     int link_model;         /* enum agg_link_model (default PARALLEL)         */
     int producer_wgs;       /* producer workgroups; 0 = automatic            */
-    int consumer_wgs;       /* consumer workgroups; 0 = automatic            */
+    int consumer_wgs;       /* consumer workgroups; 0 = automatic; at most
+                               as many as can be resident at once are used */
     int tile;               /* consumer tile shape id; 0 = automatic          */
     int32_t *acc_out;       /* int8 path only: optional DEVICE int32 [M, N]
                                receiving A x B + bias before the dequant     */
@@ -110,6 +112,9 @@ void ag_gemm_options_init(agg_options *opt);
  *              alias any input.
  *   chunk_rows rows per chunk; 0 = ag_gemm_pick_chunk_rows(S).
  * Requires K % 8 == 0 and N % 8 == 0 (AGG_E_UNSUPPORTED otherwise).
+ * Size limits (both paths, AGG_E_UNSUPPORTED past them): n_shards <= 64,
+ * S <= 2^30, K <= 2^21, N <= 2^20, at most 1024 chunks per shard, and one
+ * chunk (chunk_rows x K elements) below 2 GiB.
  * Inputs are read only; the caller owns every buffer.
  * PTO-ISA AllGather+GEMM README, "spec" table: A M x K fp16 (split on M
  * across ranks), B K x N fp16 (replicated), C M x N fp32.

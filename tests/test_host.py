@@ -62,10 +62,19 @@ def test_pick_chunk_rows_exhaustive():
 
 
 def test_workspace_bytes():
-    assert agg.workspace_bytes(8, 8192, 4096, 2) == 16384 + 7 * 1024 * 4096 * 2
-    assert agg.workspace_bytes(1, 100, 64, 2) == 16384
+    header = agg.workspace_bytes(1, 100, 64, 2)           # one shard: no slots
+    assert header >= 16384 + 64 * 1024 * 4                 # counters + chunk flags
+    assert agg.workspace_bytes(8, 8192, 4096, 2) == header + 7 * 1024 * 4096 * 2
     assert agg.workspace_bytes(3, 100, 64, 2) == 0        # M % n != 0
-    assert agg.workspace_bytes(2, 2, 8, 1) == 16384 + 256  # slots rounded to 256 B
+    assert agg.workspace_bytes(2, 2, 8, 1) == header + 256  # slots rounded to 256 B
+
+
+def test_too_many_chunks_per_source_rejected():
+    # the chunk flag matrix holds 1024 chunks per source
+    agg.plan("f16", 2, 2 * 1024, 64, 64, 1)
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 2, 2 * 1025, 64, 64, 1)
+    assert e.value.status == agg.AGG_E_UNSUPPORTED
 
 
 def _check_schedule(n, M, K, N, cr=0, **kw):
@@ -160,6 +169,9 @@ def test_plan_rejects_bad_options(kw, status):
     ("f16", 2, 64, 64, 64, 33, agg.AGG_E_INVALID),        # chunk > S
     ("f16", 2, 64, 64, 64, -1, agg.AGG_E_INVALID),
     ("f16", 2, -64, 64, 64, 0, agg.AGG_E_INVALID),
+    ("f16", 2, 64, (1 << 21) + 8, 64, 0, agg.AGG_E_UNSUPPORTED),   # K limit
+    ("f16", 2, 64, 64, (1 << 20) + 8, 0, agg.AGG_E_UNSUPPORTED),   # N limit
+    ("i8", 2, 64, 64, (1 << 20) + 8, 0, agg.AGG_E_UNSUPPORTED),
 ])
 def test_plan_rejects_bad_sizes(kind, n, M, K, N, cr, status):
     with pytest.raises(agg.AggError) as e:
