@@ -17,10 +17,25 @@ consumer kernel (its own average duration, taken with HIP events recorded
 around it on the stream it runs on), the oracle's CPU throughput on a bounded
 sample of the same workload, and the overlap figures (compute-only,
 copy-only, sequential and pipelined times).
+
+The roofline's "traffic" (HBM bytes per consumer launch) comes from hardware
+counters, which this script cannot read itself: rocprofv3 --pmc runs of
+FETCH_SIZE and WRITE_SIZE over this script, scaled by what the same counters
+read for a plain device copy of known size (``--copy-calibration``), are
+kept in profiles/ together with a digest of the consumer's sources; the
+figure is reported only while those sources are unchanged.
+
+Helpers for those runs:
+    python bench.py --copy-calibration      a 256 MiB device copy, 10 times
+    python bench.py --pmc-summary DIR       mean counter value per dispatch
+                                            and kernel, from rocprofv3 CSVs
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +54,12 @@ PEAK_HBM_GBS = 8000.0
 # Ascend 910B1 (each rank computes all of C): other hardware, context only.
 PAGE_TFLOPS_8192 = 191.03
 
+# counter-derived traffic of the consumer on the default workload
+TRAFFIC_NOTE = os.path.join(ROOT, "profiles", "consumer_f16_8x1024x4096x4096_traffic.md")
+CONSUMER_SOURCES = ["consumer.hip", "kernels.hpp", "schedule.hpp", "sync.hpp"]
+COPY_CALIBRATION_BYTES = 256 << 20
+MODES = {"pipelined": 0, "compute": 1, "sequential": 2, "copy": 3}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -53,7 +74,66 @@ def parse():
     ap.add_argument("--no-modes", action="store_true", help="skip the overlap modes")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--mode", choices=sorted(MODES), default="pipelined",
+                    help="mode of the timed calls; hardware-counter runs use 'compute' "
+                         "because counter collection serializes the two kernels")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="summarise rocprofv3 counter CSVs under DIR and exit")
     return ap.parse_args()
+
+
+def consumer_digest():
+    h = hashlib.sha256()
+    for name in CONSUMER_SOURCES:
+        with open(os.path.join(ROOT, "communication_gemm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload):
+    """HBM bytes per consumer launch from the counter note, or None when the
+    note is missing, is for another workload, or predates the sources."""
+    try:
+        with open(TRAFFIC_NOTE) as f:
+            kv = dict(line.strip()[2:].split(": ", 1) for line in f
+                      if line.startswith("- ") and ": " in line)
+    except OSError:
+        return None
+    if kv.get("consumer_sources_sha256") != consumer_digest():
+        return None
+    if kv.get("workload") != workload:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def pmc_summary(root):
+    """Mean of every counter per dispatch, by kernel, over rocprofv3's
+    counter_collection CSV files under `root`."""
+    acc = {}
+    for path in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"),
+                                 recursive=True)):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                key = (row["Kernel_Name"], row["Counter_Name"])
+                s, n = acc.get(key, (0.0, 0))
+                acc[key] = (s + float(row["Counter_Value"]), n + 1)
+    for (kern, ctr), (s, n) in sorted(acc.items()):
+        print(f"{ctr:16s} {s / n:18.1f}  dispatches={n:4d}  {kern}")
+
+
+def copy_calibration(torch):
+    x = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_CALIBRATION_BYTES, "copies": 10,
+                      "expected_fetch_KiB": COPY_CALIBRATION_BYTES / 1024,
+                      "expected_write_KiB": COPY_CALIBRATION_BYTES / 1024}), flush=True)
 
 
 def timed(torch, fn, steps, warmup, with_consumer=True):
@@ -107,13 +187,14 @@ def run_f16(args, torch, agg, synth):
 
     flops = 2.0 * case.M * case.K * case.N
     res = {}
-    t_pipe, c_pipe = timed(torch, call(agg.MODE_PIPELINED), args.steps, args.warmup)
+    t_pipe, c_pipe = timed(torch, call(MODES[args.mode]), args.steps, args.warmup,
+                           with_consumer=args.mode != "copy")
     rc = agg.check()
     if rc:
-        raise SystemExit(f"pipelined run failed: {agg.status_string(rc)}")
-    res["pipelined_ms"] = t_pipe
+        raise SystemExit(f"{args.mode} run failed: {agg.status_string(rc)}")
+    res["step_ms"] = t_pipe
     res["consumer_ms"] = c_pipe
-    if not args.no_modes:
+    if not args.no_modes and args.mode == "pipelined":
         t_copy, _ = timed(torch, call(agg.MODE_COPY_ONLY), args.steps, 2, with_consumer=False)
         t_comp, c_comp = timed(torch, call(agg.MODE_COMPUTE_ONLY), args.steps, 2)
         t_seq, _ = timed(torch, call(agg.MODE_SEQUENTIAL), args.steps, 2)
@@ -131,6 +212,7 @@ def run_f16(args, torch, agg, synth):
     info, _, _ = agg.plan("f16", case.n_shards, case.M, case.K, case.N, cr,
                           agg.options(tile=args.tile))
     res["tile"] = [info.tile_m, info.tile_n]
+    res["tile_id"] = info.tile_id
     res["chunk_rows"] = info.chunk_rows
     res["tflops"] = flops / (t_pipe * 1e-3) / 1e12
     return case, res, flops, (shards, B)
@@ -167,11 +249,17 @@ def cpu_baseline(case, inputs, budget_s):
     shards, B = inputs
     rows_all = np.arange(case.M, dtype=np.int64)
     rng = np.random.default_rng(0)
-    probe = rng.choice(rows_all, 16, replace=False)
-    t0 = time.perf_counter()
-    oracle.ag_gemm_f16(shards, B, rows=probe, with_abs=False)
-    dt = time.perf_counter() - t0
-    n = int(min(case.M, max(16, 16 * budget_s / max(dt, 1e-6))))
+    # two probes separate the per-call cost (converting B) from the per-row
+    # cost, so the sample can be sized to the time budget
+    probe_t = []
+    for k in (16, 128):
+        probe = rng.choice(rows_all, k, replace=False)
+        t0 = time.perf_counter()
+        oracle.ag_gemm_f16(shards, B, rows=probe, with_abs=False)
+        probe_t.append(time.perf_counter() - t0)
+    per_row = max((probe_t[1] - probe_t[0]) / 112, 1e-7)
+    fixed = max(probe_t[0] - 16 * per_row, 0.0)
+    n = int(min(case.M, max(16, (budget_s - fixed) / per_row)))
     rows = np.sort(rng.choice(rows_all, n, replace=False))
     t0 = time.perf_counter()
     oracle.ag_gemm_f16(shards, B, rows=rows, with_abs=False)
@@ -185,6 +273,9 @@ def cpu_baseline(case, inputs, budget_s):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the streamed "
               "AllGather is emulated on a single device; there is no multi-GPU path.",
@@ -196,9 +287,12 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     case, res, flops, inputs = run_f16(args, torch, agg, synth)
     cons_ms = res["consumer_ms"]
-    achieved = flops / (cons_ms * 1e-3) / 1e12
+    achieved = flops / (cons_ms * 1e-3) / 1e12 if cons_ms else None
     line = {
         "metric": METRIC,
         "value": round(res["tflops"], 2),
@@ -206,7 +300,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["pipelined_ms"], 5),
+        "ms_per_step": round(res["step_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(res["tflops"] / PAGE_TFLOPS_8192, 3) if case.case_id == 4 else None,
@@ -215,15 +309,17 @@ def main():
         "config": {"workload": case.name + " streamed AllGather+GEMM, fp16 in, fp32 out",
                    "M": case.M, "K": case.K, "N": case.N, "n_shards": case.n_shards,
                    "chunk_rows": res["chunk_rows"], "tile": res["tile"],
+                   "tile_id": res["tile_id"],
                    "link_gbps": case.link_gbps if args.link_gbps is None else args.link_gbps,
-                   "parallelism": "single GPU, shards emulated"},
+                   "mode": args.mode, "parallelism": "single GPU, shards emulated"},
         "frac_of_peak": round(res["tflops"] / PEAK_F16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                     "traffic": None, "kernel": "consumer (persistent MFMA GEMM)",
-                     "kernel_ms": round(cons_ms, 5)},
+        "roofline": None if achieved is None else {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "traffic": stored_traffic(case.name) if args.tile == 0 else None,
+            "kernel": "consumer (persistent MFMA GEMM)", "kernel_ms": round(cons_ms, 5)},
         "overlap": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()
-                    if k not in ("tflops", "tile", "chunk_rows")},
+                    if k not in ("tflops", "tile", "tile_id", "chunk_rows")},
         "baseline_note": "vs_baseline divides by the PTO-ISA page's 8-card 8192x4096x4096 "
                          "figure on Ascend 910B1 (191.03 TFLOPS): other hardware, context only",
     }

@@ -65,6 +65,7 @@ class PlanInfo(ctypes.Structure):
         ("total_chunks", ctypes.c_int64),
         ("consumer_wgs", ctypes.c_int),
         ("producer_wgs", ctypes.c_int),
+        ("tile_id", ctypes.c_int),
     ]
 
 

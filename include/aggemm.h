@@ -193,6 +193,7 @@ typedef struct agg_plan_info {
     int64_t total_chunks;   /* (n_shards - 1) * chunks_per_source */
     int consumer_wgs;       /* persistent consumer grid */
     int producer_wgs;       /* producer grid */
+    int tile_id;            /* consumer tile configuration (agg_options.tile) */
 } agg_plan_info;
 
 /*

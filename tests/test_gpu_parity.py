@@ -78,7 +78,7 @@ def test_large_cases_sampled_rows(agg, orc, cid):
     check_f16(C[rows], Co, So, c.name)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("n,S,K,N,cr", [
     (3, 100, 296, 168, 7),     # ragged rows, k tail, n tail, ragged last chunk
     (2, 300, 520, 264, 0),
@@ -89,6 +89,35 @@ def test_ragged_shapes(agg, orc, tile, n, S, K, N, cr):
     C = run_f16(agg, shards, B, cr, agg.options(tile=tile))
     Co, So = orc.ag_gemm_f16(shards, B)
     check_f16(C, Co, So, f"tile {tile} n={n} S={S} K={K} N={N}")
+
+
+@pytest.mark.parametrize("kind,tile", [("f16", 6), ("f16", 3), ("i8", 6), ("i8", 2)])
+def test_no_store_outside_c(agg, kind, tile):
+    """Rows past the last shard's end and columns past N are dropped by
+    the epilogue: memory right after C (and after acc_out) keeps its
+    contents."""
+    n, S, K, N = 2, 300, 64, 200          # ragged m- and n-tiles
+    M = n * S
+    pad = 1 << 16
+    if kind == "f16":
+        shards, B = synth.make_f16(M, K, N, n, "normal", 33000 + tile)
+        ts = [dev(s, torch) for s in shards]
+        buf = torch.full((M * N + pad,), 12345.0, device="cuda")
+        agg.ag_gemm_f16(ts, dev(B, torch), buf[:M * N].view(M, N), 0,
+                        opts=agg.options(tile=tile))
+        assert agg.check() == 0
+        assert (buf[M * N:] == 12345.0).all()
+        assert torch.isfinite(buf[:M * N]).all()
+    else:
+        shards, B, bias, scale = synth.make_i8(M, K, N, n, 33100 + tile)
+        ts = [dev(s, torch) for s in shards]
+        buf = torch.full((M * N + pad,), 7.0, dtype=torch.float16, device="cuda")
+        acc = torch.full((M * N + pad,), -5, dtype=torch.int32, device="cuda")
+        agg.ag_gemm_i8_dequant(ts, dev(B, torch), dev(bias, torch), dev(scale, torch),
+                               buf[:M * N].view(M, N), 0,
+                               opts=agg.options(tile=tile, acc_out=acc[:M * N]))
+        assert agg.check() == 0
+        assert (buf[M * N:] == 7.0).all() and (acc[M * N:] == -5).all()
 
 
 def test_single_shard_and_many_shards(agg, orc):
@@ -130,7 +159,7 @@ def test_i8_small_full(agg, orc):
     check_i8(acc, D, ao, Do, "int8 small")
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7])
 def test_i8_ragged(agg, orc, tile):
     shards, B, bias, scale = synth.make_i8(3 * 77, 16 * 37, 8 * 19, 3, 41000 + tile)
     acc, D = run_i8(agg, shards, B, bias, scale, 9, dict(tile=tile))
