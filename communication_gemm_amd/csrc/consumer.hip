@@ -72,9 +72,19 @@ struct F16 {
             __builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0, 0);
     }
 
-    // B piece swizzle: spreads the 4-row x 32-byte footprint of a transpose
-    // load group, and the second group 8 rows further, over all banks.
-    __device__ static int swz_b(int k) { return 2 * ((k & 3) + 4 * ((k >> 3) & 1)); }
+    // B piece swizzle, LB bytes per B row in LDS.  The LDS has 64 banks of
+    // 4 bytes, and a b64 read is served 32 lanes (256 bytes) at a time: two
+    // 16-lane groups that read 4 rows x 32 bytes each, 16 pieces in all.
+    // Rows of 256 bytes or more all start at bank 0, so rows k % 4 = 0..3
+    // take pieces 4(k % 4) + 0..3; rows of 128 bytes alternate halves of
+    // the banks, so rows k and k + 2 are set apart instead.  It depends only
+    // on k % 4 (and k / 2 % 2), which the slice's other reads, 4 and 16 rows
+    // on, leave unchanged.
+    template <int LB>
+    __device__ static int swz_b(int k)
+    {
+        return LB >= 256 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+    }
 
     // B operand of 32 columns, MFMA step kk of the slice: 8 values
     // k = 16kk + 8(lane/32) + 0..7 from two b16 transpose loads.  b_offset
@@ -88,7 +98,7 @@ struct F16 {
         const int g = lane >> 4, jj = lane & 15;
         const int n = n_base + 16 * (g & 1) + 4 * (jj & 3);      // first of 4 halves
         const int k = 8 * (g >> 1) + (jj >> 2);
-        const int phys = (n >> 3) ^ (swz_b(k) & (LB / 16 - 1));
+        const int phys = (n >> 3) ^ (swz_b<LB>(k) & (LB / 16 - 1));
         return k * LB + phys * 16 + (n & 7) * 2;
     }
 
@@ -118,8 +128,16 @@ struct I8 {
             __builtin_bit_cast(intx4, a), __builtin_bit_cast(intx4, b), c, 0, 0, 0);
     }
 
-    // an 8-row x 16-byte transpose load group lands on 8 distinct pieces
-    __device__ static int swz_b(int k) { return 2 * (k & 7); }
+    // B piece swizzle: a b64 read's 32 lanes read 8 rows x 32 bytes, 16
+    // pieces in all.  Rows of 256 bytes or more start at bank 0 and take
+    // pieces 2(k % 8) + 0..1; rows of 128 bytes alternate halves of the
+    // banks, so the even rows (and the odd ones) are spread by k / 2 % 4.
+    // Reads 8 and 32 rows on keep the same swizzle.
+    template <int LB>
+    __device__ static int swz_b(int k)
+    {
+        return LB >= 256 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
+    }
 
     // B operand: 16 values k = 32kk + 16(lane/32) + 0..15 from two b8
     // transpose loads, 8 and 32 rows apart (the swizzle only looks at
@@ -130,7 +148,7 @@ struct I8 {
         const int g = lane >> 4, jj = lane & 15;
         const int n = n_base + 16 * (g & 1) + 8 * (jj & 1);      // first of 8 bytes
         const int k = 16 * (g >> 1) + (jj >> 1);
-        const int phys = (n >> 4) ^ (swz_b(k) & (LB / 16 - 1));
+        const int phys = (n >> 4) ^ (swz_b<LB>(k) & (LB / 16 - 1));
         return k * LB + phys * 16 + (n & 15);
     }
 
@@ -240,7 +258,7 @@ struct Engine {
             const int q = wave * kBPer + u;
             const int pos = q * 1024 + lane * 16;
             const int r = pos / kLB;
-            const int p = ((pos % kLB) >> 4) ^ (T::swz_b(r) & (kLB / 16 - 1));
+            const int p = ((pos % kLB) >> 4) ^ (T::template swz_b<kLB>(r) & (kLB / 16 - 1));
             L.b_ld[u] = (uint32_t)(r * N * T::kElt + p * 16);
         }
 #pragma unroll
@@ -300,7 +318,7 @@ struct Engine {
             const int q = wave * kBPer + u;
             const int pos = q * 1024 + lane * 16;
             const int r = pos / kLB;
-            const int p = ((pos % kLB) >> 4) ^ (T::swz_b(r) & (kLB / 16 - 1));
+            const int p = ((pos % kLB) >> 4) ^ (T::template swz_b<kLB>(r) & (kLB / 16 - 1));
             const bool in = src.n0 + p * (16 / T::kElt) < src.N;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (LDS_PTR void*)(stage + kABytes + q * 1024), 16,

@@ -9,17 +9,18 @@
 // Workgroup w copies producer positions w, w + G, w + 2G, ... (send order)
 // in parallel with the others.  A finished chunk is published in two
 // steps, neither of which waits for another workgroup:
-//   * its copier makes the data visible at device scope (release fence)
-//     and stores the call's epoch in the chunk's flag (the chunk flag
-//     matrix);
+//   * its copier waits until its device-scope (write-through) stores of
+//     the chunk are performed in memory, then stores the call's epoch in
+//     the chunk's flag (the chunk flag matrix);
 //   * the copier then advances the source's summary counter over every
 //     flagged chunk contiguous with it, in one compare-and-swap.
 // So a counter value c means "chunks 0..c-1 are flagged", and the counter
 // moves as soon as the lowest missing chunk lands, whoever copied it.  The
 // consumer waits on the counter, then reads the flags of the chunks it
-// needs and acquires: that pairs with each copier's release directly, so
-// the counter itself carries no data ordering and is updated with relaxed
-// atomics only (no cache maintenance on the counter path).
+// needs and acquires (invalidating what its caches may hold of the
+// workspace): a flag it sees was stored after the chunk's data reached
+// memory.  Counter and flags are updated with relaxed device-scope
+// atomics only, and the producer does no cache maintenance at all.
 //
 // Pacing: with ticks_per_byte > 0 a chunk is not flagged before the
 // emulated link could have carried it (parallel links: its own source's
@@ -38,8 +39,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned int)))) unsigned int 
 constexpr int kProducerThreads = 256;
 constexpr int kRsrcWord3 = 0x00020000;   // untyped 32-bit buffer accesses
 // Cache policy of the copy's stores: device scope (written through to
-// memory), so the release before a chunk's flag has little left to write
-// back.
+// memory), so that their completion alone publishes them.
 constexpr int kStoreDevice = 16;
 constexpr int kUnroll = 8;   // 16-byte vectors in flight per lane
 
@@ -126,9 +126,12 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
         const int64_t rows = chunk_row_end(s, r.j) - row0;
         copy_bytes(a.dst[r.shard] + row0 * row_bytes,
                    a.src[r.shard] + row0 * row_bytes, rows * row_bytes);
-        // each lane makes its own stores visible at device scope before the
-        // chunk is flagged
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // The copy's stores are device-scope stores, written through to
+        // memory; a store is counted done only once it is performed there.
+        // Waiting for them is what makes the chunk visible to every CU, so
+        // no cache write-back (what a release fence would add, for the
+        // whole L2) is needed before the flag.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0 && c != a.drop) {
             bool ok = true;
