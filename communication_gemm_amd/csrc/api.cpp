@@ -36,7 +36,7 @@ struct Device {
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
-    int occ[2][8] = {{0}};
+    int occ[2][16] = {{0}};   // by tile id
 };
 
 std::mutex g_mu;
@@ -73,7 +73,7 @@ int device_state(Device** out)
 
 int occupancy(Device& d, int kind, int tile)
 {
-    int& o = d.occ[kind][tile & 7];
+    int& o = d.occ[kind][tile & 15];
     if (!o) o = consumer_occupancy(kind, tile);
     return o;
 }
@@ -233,6 +233,8 @@ int run(const Call& c)
     if (cwgs > d->num_cus * occ) cwgs = d->num_cus * occ;
     // No slots are held back for the producer: every consumer kernel leaves
     // room for producer waves on each CU even at full occupancy.
+    // Workgroups of one XCD take neighbouring tiles (the grid is now final).
+    ca.s.xf = pick_xcd_split(ca.s, cwgs);
 
     hipEvent_t* cev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opt->consumer_events));
     auto consumer = [&](hipStream_t st) -> hipError_t {

@@ -44,7 +44,6 @@ typedef short short4_ __attribute__((ext_vector_type(4)));
 #define LDS_PTR __attribute__((address_space(3)))
 #define GLB_PTR __attribute__((address_space(1)))
 
-constexpr int kThreads = 256;   // 4 waves
 constexpr int kLdsBytes = 163840;
 // Buffer descriptor word 3 for untyped 32-bit accesses, and an offset no
 // buffer of this code reaches (range checks return zero for it).
@@ -197,10 +196,12 @@ __device__ __forceinline__ void bare_barrier()
 
 // ---- the tile engine --------------------------------------------------
 
-template <class T, int BM, int BN, int SB, int NS>
+template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
 struct Engine {
-    static constexpr int kTM = BM / 64;             // 32x32 blocks per wave along M
-    static constexpr int kTN = BN / 64;             // ... along N
+    static constexpr int kWaves = WM * WN;          // WM x WN grid of waves
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kTM = BM / (32 * WM);      // 32x32 blocks per wave along M
+    static constexpr int kTN = BN / (32 * WN);      // ... along N
     static constexpr int kPieces = SB / 16;         // 16-byte pieces per A row
     static constexpr int kSteps = SB / 32;          // MFMA steps per slice
     static constexpr int kBK = SB / T::kElt;        // k per slice
@@ -211,14 +212,15 @@ struct Engine {
     static constexpr int kLds = NS * kStage;
     static constexpr int kAInstr = kABytes / 1024;  // 1 KiB per load instruction
     static constexpr int kBInstr = kBBytes / 1024;
-    static constexpr int kGroup = (kAInstr + kBInstr) / 4;   // load instructions per wave per slice
-    static_assert(kAInstr % 4 == 0 && kBInstr % 4 == 0, "loads split over 4 waves");
+    static constexpr int kGroup = (kAInstr + kBInstr) / kWaves;   // loads per wave per slice
+    static_assert(kAInstr % kWaves == 0 && kBInstr % kWaves == 0, "loads split over the waves");
+    static_assert(kTM >= 1 && kTN >= 1 && kWaves % 4 == 0, "wave grid");
     static_assert(kSteps % 2 == 0 && NS >= 2 && NS <= 4, "pipeline shape");
     static_assert(kLds + 1024 <= kLdsBytes, "LDS ring too large");
     static_assert(kGroup * (NS - 2) < 64, "vmcnt range");
 
-    static constexpr int kAPer = kAInstr / 4;       // A loads per wave per slice
-    static constexpr int kBPer = kBInstr / 4;       // B loads per wave per slice
+    static constexpr int kAPer = kAInstr / kWaves;  // A loads per wave per slice
+    static constexpr int kBPer = kBInstr / kWaves;  // B loads per wave per slice
 
     // A piece swizzle: the 16 rows of a quarter-wave reading one piece land
     // on 16 distinct 16-byte bank groups.  Rows 32 apart share it.
@@ -245,7 +247,7 @@ struct Engine {
     __device__ static void lane_offsets(Lane& L, int64_t K, int64_t N)
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
+        const int wm = (wave / WN) * (BM / WM), wn = (wave % WN) * (BN / WN);
 #pragma unroll
         for (int u = 0; u < kAPer; ++u) {
             const int q = wave * kAPer + u;
@@ -354,6 +356,20 @@ struct Engine {
                 acc[i][j] = T::mma(f.a[i], f.b[j], acc[i][j]);
     }
 
+    // Issue order inside one MFMA step: an LDS read of the next step after
+    // each MFMA, so the reads overlap the matrix pipe instead of queueing
+    // in front of it (one wave per SIMD cannot hide a stall otherwise).
+    __device__ __forceinline__ static void interleave_reads()
+    {
+        constexpr int kR = kTM + 2 * kTN;   // LDS reads per step
+        constexpr int kM = kTM * kTN;       // MFMAs per step
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            if (i < kR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+    }
+
     // Wait until at most `behind` slices of this wave's loads are still in
     // flight (and every LDS read has returned).
     __device__ __forceinline__ static void wait_slices(int behind)
@@ -383,14 +399,19 @@ struct Engine {
         for (int st = 1; st < kSteps; ++st) {
             read_step(cur, L, st, (st & 1) ? f1 : f0);
             mma_step((st & 1) ? f0 : f1, acc);
+            interleave_reads();
             __builtin_amdgcn_sched_barrier(0);
         }
         // the next slice has landed for this wave; every wave is done with
         // reading `cur`, which a later slice's loads will overwrite
         wait_slices(behind);
         bare_barrier();
-        if (more) read_step(nxt, L, 0, f0);
+        // after the last slice this reads a stage nobody uses again (still
+        // inside the ring); reading unconditionally keeps the reads and the
+        // MFMAs in one scheduling region
+        read_step(nxt, L, 0, f0);
         mma_step(f1, acc);
+        interleave_reads();
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -446,14 +467,15 @@ __device__ __forceinline__ uint32_t acc_read(int32_t x)
     return v;
 }
 
-template <class T, int BM, int BN, bool kKeepAcc>
-__device__ __forceinline__ void store_tile_as(const ConsumerArgs& a, int shard, int m, int n,
-                                              typename T::Acc (&acc)[BM / 64][BN / 64])
+template <class T, int BM, int BN, int WM, int WN, bool kKeepAcc>
+__device__ __forceinline__ void store_tile_as(
+    const ConsumerArgs& a, int shard, int m, int n,
+    typename T::Acc (&acc)[BM / (32 * WM)][BN / (32 * WN)])
 {
     typedef typename T::Out Out;
     const Schedule& s = a.s;
     const int lane = opaque_lane(), wave = threadIdx.x >> 6;
-    const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
+    const int wm = (wave / WN) * (BM / WM), wn = (wave % WN) * (BN / WN);
     const int64_t row0 = (int64_t)m * BM;
     const int64_t left = s.S - row0;
     const uint32_t rows = (uint32_t)(left < BM ? left : BM);
@@ -469,7 +491,7 @@ __device__ __forceinline__ void store_tile_as(const ConsumerArgs& a, int shard, 
     const uint32_t lrow = (uint32_t)(wm + 4 * (lane >> 5));
     const int64_t col_lane = (int64_t)n * BN + wn + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < BN / 64; ++j) {
+    for (int j = 0; j < BN / (32 * WN); ++j) {
         const bool in = col_lane + 32 * j < s.N;
         const uint32_t c = (uint32_t)(wn + (lane & 31) + 32 * j);
         const uint32_t vo = in ? lrow * row_out + c * (uint32_t)sizeof(Out) : kOutOfRange;
@@ -483,7 +505,7 @@ __device__ __forceinline__ void store_tile_as(const ConsumerArgs& a, int shard, 
             }
         }
 #pragma unroll
-        for (int i = 0; i < BM / 64; ++i) {
+        for (int i = 0; i < BM / (32 * WM); ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const uint32_t roff = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
@@ -510,30 +532,31 @@ __device__ __forceinline__ void store_tile_as(const ConsumerArgs& a, int shard, 
     }
 }
 
-template <class T, int BM, int BN>
-__device__ __forceinline__ void store_tile(const ConsumerArgs& a, int shard, int m, int n,
-                                           typename T::Acc (&acc)[BM / 64][BN / 64])
+template <class T, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void store_tile(
+    const ConsumerArgs& a, int shard, int m, int n,
+    typename T::Acc (&acc)[BM / (32 * WM)][BN / (32 * WN)])
 {
     if constexpr (T::kElt == 1) {
         if (a.acc_out) {
-            store_tile_as<T, BM, BN, true>(a, shard, m, n, acc);
+            store_tile_as<T, BM, BN, WM, WN, true>(a, shard, m, n, acc);
             return;
         }
     }
-    store_tile_as<T, BM, BN, false>(a, shard, m, n, acc);
+    store_tile_as<T, BM, BN, WM, WN, false>(a, shard, m, n, acc);
 }
 
-template <class T, int BM, int BN, int SB, int NS>
-__global__ __launch_bounds__(kThreads, 1) void consumer_kernel(ConsumerArgs a)
+template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs a)
 {
-    typedef Engine<T, BM, BN, SB, NS> E;
+    typedef Engine<T, BM, BN, SB, NS, WM, WN> E;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ uint32_t seen_sh[kMaxShards];
     __shared__ int ok_sh;
 
     const Schedule& s = a.s;
     const int tid = threadIdx.x;
-    for (int i = tid; i < kMaxShards; i += kThreads) seen_sh[i] = 0;
+    for (int i = tid; i < kMaxShards; i += E::kThreads) seen_sh[i] = 0;
     __syncthreads();
 
     const int64_t tiles = total_tiles(s);
@@ -541,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 1) void consumer_kernel(ConsumerArgs a)
     typename E::Lane L;
     E::lane_offsets(L, s.K, s.N);
 
-    for (int64_t p = blockIdx.x; p < tiles; p += gridDim.x) {
+    for (int64_t p = wg_position(s, blockIdx.x, gridDim.x); p < tiles; p += gridDim.x) {
         const TileRef t = tile_at(s, p);
         if (t.need > 0 && !a.no_wait) {
             // wave 0 waits; the other waves hold at the barrier
@@ -583,38 +606,43 @@ __global__ __launch_bounds__(kThreads, 1) void consumer_kernel(ConsumerArgs a)
         const typename E::Src src{a.a[t.shard] + row0 * s.K * T::kElt,
                                   rows < BM ? rows : BM, a.B, s.K, s.N, (int64_t)t.n * BN};
 
-        typename T::Acc acc[BM / 64][BN / 64];
+        typename T::Acc acc[E::kTM][E::kTN];
 #pragma unroll
-        for (int i = 0; i < BM / 64; ++i)
+        for (int i = 0; i < E::kTM; ++i)
 #pragma unroll
-            for (int j = 0; j < BN / 64; ++j) acc[i][j] = T::zero();
+            for (int j = 0; j < E::kTN; ++j) acc[i][j] = T::zero();
 
         if (nk > 0) E::run(lds, nk, src, L, acc);
-        store_tile<T, BM, BN>(a, t.shard, t.m, t.n, acc);
+        store_tile<T, BM, BN, WM, WN>(a, t.shard, t.m, t.n, acc);
     }
 }
 
-// Tile configurations: output tile, slice width (bytes of K per row) and
-// LDS ring depth, by the id the host plans with.  The big tiles walk K in
-// 64-byte slices with four stages (three in flight) or in 128-byte slices
-// with two; the small ones use two 128-byte stages so that several
-// workgroups share a CU.
+// Tile configurations: output tile, slice width (bytes of K per row), LDS
+// ring depth and wave grid, by the id the host plans with.  The big tiles
+// walk K in 64-byte slices with four stages (three in flight) or in
+// 128-byte slices with two; the small ones use two 128-byte stages so that
+// several workgroups share a CU.  The 8-wave configurations put two waves
+// on each SIMD (each owning a 128 x 64 block), so that one wave's waits
+// overlap the other's MFMAs.
 template <int ID> struct Cfg;
-template <> struct Cfg<1> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 4; };
-template <> struct Cfg<2> { static constexpr int BM = 128, BN = 128, SB = 128, NS = 2; };
-template <> struct Cfg<3> { static constexpr int BM = 64, BN = 64, SB = 128, NS = 2; };
-template <> struct Cfg<4> { static constexpr int BM = 256, BN = 128, SB = 64, NS = 4; };
-template <> struct Cfg<5> { static constexpr int BM = 128, BN = 256, SB = 64, NS = 4; };
-template <> struct Cfg<6> { static constexpr int BM = 256, BN = 256, SB = 128, NS = 2; };
-template <> struct Cfg<7> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 3; };
+template <> struct Cfg<1> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WM = 2, WN = 2; };
+template <> struct Cfg<2> { static constexpr int BM = 128, BN = 128, SB = 128, NS = 2, WM = 2, WN = 2; };
+template <> struct Cfg<3> { static constexpr int BM = 64, BN = 64, SB = 128, NS = 2, WM = 2, WN = 2; };
+template <> struct Cfg<4> { static constexpr int BM = 256, BN = 128, SB = 64, NS = 4, WM = 2, WN = 2; };
+template <> struct Cfg<5> { static constexpr int BM = 128, BN = 256, SB = 64, NS = 4, WM = 2, WN = 2; };
+template <> struct Cfg<6> { static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WM = 2, WN = 2; };
+template <> struct Cfg<7> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 3, WM = 2, WN = 2; };
+template <> struct Cfg<8> { static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WM = 2, WN = 4; };
+template <> struct Cfg<9> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WM = 2, WN = 4; };
 
 template <class T, int ID>
 struct Kern {
     typedef Cfg<ID> C;
-    typedef Engine<T, C::BM, C::BN, C::SB, C::NS> E;
+    typedef Engine<T, C::BM, C::BN, C::SB, C::NS, C::WM, C::WN> E;
     static const void* fn()
     {
-        return reinterpret_cast<const void*>(consumer_kernel<T, C::BM, C::BN, C::SB, C::NS>);
+        return reinterpret_cast<const void*>(
+            consumer_kernel<T, C::BM, C::BN, C::SB, C::NS, C::WM, C::WN>);
     }
     static hipError_t launch(const ConsumerArgs& a, int wgs, hipStream_t st)
     {
@@ -625,14 +653,14 @@ struct Kern {
             if (e != hipSuccess) return e;
             attr_set = true;
         }
-        hipLaunchKernelGGL((consumer_kernel<T, C::BM, C::BN, C::SB, C::NS>), dim3(wgs),
-                           dim3(kThreads), (size_t)E::kLds, st, a);
+        hipLaunchKernelGGL((consumer_kernel<T, C::BM, C::BN, C::SB, C::NS, C::WM, C::WN>),
+                           dim3(wgs), dim3(E::kThreads), (size_t)E::kLds, st, a);
         return hipGetLastError();
     }
     static int occupancy()
     {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn(), kThreads, E::kLds) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn(), E::kThreads, E::kLds) !=
             hipSuccess)
             return 0;
         return n;
@@ -650,6 +678,8 @@ hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t 
     case 5: return Kern<T, 5>::launch(a, wgs, st);
     case 6: return Kern<T, 6>::launch(a, wgs, st);
     case 7: return Kern<T, 7>::launch(a, wgs, st);
+    case 8: return Kern<T, 8>::launch(a, wgs, st);
+    case 9: return Kern<T, 9>::launch(a, wgs, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -665,6 +695,8 @@ int occupancy_kind(int tile_id)
     case 5: return Kern<T, 5>::occupancy();
     case 6: return Kern<T, 6>::occupancy();
     case 7: return Kern<T, 7>::occupancy();
+    case 8: return Kern<T, 8>::occupancy();
+    case 9: return Kern<T, 9>::occupancy();
     default: return 0;
     }
 }

@@ -10,8 +10,9 @@ namespace agg {
 namespace {
 
 // Output tiles the consumer kernels are instantiated for, largest first.
-// Ids 1, 6 and 7 are the same 256 x 256 tile with different K pipelines
-// (see the Cfg table of the consumer); 6 measured fastest on both paths,
+// Ids 1, 6, 7, 8 and 9 are the same 256 x 256 tile with different K
+// pipelines and wave grids (see the Cfg table of the consumer); 8 (eight
+// waves, two per SIMD, 128-byte slices) measured fastest on both paths,
 // so it is the one picked automatically.
 // All use 4 waves of 64 lanes.  The big tiles keep the MFMA pipes fed at
 // large shapes; the smaller ones give enough tiles to fill 256 CUs and to
@@ -21,22 +22,26 @@ namespace {
 // report by the test suite), so the producer always finds room beside a
 // consumer grid that fills the chip.
 const TileShape kF16Shapes[] = {
-    {6, 256, 256, 256, true},
+    {8, 256, 256, 512, true},
     {4, 256, 128, 256, true},
     {5, 128, 256, 256, true},
     {2, 128, 128, 256, true},
     {3, 64, 64, 256, true},
     {1, 256, 256, 256, false},
+    {6, 256, 256, 256, false},
     {7, 256, 256, 256, false},
+    {9, 256, 256, 512, false},
 };
 const TileShape kI8Shapes[] = {
-    {6, 256, 256, 256, true},
+    {8, 256, 256, 512, true},
     {4, 256, 128, 256, true},
     {5, 128, 256, 256, true},
     {2, 128, 128, 256, true},
     {3, 64, 64, 256, true},
     {1, 256, 256, 256, false},
+    {6, 256, 256, 256, false},
     {7, 256, 256, 256, false},
+    {9, 256, 256, 512, false},
 };
 
 }  // namespace

@@ -114,6 +114,10 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     __shared__ uint64_t origin_sh;
     __shared__ int stop_sh;
 
+    // Producer waves share their SIMDs with consumer waves; they issue few
+    // instructions, each of which the consumer is waiting on, so they go
+    // first when both are ready.
+    __builtin_amdgcn_s_setprio(3);
     if (threadIdx.x == 0) {
         origin_sh = a.ticks_per_byte > 0.0 ? pacing_origin(a.clock, a.epoch) : 0;
         stop_sh = 0;

@@ -20,11 +20,10 @@ namespace agg {
 constexpr int kMaxShards = 64;
 
 // Workspace header: one 32-bit summary counter per source shard, each on
-// its own 128-byte line, then the error word, the pacing origin, a page of
-// zeros and the chunk flag matrix (one
-// 32-bit word per source and chunk: the epoch of the call that released
-// it).  The PTO-ISA README keeps the same two structures: per-chunk flags
-// and a per-source summary counter.
+// its own 128-byte line, then the error word, the pacing origin and the
+// chunk flag matrix (one 32-bit word per source and chunk: the epoch of the
+// call that released it).  The PTO-ISA README keeps the same two
+// structures: per-chunk flags and a per-source summary counter.
 constexpr int kCounterStride = 128;                       // bytes
 constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
 constexpr int kClockOffset = kErrorOffset + kCounterStride; // uint64
@@ -44,7 +43,10 @@ struct Schedule {
     int64_t S, K, N;
     int order[kMaxShards]; // order[0] = local, order[1..n-1] = send order
     int slot[kMaxShards];  // workspace slot of each shard (-1: local)
+    int xf;                // XCD blocking: n-tile groups per round (0 = none)
 };
+
+constexpr int kXcds = 8;   // XCDs; workgroup b of a grid runs on XCD b % 8
 
 AGG_HD int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -145,6 +147,56 @@ AGG_HD ChunkRef chunk_at(const Schedule& s, int64_t c)
     r.j = (int)(c % s.cps);
     r.shard = s.order[1 + r.src];
     return r;
+}
+
+// ---- XCD-aware placement of consumer positions --------------------------
+//
+// The consumer runs in rounds: round r covers positions [rG, rG + G) of the
+// tile list, one per workgroup (G = grid size).  A round is a set of row
+// panels (one shard's m-tile, all nt n-tiles) taken in list order.  Each of
+// the 8 XCDs has its own L2, and the workgroups of one XCD are b = x,
+// x + 8, ...; so that they share A and B there, XCD x takes one block of
+// the round: P/gp panels x nt/f n-tiles, with gp * f = 8.  Workgroups on
+// one XCD move through K together, so a panel's slice is fetched into that
+// L2 once for all of them.  Per round, A panels are then fetched f times
+// and B panels gp times (instead of up to 8 times each).
+
+// The n-tile split f for a grid of G workgroups (0 = keep list order):
+// minimises f * P * tm + (8 / f) * nt * tn, the A and B rows fetched.
+AGG_HD int pick_xcd_split(const Schedule& s, int64_t G)
+{
+    if (G < kXcds || G % kXcds != 0 || s.nt <= 0 || G % s.nt != 0) return 0;
+    const int64_t P = G / s.nt;   // panels per round
+    int best = 0;
+    int64_t best_cost = 0;
+    for (int f = 1; f <= kXcds; f *= 2) {
+        const int gp = kXcds / f;
+        if (s.nt % f != 0 || P % gp != 0) continue;
+        const int64_t cost = (int64_t)f * P * s.tm + (int64_t)gp * s.nt * s.tn;
+        if (best == 0 || cost < best_cost) {
+            best = f;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+// First position (within round 0) of workgroup b; it then takes that
+// position plus multiples of G.  A permutation of [0, G) for every grid
+// pick_xcd_split accepted, the identity otherwise.
+AGG_HD int64_t wg_position(const Schedule& s, int64_t b, int64_t G)
+{
+    const int f = s.xf;
+    if (f <= 0) return b;
+    const int64_t P = G / s.nt;
+    const int gp = kXcds / f;
+    const int64_t bp = P / gp;          // panels per XCD block
+    const int64_t bn = s.nt / f;        // n-tiles per XCD block
+    const int64_t x = b % kXcds, slot = b / kXcds;
+    const int64_t g = x / f, h = x % f;
+    const int64_t panel = g * bp + slot / bn;
+    const int64_t n = h * bn + slot % bn;
+    return panel * s.nt + n;
 }
 
 // Rows of chunk j: [j*cr, min((j+1)*cr, S)).

@@ -78,7 +78,7 @@ def test_large_cases_sampled_rows(agg, orc, cid):
     check_f16(C[rows], Co, So, c.name)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("n,S,K,N,cr", [
     (3, 100, 296, 168, 7),     # ragged rows, k tail, n tail, ragged last chunk
     (2, 300, 520, 264, 0),
@@ -91,7 +91,7 @@ def test_ragged_shapes(agg, orc, tile, n, S, K, N, cr):
     check_f16(C, Co, So, f"tile {tile} n={n} S={S} K={K} N={N}")
 
 
-@pytest.mark.parametrize("kind,tile", [("f16", 6), ("f16", 3), ("i8", 6), ("i8", 2)])
+@pytest.mark.parametrize("kind,tile", [("f16", 6), ("f16", 3), ("f16", 8), ("i8", 6), ("i8", 2), ("i8", 9)])
 def test_no_store_outside_c(agg, kind, tile):
     """Rows past the last shard's end and columns past N are dropped by
     the epilogue: memory right after C (and after acc_out) keeps its
@@ -159,7 +159,7 @@ def test_i8_small_full(agg, orc):
     check_i8(acc, D, ao, Do, "int8 small")
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_i8_ragged(agg, orc, tile):
     shards, B, bias, scale = synth.make_i8(3 * 77, 16 * 37, 8 * 19, 3, 41000 + tile)
     acc, D = run_i8(agg, shards, B, bias, scale, 9, dict(tile=tile))

@@ -48,26 +48,28 @@ def reports():
 
 
 def shape_table():
-    """(kind, id) -> (BM, BN, SB, NS) from the sources."""
+    """(kind, id) -> (BM, BN, SB, NS, WM, WN) from the sources."""
     plan = open(os.path.join(CSRC, "plan.cpp")).read()
     cons = open(os.path.join(CSRC, "consumer.hip")).read()
     cfg = {int(i): tuple(int(x) for x in v) for i, *v in re.findall(
-        r"struct Cfg<(\d+)> \{ static constexpr int BM = (\d+), BN = (\d+), SB = (\d+), NS = (\d+);",
-        cons)}
+        r"struct Cfg<(\d+)> \{ static constexpr int BM = (\d+), BN = (\d+), SB = (\d+), "
+        r"NS = (\d+), WM = (\d+), WN = (\d+);", cons)}
     tables = {}
     for kind, name in (("F16", "kF16Shapes"), ("I8", "kI8Shapes")):
         body = plan[plan.index(name):]
         body = body[:body.index("};")]
-        for i, tm, tn, _, _ in re.findall(
+        for i, tm, tn, threads, _ in re.findall(
                 r"\{(\d+), (\d+), (\d+), (\d+), (true|false)\}", body):
-            bm, bn, sb, ns = cfg[int(i)]
+            bm, bn, sb, ns, wm, wn = cfg[int(i)]
             assert (bm, bn) == (int(tm), int(tn))
-            tables[(kind, int(i))] = (bm, bn, sb, ns)
+            assert int(threads) == 64 * wm * wn
+            tables[(kind, int(i))] = (bm, bn, sb, ns, wm, wn)
     return tables
 
 
-def consumer_report(cons, kind, bm, bn, sb, ns):
-    key = f"consumer_kernelINS0_{len(kind)}{kind}ELi{bm}ELi{bn}ELi{sb}ELi{ns}E"
+def consumer_report(cons, kind, bm, bn, sb, ns, wm, wn):
+    key = (f"consumer_kernelINS0_{len(kind)}{kind}ELi{bm}ELi{bn}ELi{sb}ELi{ns}E"
+           f"Li{wm}ELi{wn}EEEv")
     name = [k for k in cons if key in k]
     assert len(name) == 1, (kind, key)
     return cons[name[0]]
@@ -83,16 +85,19 @@ def test_every_consumer_leaves_room_for_the_producer(reports):
     prod_lds = pk.get("LDS Size [bytes/block]", 0)
     assert pk.get("ScratchSize [bytes/lane]", 0) == 0
     table = shape_table()
-    assert len(table) == 14
-    for (kind, i), (bm, bn, sb, ns) in table.items():
-        r = consumer_report(cons, kind, bm, bn, sb, ns)
+    assert len(table) == 18
+    for (kind, i), (bm, bn, sb, ns, wm, wn) in table.items():
+        r = consumer_report(cons, kind, bm, bn, sb, ns, wm, wn)
         regs = align8(r["VGPRs"]) + align8(r["AGPRs"])
-        # consumer workgroups (4 waves, one per SIMD) on a CU: bounded by
-        # registers and by the LDS ring (ns stages of (bm + bn) x sb bytes)
+        per_simd = wm * wn // 4          # waves of one workgroup on each SIMD
+        # consumer workgroups on a CU: bounded by registers and by the LDS
+        # ring (ns stages of (bm + bn) x sb bytes)
         lds = ns * sb * (bm + bn) + r.get("LDS Size [bytes/block]", 0)
-        waves = min(512 // regs, 163840 // lds, 8)
+        wgs = min(512 // (regs * per_simd), 163840 // lds, 8 // per_simd)
+        assert wgs >= 1, (kind, i)
+        waves = wgs * per_simd
         assert 512 - waves * regs >= prod_regs, (kind, i, regs, prod_regs)
-        assert 163840 - waves * lds >= prod_lds, (kind, i, lds)
+        assert 163840 - wgs * lds >= prod_lds, (kind, i, lds)
         assert waves + 1 <= 8, (kind, i)
 
 

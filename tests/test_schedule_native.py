@@ -1,0 +1,76 @@
+"""The XCD placement of consumer positions, compiled from the same header
+the kernels use (schedule.hpp is plain integer C++): for every grid the
+planner accepts, the workgroups of one round take each position exactly
+once, the workgroups of one XCD take a block of whole row panels x n-tile
+groups, and a grid it cannot split keeps list order."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "communication_gemm_amd", "csrc")
+
+PROGRAM = r"""
+#include <cstdio>
+#include <vector>
+#include "schedule.hpp"
+using namespace agg;
+int main() {
+    int checked = 0, split = 0;
+    for (int nt = 1; nt <= 64; ++nt)
+    for (int G = 1; G <= 1024; ++G) {
+        Schedule s{};
+        s.nt = nt; s.tm = 256; s.tn = (nt % 3) ? 128 : 256;
+        s.xf = pick_xcd_split(s, G);
+        std::vector<int> seen(G, 0);
+        for (int b = 0; b < G; ++b) {
+            long p = wg_position(s, b, G);
+            if (p < 0 || p >= G) { printf("out of range G=%d nt=%d b=%d p=%ld\n", G, nt, b, p); return 1; }
+            seen[p]++;
+            if (s.xf == 0 && p != b) { printf("not identity G=%d nt=%d\n", G, nt); return 1; }
+        }
+        for (int p = 0; p < G; ++p)
+            if (seen[p] != 1) { printf("not a permutation G=%d nt=%d p=%d\n", G, nt, p); return 1; }
+        if (s.xf) {
+            ++split;
+            // one XCD: its positions form a block of panels x n-tiles
+            int f = s.xf, gp = kXcds / f;
+            for (int x = 0; x < kXcds; ++x) {
+                long pmin = 1L << 40, pmax = -1, nmin = 1L << 40, nmax = -1, cnt = 0;
+                for (int b = x; b < G; b += kXcds) {
+                    long p = wg_position(s, b, G);
+                    long panel = p / nt, n = p % nt;
+                    pmin = panel < pmin ? panel : pmin; pmax = panel > pmax ? panel : pmax;
+                    nmin = n < nmin ? n : nmin; nmax = n > nmax ? n : nmax; ++cnt;
+                }
+                long P = G / nt;
+                if (pmax - pmin + 1 != P / gp || nmax - nmin + 1 != nt / f || cnt != (P / gp) * (nt / f)) {
+                    printf("bad block G=%d nt=%d x=%d\n", G, nt, x); return 1;
+                }
+            }
+        }
+        ++checked;
+    }
+    // the shapes the workloads run: 256 workgroups, 16 n-tiles
+    Schedule s{}; s.nt = 16; s.tm = 256; s.tn = 256;
+    int f = pick_xcd_split(s, 256);
+    printf("%d %d %d\n", checked, split, f);
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ needed")
+def test_xcd_placement_is_a_blocked_permutation(tmp_path):
+    src = tmp_path / "sched.cpp"
+    src.write_text(PROGRAM)
+    exe = tmp_path / "sched"
+    subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout
+    checked, split, f = map(int, out.stdout.split())
+    assert checked == 64 * 1024 and split > 1000
+    assert f in (2, 4)          # 16 panels x 16 n-tiles: 4 x 8 or 8 x 4 blocks
