@@ -217,6 +217,8 @@ int run(const Call& c)
     ca.acc_out = opt->acc_out;
     pa.counters = header;
     pa.flags = header + kFlagOffset / 4;
+    pa.pieces = reinterpret_cast<uint64_t*>(ws + kPieceOffset);
+    pa.ppc = p.ppc;
     pa.err = header + kErrorOffset / 4;
     pa.clock = reinterpret_cast<uint64_t*>(ws + kClockOffset);
     pa.epoch = epoch;

@@ -634,6 +634,8 @@ template <> struct Cfg<6> { static constexpr int BM = 256, BN = 256, SB = 128, N
 template <> struct Cfg<7> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 3, WM = 2, WN = 2; };
 template <> struct Cfg<8> { static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WM = 2, WN = 4; };
 template <> struct Cfg<9> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WM = 2, WN = 4; };
+template <> struct Cfg<10> { static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WM = 4, WN = 2; };
+template <> struct Cfg<11> { static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WM = 2, WN = 4; };
 
 template <class T, int ID>
 struct Kern {
@@ -680,6 +682,8 @@ hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t 
     case 7: return Kern<T, 7>::launch(a, wgs, st);
     case 8: return Kern<T, 8>::launch(a, wgs, st);
     case 9: return Kern<T, 9>::launch(a, wgs, st);
+    case 10: return Kern<T, 10>::launch(a, wgs, st);
+    case 11: return Kern<T, 11>::launch(a, wgs, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -697,6 +701,8 @@ int occupancy_kind(int tile_id)
     case 7: return Kern<T, 7>::occupancy();
     case 8: return Kern<T, 8>::occupancy();
     case 9: return Kern<T, 9>::occupancy();
+    case 10: return Kern<T, 10>::occupancy();
+    case 11: return Kern<T, 11>::occupancy();
     default: return 0;
     }
 }

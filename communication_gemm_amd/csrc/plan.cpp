@@ -31,6 +31,8 @@ const TileShape kF16Shapes[] = {
     {6, 256, 256, 256, false},
     {7, 256, 256, 256, false},
     {9, 256, 256, 512, false},
+    {10, 256, 128, 512, false},
+    {11, 128, 256, 512, false},
 };
 const TileShape kI8Shapes[] = {
     {8, 256, 256, 512, true},
@@ -42,6 +44,8 @@ const TileShape kI8Shapes[] = {
     {6, 256, 256, 256, false},
     {7, 256, 256, 256, false},
     {9, 256, 256, 512, false},
+    {10, 256, 128, 512, false},
+    {11, 128, 256, 512, false},
 };
 
 }  // namespace
@@ -174,11 +178,16 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     int cw = opt->consumer_wgs ? opt->consumer_wgs : num_cus;
     if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
     if (cw < 1) cw = 1;
+    // pieces per chunk (a chunk is below 2 GiB, so at most 65536)
+    const int64_t chunk_bytes = (int64_t)s.cr * K * (kind == kF16 ? 2 : 1);
+    const int ppc = chunk_bytes > 0 ? (int)cdiv(chunk_bytes, kPieceBytes) : 1;
+    const int64_t items = chunks * ppc;
     int pw = opt->producer_wgs ? opt->producer_wgs : num_cus;
-    if (pw > chunks) pw = (int)(chunks > 0 ? chunks : 1);
+    if (pw > items) pw = (int)(items > 0 ? items : 1);
     if (pw < 1) pw = 1;
     p.consumer_wgs = cw;
     p.producer_wgs = pw;
+    p.ppc = ppc;
     p.mode = opt->mode;
     p.link_gbps = opt->link_gbps;
     p.elt = (kind == kF16) ? 2 : 1;

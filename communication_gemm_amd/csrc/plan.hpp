@@ -30,6 +30,7 @@ struct Plan {
     double link_gbps;
     int consumer_wgs;
     int producer_wgs;
+    int ppc;            // producer pieces per chunk
     int elt;            // bytes per A element
     int64_t M;
     size_t ws_bytes;    // workspace bytes this call needs

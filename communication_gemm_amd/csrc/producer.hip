@@ -6,14 +6,18 @@
 // summary counter; several communication blocks per destination; chunks
 // sent in the order they are consumed).
 //
-// Workgroup w copies producer positions w, w + G, w + 2G, ... (send order)
-// in parallel with the others.  A finished chunk is published in two
-// steps, neither of which waits for another workgroup:
-//   * its copier waits until its device-scope (write-through) stores of
-//     the chunk are performed in memory, then stores the call's epoch in
-//     the chunk's flag (the chunk flag matrix);
-//   * the copier then advances the source's summary counter over every
-//     flagged chunk contiguous with it, in one compare-and-swap.
+// Each chunk is cut into 512 KiB pieces; piece q of producer position c is
+// item c * P + q, and workgroup w copies items w, w + G, w + 2G, ..., so
+// all workgroups work on the earliest chunks first and chunks complete in
+// about the order they are sent.  A finished chunk is published in three
+// steps, none of which waits for another workgroup:
+//   * each piece's copier waits until its device-scope (write-through)
+//     stores are performed in memory, then counts the piece in the chunk's
+//     piece counter;
+//   * the copier of the chunk's last piece stores the call's epoch in the
+//     chunk's flag (the chunk flag matrix);
+//   * it then advances the source's summary counter over every flagged
+//     chunk contiguous with it, in one compare-and-swap.
 // So a counter value c means "chunks 0..c-1 are flagged", and the counter
 // moves as soon as the lowest missing chunk lands, whoever copied it.  The
 // consumer waits on the counter, then reads the flags of the chunks it
@@ -104,12 +108,28 @@ __device__ void advance(uint32_t* ctr, const uint32_t* flags, uint32_t base, int
     }
 }
 
+// Count one copied piece of a chunk; true for the piece that completes it.
+// The word holds the call's epoch above the count, so it needs no reset: a
+// word left by an earlier call restarts at one.
+__device__ bool count_piece(uint64_t* word, uint32_t epoch, int ppc)
+{
+    uint64_t cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const uint64_t next = (uint32_t)(cur >> 32) == epoch
+                                  ? cur + 1
+                                  : ((uint64_t)epoch << 32) | 1u;
+        if (__hip_atomic_compare_exchange_strong(word, &cur, next, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return (uint32_t)next == (uint32_t)ppc;
+    }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs a)
 {
     const Schedule& s = a.s;
-    const int64_t total = total_chunks(s);
+    const int64_t items = total_chunks(s) * a.ppc;
     const int64_t row_bytes = s.K * a.elt;
     __shared__ uint64_t origin_sh;
     __shared__ int stop_sh;
@@ -124,20 +144,27 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     }
     __syncthreads();
 
-    for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int64_t c = it / a.ppc;                  // producer position
+        const int64_t q = it % a.ppc;                  // piece of its chunk
         const ChunkRef r = chunk_at(s, c);
         const int64_t row0 = (int64_t)r.j * s.cr;
-        const int64_t rows = chunk_row_end(s, r.j) - row0;
-        copy_bytes(a.dst[r.shard] + row0 * row_bytes,
-                   a.src[r.shard] + row0 * row_bytes, rows * row_bytes);
+        const int64_t bytes = (chunk_row_end(s, r.j) - row0) * row_bytes;
+        const int64_t begin = q * kPieceBytes;
+        const int64_t end = begin + kPieceBytes < bytes ? begin + kPieceBytes : bytes;
+        if (begin < end)
+            copy_bytes(a.dst[r.shard] + row0 * row_bytes + begin,
+                       a.src[r.shard] + row0 * row_bytes + begin, end - begin);
         // The copy's stores are device-scope stores, written through to
         // memory; a store is counted done only once it is performed there.
-        // Waiting for them is what makes the chunk visible to every CU, so
+        // Waiting for them is what makes the piece visible to every CU, so
         // no cache write-back (what a release fence would add, for the
-        // whole L2) is needed before the flag.
+        // whole L2) is needed before the piece is counted.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x == 0 && c != a.drop) {
+        if (threadIdx.x == 0 &&
+            count_piece(a.pieces + r.shard * kFlagCap + r.j, a.epoch, a.ppc) && c != a.drop) {
+            // every piece of the chunk is in memory: release it
             bool ok = true;
             if (a.ticks_per_byte > 0.0) {
                 const double b = (double)paced_bytes(s, r, a.elt);

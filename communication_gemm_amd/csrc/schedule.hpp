@@ -20,16 +20,26 @@ namespace agg {
 constexpr int kMaxShards = 64;
 
 // Workspace header: one 32-bit summary counter per source shard, each on
-// its own 128-byte line, then the error word, the pacing origin and the
+// its own 128-byte line, then the error word, the pacing origin, the
 // chunk flag matrix (one 32-bit word per source and chunk: the epoch of the
-// call that released it).  The PTO-ISA README keeps the same two
+// call that released it) and the piece counters (one 64-bit word per
+// source and chunk: the call's epoch above the number of the chunk's
+// pieces copied so far).  The PTO-ISA README keeps the first two
 // structures: per-chunk flags and a per-source summary counter.
 constexpr int kCounterStride = 128;                       // bytes
 constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
 constexpr int kClockOffset = kErrorOffset + kCounterStride; // uint64
 constexpr int kFlagOffset = 16384;
 constexpr int kFlagCap = 1024;       // chunks per source the flag matrix holds
-constexpr int kHeaderBytes = kFlagOffset + kMaxShards * kFlagCap * 4;
+constexpr int kPieceOffset = kFlagOffset + kMaxShards * kFlagCap * 4;
+constexpr int kHeaderBytes = kPieceOffset + kMaxShards * kFlagCap * 8;
+
+// The producer copies a chunk in pieces of up to this many bytes, dealt to
+// its workgroups in send order, so that a large chunk is shared by many
+// workgroups and all of them work on the earliest chunks first.  Each
+// piece ends in a wait for its stores and an atomic count, so pieces are
+// kept large enough (16 sweeps of a workgroup) for that to stay small.
+constexpr int kPieceBytes = 524288;
 
 struct Schedule {
     int n_shards;
