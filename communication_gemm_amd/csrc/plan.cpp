@@ -155,14 +155,15 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
             if (shapes[i].id == opt->tile) pick = &shapes[i];
         if (!pick) return AGG_E_INVALID;
     } else {
-        // the largest tile that still gives every CU two or more tiles,
-        // else the smallest
+        // the largest tile that still gives every CU a tile (a full first
+        // round), else the smallest: a bigger tile wins on MFMA efficiency
+        // by more than a second round would gain in overlap
         const TileShape* smallest = nullptr;
         for (int i = 0; i < count && !pick; ++i) {
             if (!shapes[i].auto_pick) continue;
             int64_t tiles = (int64_t)n_shards * cdiv(S, shapes[i].tm) *
                             cdiv(N, shapes[i].tn);
-            if (tiles >= 2LL * num_cus) pick = &shapes[i];
+            if (tiles >= num_cus) pick = &shapes[i];
             smallest = &shapes[i];
         }
         if (!pick) pick = smallest;
