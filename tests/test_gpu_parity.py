@@ -120,6 +120,28 @@ def test_no_store_outside_c(agg, kind, tile):
         assert (buf[M * N:] == 7.0).all() and (acc[M * N:] == -5).all()
 
 
+def test_chunks_in_several_pieces(agg, orc):
+    """Chunks of 2 MiB are copied as four 512 KiB pieces by different
+    producer workgroups; the last chunk of each shard is short, so some of
+    its pieces are empty.  Repeated calls on one workspace reuse the
+    epoch-tagged piece counters."""
+    n, S, K, N, cr = 3, 70, 1 << 16, 64, 16          # 16 rows x 128 KiB per chunk
+    info, _, _ = agg.plan("f16", n, n * S, K, N, cr)
+    assert info.chunks_per_source == 5
+    shards, B = synth.make_f16(n * S, K, N, n, "normal", 34000)
+    ts = [dev(s, torch) for s in shards]
+    tB = dev(B, torch)
+    ws = torch.empty(agg.workspace_bytes(n, n * S, K, 2), dtype=torch.uint8, device="cuda")
+    agg.workspace_reset(ws)
+    Co, So = orc.ag_gemm_f16(shards, B)
+    for it, kw in enumerate([dict(), dict(producer_wgs=3), dict(mode=agg.MODE_SEQUENTIAL),
+                             dict(link_gbps=200.0), dict()]):
+        C = torch.full((n * S, N), float("nan"), device="cuda")
+        agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(workspace=ws, **kw))
+        assert agg.check() == 0
+        check_f16(C.cpu().numpy(), Co, So, f"pieces, call {it} {kw}")
+
+
 def test_single_shard_and_many_shards(agg, orc):
     shards, B = synth.make_f16(96, 64, 32, 1, "normal", 32000)
     C = run_f16(agg, shards, B)
