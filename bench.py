@@ -249,6 +249,24 @@ def run_f16(args, torch, agg, synth):
         res["copy_only_GBps"] = 2 * copied / (t_copy * 1e-3) / 1e9
     info, _, _ = agg.plan("f16", case.n_shards, case.M, case.K, case.N, cr,
                           agg.options(tile=args.tile))
+    if args.mode == "pipelined":
+        # one more pipelined call, untimed, with the device trace on: how
+        # long consumer tiles waited for chunks and when the last landed
+        trace = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
+        agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(workspace=ws, link_gbps=gbps,
+                                                         tile=args.tile, trace=trace))
+        if agg.check():
+            raise SystemExit("traced run failed")
+        tr = trace.cpu().numpy().view(np.uint64).astype(np.float64)
+        nc = info.total_chunks
+        start, rel, cons = tr[0], tr[1:1 + nc], tr[1 + nc:].reshape(-1, 3)
+        waits = cons[:, 1] - cons[:, 0]
+        res["trace"] = {
+            "tile_wait_share": round(float(waits.sum() / (cons[:, 2] - cons[:, 0]).sum()), 4),
+            "mean_tile_wait_us": round(float(waits.mean()) / 100.0, 2),
+            "max_tile_wait_us": round(float(waits.max()) / 100.0, 2),
+            "last_release_us": round(float(rel.max() - start) / 100.0, 2) if nc else 0.0,
+            "consumer_span_us": round(float(cons[:, 2].max() - start) / 100.0, 2)}
     res["tile"] = [info.tile_m, info.tile_n]
     res["tile_id"] = info.tile_id
     res["chunk_rows"] = info.chunk_rows

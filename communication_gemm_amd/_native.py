@@ -47,6 +47,7 @@ class Options(ctypes.Structure):
         ("timeout_ms", ctypes.c_double),
         ("debug_drop_chunk", ctypes.c_int),
         ("consumer_events", ctypes.c_void_p * 2),
+        ("trace", ctypes.c_void_p),
     ]
 
 
@@ -66,6 +67,7 @@ class PlanInfo(ctypes.Structure):
         ("consumer_wgs", ctypes.c_int),
         ("producer_wgs", ctypes.c_int),
         ("tile_id", ctypes.c_int),
+        ("trace_words", ctypes.c_int64),
     ]
 
 
@@ -148,7 +150,7 @@ def options(**kw) -> Options:
         elif k == "consumer_events":
             o.consumer_events[0] = ctypes.c_void_p(v[0].cuda_event)
             o.consumer_events[1] = ctypes.c_void_p(v[1].cuda_event)
-        elif k in ("acc_out", "workspace"):
+        elif k in ("acc_out", "workspace", "trace"):
             setattr(o, k, v.data_ptr() if hasattr(v, "data_ptr") else int(v))
             if k == "workspace" and hasattr(v, "numel"):
                 o.workspace_bytes = v.numel() * v.element_size()

@@ -150,6 +150,7 @@ int run(const Call& c)
             if (opt->acc_out && !aligned(opt->acc_out, 16)) return AGG_E_UNSUPPORTED;
         }
     }
+    if (opt->trace && !aligned(opt->trace, 8)) return AGG_E_UNSUPPORTED;
 
     // every argument check runs before the first HIP call
     Plan p;
@@ -215,6 +216,9 @@ int run(const Call& c)
     ca.bias = c.bias;
     ca.scale = c.scale;
     ca.acc_out = opt->acc_out;
+    ca.trace = opt->trace ? opt->trace + 1 + total_chunks(s) : nullptr;
+    ca.trace_start = opt->trace;
+    pa.trace = opt->trace;
     pa.counters = header;
     pa.flags = header + kFlagOffset / 4;
     pa.pieces = reinterpret_cast<uint64_t*>(ws + kPieceOffset);

@@ -557,6 +557,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     const Schedule& s = a.s;
     const int tid = threadIdx.x;
     for (int i = tid; i < kMaxShards; i += E::kThreads) seen_sh[i] = 0;
+    if (a.trace_start && blockIdx.x == 0 && tid == 0) a.trace_start[0] = ticks();
     __syncthreads();
 
     const int64_t tiles = total_tiles(s);
@@ -566,6 +567,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
 
     for (int64_t p = wg_position(s, blockIdx.x, gridDim.x); p < tiles; p += gridDim.x) {
         const TileRef t = tile_at(s, p);
+        if (a.trace && tid == 0) a.trace[3 * p] = ticks();
         if (t.need > 0 && !a.no_wait) {
             // wave 0 waits; the other waves hold at the barrier
             if (tid < 64) {
@@ -600,6 +602,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
             __syncthreads();
             if (!ok_sh) break;   // the call has failed; every lane leaves
         }
+        if (a.trace && tid == 0) a.trace[3 * p + 1] = ticks();
 
         const int64_t row0 = (int64_t)t.m * BM;
         const int64_t rows = s.S - row0;
@@ -614,6 +617,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
 
         if (nk > 0) E::run(lds, nk, src, L, acc);
         store_tile<T, BM, BN, WM, WN>(a, t.shard, t.m, t.n, acc);
+        if (a.trace && tid == 0) a.trace[3 * p + 2] = ticks();
     }
 }
 

@@ -26,6 +26,7 @@ struct ProducerArgs {
     int64_t drop;                  // producer position whose release is withheld
     double ticks_per_byte;         // pacing; 0 = unpaced
     uint64_t limit;                // wait limit in clock ticks
+    uint64_t* trace;               // optional timestamps (see agg_options.trace)
 };
 
 // Persistent consumer GEMM.
@@ -45,6 +46,8 @@ struct ConsumerArgs {
     const int32_t* bias;
     const float* scale;
     int32_t* acc_out;
+    uint64_t* trace;               // optional timestamps, consumer part
+    uint64_t* trace_start;         // word 0 of the timestamps (call start)
 };
 
 hipError_t launch_producer(const ProducerArgs& a, int wgs, hipStream_t st);

@@ -262,6 +262,7 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
         info->consumer_wgs = p.consumer_wgs;
         info->producer_wgs = p.producer_wgs;
         info->tile_id = p.shape.id;
+        info->trace_words = 1 + agg::total_chunks(s) + 3 * agg::total_tiles(s);
     }
     if (tile_order) {
         int64_t T = agg::total_tiles(s);

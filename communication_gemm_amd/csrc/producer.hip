@@ -179,6 +179,9 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
             }
             if (ok) {
                 uint32_t* flags = a.flags + r.shard * kFlagCap;
+                // stamped before the flag, so a consumer that saw the flag
+                // started after this time
+                if (a.trace) a.trace[1 + c] = ticks();
                 __hip_atomic_store(flags + r.j, a.epoch, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
                 // the flag store is performed before the counter is read

@@ -98,6 +98,19 @@ typedef struct agg_options {
     void *consumer_events[2]; /* optional hipEvent_t pair recorded right
                                  before and after the consumer kernel, on
                                  the stream it runs on                       */
+    uint64_t *trace;        /* optional DEVICE buffer of at least
+                               agg_plan_info.trace_words uint64, 8-byte
+                               aligned, receiving 100 MHz device timestamps:
+                                 [0]            consumer start (its first
+                                                workgroup; the consumer is
+                                                launched before the producer)
+                                 [1 + c]        release of producer position c
+                                 [1 + C + 3p + 0..2]  consumer position p:
+                                                wait start, compute start, end
+                               (C = total_chunks).  Entries a call does not
+                               reach keep their contents; the caller clears
+                               the buffer.  A chunk's release is stamped
+                               before its flag is published.                 */
 } agg_options;
 
 /* Fill *opt with the defaults above. */
@@ -194,6 +207,7 @@ typedef struct agg_plan_info {
     int consumer_wgs;       /* persistent consumer grid */
     int producer_wgs;       /* producer grid */
     int tile_id;            /* consumer tile configuration (agg_options.tile) */
+    int64_t trace_words;    /* 1 + total_chunks + 3 * total_tiles          */
 } agg_plan_info;
 
 /*

@@ -1,0 +1,59 @@
+"""The optional device trace: chunk releases and consumer tile phases, in
+100 MHz device ticks.  Besides the bookkeeping, it checks the release
+protocol itself on a paced run (PTO-ISA AllGather+GEMM README, two-stream
+pipeline: the compute side starts a remote tile only after the counter
+covers its rows): every remote tile starts computing after the release of
+the last chunk it needs, and the pacing really spreads the releases."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def agg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import communication_gemm_amd as m
+    return m
+
+
+def test_trace_orders_releases_before_dependent_tiles(agg):
+    n, S, K, N, cr, gbps = 4, 1024, 1024, 512, 32, 20.0
+    M = n * S
+    shards, B = synth.make_f16(M, K, N, n, "normal", 60000)
+    ts = [dev(s, torch) for s in shards]
+    tB = dev(B, torch)
+    opts = dict(link_gbps=gbps)
+    info, tiles, chunks = agg.plan("f16", n, M, K, N, cr, agg.options(**opts), orders=True)
+    assert info.trace_words == 1 + info.total_chunks + 3 * info.total_tiles
+    trace = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
+    C = torch.empty((M, N), device="cuda")
+    agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(trace=trace, **opts))
+    assert agg.check() == 0
+    ref = torch.empty_like(C)
+    agg.ag_gemm_f16(ts, tB, ref, cr, opts=agg.options(**opts))
+    assert agg.check() == 0
+    assert torch.equal(C, ref)                 # tracing changes nothing computed
+
+    tr = trace.cpu().numpy().view(np.uint64).astype(np.float64)
+    nc = info.total_chunks
+    start, rel, cons = tr[0], tr[1:1 + nc], tr[1 + nc:].reshape(-1, 3)
+    assert start > 0 and (rel > 0).all() and (cons > 0).all()
+    assert (cons[:, 0] <= cons[:, 1]).all() and (cons[:, 1] <= cons[:, 2]).all()
+    pos = {(int(s), int(j)): i for i, (s, j) in enumerate(chunks)}
+    waited = 0
+    for p, (shard, m, nn, need) in enumerate(tiles):
+        if need > 0:
+            r = rel[pos[(int(shard), int(need) - 1)]]
+            assert cons[p, 1] >= r, (p, shard, m, need)
+            waited += cons[p, 1] > cons[p, 0]
+    assert waited > 0
+    # a source's S x K fp16 rows cannot cross a 20 GB/s link in less than
+    # this; the consumer starts before the producer
+    pace_ticks = S * K * 2 / (gbps * 1e9) * 1e8
+    assert rel.max() - start >= 0.9 * pace_ticks
