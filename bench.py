@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true", help="skip the overlap modes")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 workload")
+    ap.add_argument("--no-chunk-sweep", action="store_true",
+                    help="skip the pipelined chunk-size sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mode", choices=sorted(MODES), default="pipelined",
                     help="mode of the timed calls; hardware-counter runs use 'compute' "
@@ -247,6 +249,22 @@ def run_f16(args, torch, agg, synth):
         res["speedup_vs_sequential"] = t_seq / t_pipe
         copied = (case.n_shards - 1) * case.shard_rows * case.K * 2
         res["copy_only_GBps"] = 2 * copied / (t_copy * 1e-3) / 1e9
+    if modes and not args.no_chunk_sweep:
+        # pipelined step time over chunk sizes (16 to 256 rows; 16 is the
+        # automatic size here), each after its own warm-up
+        sweep = {}
+        for rows in (16, 32, 64, 128, 256):
+            if rows > case.shard_rows:
+                continue
+
+            def fn(ev, rows=rows):
+                agg.ag_gemm_f16(ts, tB, C, rows, opts=agg.options(
+                    workspace=ws, link_gbps=gbps, tile=args.tile))
+            t, _ = timed(torch, fn, max(20, args.steps // 2), 10, with_consumer=False)
+            sweep[str(rows)] = round(t, 5)
+        if agg.check():
+            raise SystemExit("chunk sweep failed")
+        res["chunk_sweep_ms"] = sweep
     info, _, _ = agg.plan("f16", case.n_shards, case.M, case.K, case.N, cr,
                           agg.options(tile=args.tile))
     if args.mode == "pipelined":

@@ -21,6 +21,8 @@
  *       k order; the result is then rounded once to fp32.
  *       The kernel is free to sum in any order, so the comparison uses an
  *       error bound; S[i,j] = sum_k |A[i,k] * B[k,j]| is emitted for it.
+ *   bf16 path:  the same with bfloat16 A and B (a variant of the fp16
+ *       path: same gather, same fp32 output, a different input format).
  *   int8 path (catccos AllGatherMatmulDequant doc, section 2.2):
  *       v[i,j] = sum_k A[i,k] * B[k,j] + bias[j]     (exact, int64, must
  *                                                     fit in int32)
@@ -134,18 +136,44 @@ static int check_shape(const void *const *shards, int n_shards, int64_t M,
 }
 
 /* ------------------------------------------------------------------ */
-/* fp16 x fp16 -> fp32                                                  */
+/* bfloat16, written from the format's definition: 1 sign bit, 8       */
+/* exponent bits (bias 127), 7 fraction bits (the upper half of an     */
+/* IEEE binary32).                                                      */
 /* ------------------------------------------------------------------ */
 
+double oracle_bf16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -133);                /* subnormal: f * 2^-133 */
+    } else if (e == 255) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(128 + f), e - 134);     /* (1.f) * 2^(e-127)     */
+    }
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------ */
+/* 16-bit floats x 16-bit floats -> fp32 (fp16 and bf16 paths)          */
+/* ------------------------------------------------------------------ */
+
+typedef double (*decode16_fn)(uint16_t);
+
 /*
- * Rows `rows[0..n_rows)` of C = gather(shards) x B.
- * C_rows: n_rows x N fp32; abs_rows (may be NULL): n_rows x N double,
- * the sum over k of |A[i,k] B[k,j]|.
+ * Rows `rows[0..n_rows)` of C = gather(shards) x B, the elements of both
+ * decoded by `dec`.  C_rows: n_rows x N fp32; abs_rows (may be NULL):
+ * n_rows x N double, the sum over k of |A[i,k] B[k,j]|.  A product of two
+ * fp16 values (11 significant bits each) or two bf16 values (8 each) is
+ * exact in double.
  */
-int oracle_ag_gemm_f16_rows(const uint16_t *const *shards, int n_shards,
-                            const uint16_t *B, int64_t M, int64_t K, int64_t N,
-                            const int64_t *rows, int64_t n_rows,
-                            float *C_rows, double *abs_rows)
+static int ag_gemm_16bit_rows(decode16_fn dec, const uint16_t *const *shards,
+                              int n_shards, const uint16_t *B, int64_t M,
+                              int64_t K, int64_t N, const int64_t *rows,
+                              int64_t n_rows, float *C_rows, double *abs_rows)
 {
     if (check_shape((const void *const *)shards, n_shards, M, K, N))
         return 1;
@@ -158,7 +186,7 @@ int oracle_ag_gemm_f16_rows(const uint16_t *const *shards, int n_shards,
     if (!Bd)
         return 2;
     for (int64_t x = 0; x < K * N; x++)
-        Bd[x] = oracle_half_to_double(B[x]);
+        Bd[x] = dec(B[x]);
 
     int fail = 0;
 #pragma omp parallel
@@ -177,7 +205,7 @@ int oracle_ag_gemm_f16_rows(const uint16_t *const *shards, int n_shards,
                 (const void *const *)shards, S, K, rows[t], 2);
             for (int64_t j = 0; j < N; j++) { acc[j] = 0.0; mag[j] = 0.0; }
             for (int64_t k = 0; k < K; k++) {
-                double aik = oracle_half_to_double(a[k]);
+                double aik = dec(a[k]);
                 const double *b = Bd + k * N;
                 for (int64_t j = 0; j < N; j++) {
                     double p = aik * b[j];          /* exact */
@@ -196,6 +224,26 @@ int oracle_ag_gemm_f16_rows(const uint16_t *const *shards, int n_shards,
     }
     free(Bd);
     return fail;
+}
+
+/* fp16 x fp16 -> fp32 (PTO-ISA README "spec" table). */
+int oracle_ag_gemm_f16_rows(const uint16_t *const *shards, int n_shards,
+                            const uint16_t *B, int64_t M, int64_t K, int64_t N,
+                            const int64_t *rows, int64_t n_rows,
+                            float *C_rows, double *abs_rows)
+{
+    return ag_gemm_16bit_rows(oracle_half_to_double, shards, n_shards, B, M, K,
+                              N, rows, n_rows, C_rows, abs_rows);
+}
+
+/* bf16 x bf16 -> fp32: the same definition with bfloat16 inputs. */
+int oracle_ag_gemm_bf16_rows(const uint16_t *const *shards, int n_shards,
+                             const uint16_t *B, int64_t M, int64_t K, int64_t N,
+                             const int64_t *rows, int64_t n_rows,
+                             float *C_rows, double *abs_rows)
+{
+    return ag_gemm_16bit_rows(oracle_bf16_to_double, shards, n_shards, B, M, K,
+                              N, rows, n_rows, C_rows, abs_rows);
 }
 
 /* Whole C (M x N fp32) and optionally the whole |.| sum (M x N double). */
@@ -304,6 +352,12 @@ void oracle_half_to_double_n(const uint16_t *h, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; i++)
         out[i] = oracle_half_to_double(h[i]);
+}
+
+void oracle_bf16_to_double_n(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_bf16_to_double(h[i]);
 }
 
 void oracle_float_to_half_n(const float *x, uint16_t *out, int64_t n)

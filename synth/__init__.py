@@ -27,7 +27,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Case", "CASES", "make_f16", "make_i8", "make_case", "split_rows"]
+__all__ = ["Case", "CASES", "make_f16", "make_bf16", "make_i8", "make_case", "split_rows"]
 
 
 @dataclass(frozen=True)
@@ -99,6 +99,34 @@ def make_f16(M: int, K: int, N: int, n_shards: int, dist: str = "normal",
         else:
             raise ValueError(dist)
         return x.astype(np.float16)
+
+    A = draw(seed_base + 1, (M, K))
+    B = draw(seed_base + 2, (K, N))
+    return split_rows(A, n_shards), B
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values -> bfloat16 bit patterns (uint16), round to nearest
+    even on the dropped 16 bits; for finite inputs only (how the draws are
+    stored, like the fp16 cast above)."""
+    bits = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return bits.astype(np.uint16)
+
+
+def make_bf16(M: int, K: int, N: int, n_shards: int, dist: str = "normal",
+              seed_base: int = 0):
+    """bfloat16 shards of A and B, as uint16 bit patterns (numpy has no
+    bfloat16 type); drawn like make_f16, then rounded to bfloat16."""
+    def draw(seed, shape):
+        g = _rng(seed)
+        if dist == "normal":
+            x = g.standard_normal(shape, dtype=np.float32)
+        elif dist == "uniform":
+            x = g.uniform(-1.0, 1.0, shape).astype(np.float32)
+        else:
+            raise ValueError(dist)
+        return to_bf16_bits(x)
 
     A = draw(seed_base + 1, (M, K))
     B = draw(seed_base + 2, (K, N))

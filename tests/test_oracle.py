@@ -321,6 +321,7 @@ MUTATIONS = [
     ("int64_t v = acc[j] + (int64_t)bias[j];", "int64_t v = acc[j] - (int64_t)bias[j];"),
     ("volatile float p = f * s;", "volatile float p = f * s * 1.0001f;"),
     ("if (rem > halfway || (rem == halfway && (q & 1)))", "if (rem >= halfway)"),
+    ("v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),  # bf16 bias
 ]
 
 
@@ -355,6 +356,8 @@ def test_planted_mistake_is_caught(orc, tmp_path, idx, monkeypatch):
         lambda: test_i8_debug_mode_closed_form(oracle_mod),
         lambda: test_dequant_matches_numpy(oracle_mod),
         lambda: test_half_encode_matches_numpy_rne(oracle_mod),
+        lambda: test_bf16_decode_exhaustive(oracle_mod),
+        lambda: test_bf16_brute_force_exact_rational(oracle_mod, 0),
     ]
     caught = 0
     for chk in checks:
@@ -390,3 +393,103 @@ def test_golden_i8_hand(orc):
                                     g["scale"][0].astype(np.float32))
     assert np.array_equal(acc, g["acc"].astype(np.int32))
     assert np.array_equal(D.astype(np.float64), g["D"])
+
+
+# ----------------------------------------------------------------------------
+# bf16 x bf16 -> fp32 (the fp16 definition with bfloat16 inputs)
+# ----------------------------------------------------------------------------
+
+def bf16_ref(h):
+    """bfloat16 bits -> float64 through numpy's own binary32 decoding: a
+    bfloat16 is the upper half of a binary32."""
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def small_bf16(rng, shape):
+    """bfloat16 values m * 2^e, |m| < 128, e in [-6, 3]: exactly
+    representable (8 significant bits), sums of a few products exact."""
+    m = rng.integers(-127, 128, shape)
+    e = rng.integers(-6, 4, shape)
+    return synth.to_bf16_bits((m * np.exp2(e)).astype(np.float32))
+
+
+def test_bf16_decode_exhaustive(orc):
+    h = np.arange(65536, dtype=np.uint16)
+    ours = orc.bf16_to_double(h)
+    ref = bf16_ref(h)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert math.copysign(1.0, ours[0x8000]) == -1.0
+
+
+def test_bf16_input_rounding_is_rne():
+    """The generator's float32 -> bfloat16 rounding, against exact
+    rational rounding of random values and of every tie pattern."""
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        ((np.arange(4096, dtype=np.uint32) << 16) | 0x8000).view(np.float32)])
+    x = x[np.isfinite(x)]
+    got = bf16_ref(synth.to_bf16_bits(x))
+    for v, g in zip(x[::37], got[::37]):
+        q = Fraction(float(v))
+        lo = bf16_ref(np.array([(np.float32(v).view(np.uint32) >> 16)], np.uint16))[0]
+        hi = bf16_ref(np.array([(np.float32(v).view(np.uint32) >> 16) + 1], np.uint16))[0]
+        d_lo, d_hi = abs(q - Fraction(lo)), abs(Fraction(hi) - q)
+        if d_lo < d_hi:
+            want = lo
+        elif d_hi < d_lo:
+            want = hi
+        else:   # tie: the even bit pattern
+            want = lo if (int(np.float32(v).view(np.uint32) >> 16) % 2 == 0) else hi
+        assert g == want, (v, g, want)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bf16_brute_force_exact_rational(orc, seed):
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.choice([1, 2, 4]))
+    S = int(rng.integers(1, 4))
+    K = int(rng.integers(1, 9))
+    N = int(rng.integers(1, 9))
+    M = n * S
+    A = small_bf16(rng, (M, K))
+    B = small_bf16(rng, (K, N))
+    C, S_abs = orc.ag_gemm_bf16(synth.split_rows(A, n), B)
+    Af = [[Fraction(float(v)) for v in row] for row in bf16_ref(A)]
+    Bf = [[Fraction(float(v)) for v in row] for row in bf16_ref(B)]
+    for i in range(M):
+        for j in range(N):
+            exact = sum((Af[i][k] * Bf[k][j] for k in range(K)), Fraction(0))
+            mag = sum((abs(Af[i][k] * Bf[k][j]) for k in range(K)), Fraction(0))
+            want = frac_to_f32(exact)
+            assert f32_bits(C[i, j]) == f32_bits(want) or \
+                (C[i, j] == 0 and want == 0), (i, j, C[i, j], want)
+            assert Fraction(float(S_abs[i, j])) == mag
+
+
+def test_bf16_closed_forms(orc):
+    """B = I gives C = A; all-ones gives K."""
+    A, _ = synth.make_bf16(48, 32, 32, 3, "normal", 5100)
+    B = synth.to_bf16_bits(np.eye(32, dtype=np.float32))
+    C, _ = orc.ag_gemm_bf16(A, B)
+    assert np.array_equal(C.astype(np.float64), bf16_ref(np.concatenate(A)))
+    K = 1000
+    ones = synth.to_bf16_bits(np.ones((8, K), np.float32))
+    C1, S1 = orc.ag_gemm_bf16([ones] * 4, synth.to_bf16_bits(np.ones((K, 24), np.float32)))
+    assert np.all(C1 == np.float32(K)) and np.all(S1 == K)
+
+
+def test_bf16_matches_numpy_float64_and_permutation(orc):
+    shards, B = synth.make_bf16(36 * 3, 45, 29, 3, "normal", 5200)
+    C, S_abs = orc.ag_gemm_bf16(shards, B)
+    A64 = bf16_ref(np.concatenate(shards))
+    B64 = bf16_ref(B)
+    ref = A64 @ B64
+    mag = np.abs(A64) @ np.abs(B64)
+    assert np.all(np.abs(C.astype(np.float64) - ref) <= 1e-12 * mag + 2**-24 * np.abs(ref))
+    perm = [2, 0, 1]
+    Cp, _ = orc.ag_gemm_bf16([shards[p] for p in perm], B)
+    S = 36
+    for dst, src in enumerate(perm):
+        assert np.array_equal(Cp[dst * S:(dst + 1) * S], C[src * S:(src + 1) * S])
