@@ -77,6 +77,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true", help="skip the overlap modes")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 workload")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 variant")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip the pipelined chunk-size sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -232,23 +233,6 @@ def run_f16(args, torch, agg, synth):
         t_seq, _ = timed(torch, call(agg.MODE_SEQUENTIAL), n, 10)
         if agg.check():
             raise SystemExit("mode runs failed")
-    t_pipe, c_pipe = timed(torch, call(MODES[args.mode]), args.steps, args.warmup,
-                           with_consumer=args.mode != "copy")
-    rc = agg.check()
-    if rc:
-        raise SystemExit(f"{args.mode} run failed: {agg.status_string(rc)}")
-    res["step_ms"] = t_pipe
-    res["consumer_ms"] = c_pipe
-    if modes:
-        res.update(compute_only_ms=t_comp, compute_only_consumer_ms=c_comp,
-                   copy_only_ms=t_copy, sequential_ms=t_seq)
-        # hidden share of the copy, overlap efficiency and speedup (the page
-        # prints "overlap eff" without a formula; these are the readings)
-        res["hidden_fraction"] = (t_comp + t_copy - t_pipe) / t_copy
-        res["overlap_eff"] = (t_seq - t_pipe) / min(t_copy, t_comp)
-        res["speedup_vs_sequential"] = t_seq / t_pipe
-        copied = (case.n_shards - 1) * case.shard_rows * case.K * 2
-        res["copy_only_GBps"] = 2 * copied / (t_copy * 1e-3) / 1e9
     if modes and not args.no_chunk_sweep:
         # pipelined step time over chunk sizes (16 to 256 rows; 16 is the
         # automatic size here), each after its own warm-up
@@ -268,8 +252,8 @@ def run_f16(args, torch, agg, synth):
     info, _, _ = agg.plan("f16", case.n_shards, case.M, case.K, case.N, cr,
                           agg.options(tile=args.tile))
     if args.mode == "pipelined":
-        # one more pipelined call, untimed, with the device trace on: how
-        # long consumer tiles waited for chunks and when the last landed
+        # one pipelined call, untimed, with the device trace on: how long
+        # consumer tiles waited for chunks and when the last landed
         trace = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
         agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(workspace=ws, link_gbps=gbps,
                                                          tile=args.tile, trace=trace))
@@ -285,6 +269,23 @@ def run_f16(args, torch, agg, synth):
             "max_tile_wait_us": round(float(waits.max()) / 100.0, 2),
             "last_release_us": round(float(rel.max() - start) / 100.0, 2) if nc else 0.0,
             "consumer_span_us": round(float(cons[:, 2].max() - start) / 100.0, 2)}
+    t_pipe, c_pipe = timed(torch, call(MODES[args.mode]), args.steps, args.warmup,
+                           with_consumer=args.mode != "copy")
+    rc = agg.check()
+    if rc:
+        raise SystemExit(f"{args.mode} run failed: {agg.status_string(rc)}")
+    res["step_ms"] = t_pipe
+    res["consumer_ms"] = c_pipe
+    if modes:
+        res.update(compute_only_ms=t_comp, compute_only_consumer_ms=c_comp,
+                   copy_only_ms=t_copy, sequential_ms=t_seq)
+        # hidden share of the copy, overlap efficiency and speedup (the page
+        # prints "overlap eff" without a formula; these are the readings)
+        res["hidden_fraction"] = (t_comp + t_copy - t_pipe) / t_copy
+        res["overlap_eff"] = (t_seq - t_pipe) / min(t_copy, t_comp)
+        res["speedup_vs_sequential"] = t_seq / t_pipe
+        copied = (case.n_shards - 1) * case.shard_rows * case.K * 2
+        res["copy_only_GBps"] = 2 * copied / (t_copy * 1e-3) / 1e9
     res["tile"] = [info.tile_m, info.tile_n]
     res["tile_id"] = info.tile_id
     res["chunk_rows"] = info.chunk_rows
@@ -315,6 +316,33 @@ def run_i8(args, torch, agg, synth):
     return {"workload": case.name, "ms": t, "consumer_ms": c, "tops": ops / (t * 1e-3) / 1e12,
             "consumer_tops": ops / (c * 1e-3) / 1e12,
             "frac_of_peak": ops / (c * 1e-3) / 1e12 / PEAK_I8_TOPS}
+
+
+def run_bf16(args, torch, agg, synth):
+    """The bf16 variant on the same 8 x 1024-row workload, pipelined."""
+    case = synth.CASES[args.case]
+    shards, B = synth.make_bf16(case.M, case.K, case.N, case.n_shards, "normal",
+                                1000 * case.case_id)
+
+    def bdev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(
+            torch.bfloat16)
+    ts = [bdev(s) for s in shards]
+    tB = bdev(B)
+    C = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(agg.workspace_bytes(case.n_shards, case.M, case.K, 2), dtype=torch.uint8,
+                     device="cuda")
+    agg.workspace_reset(ws)
+
+    def fn(ev):
+        agg.ag_gemm_bf16(ts, tB, C, 0, opts=agg.options(workspace=ws, consumer_events=ev))
+    t, c = timed(torch, fn, max(20, args.steps // 2), 20)
+    if agg.check():
+        raise SystemExit("bf16 run failed")
+    flops = 2.0 * case.M * case.K * case.N
+    return {"workload": case.name.replace("f16", "bf16", 1), "ms": t, "consumer_ms": c,
+            "tflops": flops / (t * 1e-3) / 1e12,
+            "consumer_tflops": flops / (c * 1e-3) / 1e12}
 
 
 def cpu_baseline(case, inputs, budget_s):
@@ -400,6 +428,8 @@ def main():
         "baseline_note": "vs_baseline divides by the PTO-ISA page's 8-card 8192x4096x4096 "
                          "figure on Ascend 910B1 (191.03 TFLOPS): other hardware, context only",
     }
+    if not args.no_bf16:
+        line["bf16"] = run_bf16(args, torch, agg, synth)
     if not args.no_int8:
         line["int8"] = run_i8(args, torch, agg, synth)
     if not args.no_cpu_baseline:

@@ -1,6 +1,7 @@
 """Build libaggemm.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m communication_gemm_amd.build
+    python communication_gemm_amd/build.py   (run by path: importing the
+                                             package would load the library)
 """
 from __future__ import annotations
 

@@ -36,7 +36,7 @@ struct Device {
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
-    int occ[2][16] = {{0}};   // by tile id
+    int occ[3][16] = {{0}};   // by kind and tile id
 };
 
 std::mutex g_mu;
@@ -165,7 +165,7 @@ int run(const Call& c)
     rc = make_plan(c.kind, c.n, c.M, c.K, c.N, c.chunk_rows, opt, d->num_cus, &p);
     if (rc) return rc;
 
-    const int kind = c.kind == kF16 ? 0 : 1;
+    const int kind = static_cast<int>(c.kind);
     const bool run_producer = p.mode != AGG_MODE_COMPUTE_ONLY && c.n > 1 && c.K > 0;
     const bool run_consumer = p.mode != AGG_MODE_COPY_ONLY;
 
@@ -247,8 +247,9 @@ int run(const Call& c)
         hipError_t e = hipSuccess;
         if (cev[0]) e = hipEventRecord(cev[0], st);
         if (e == hipSuccess)
-            e = (c.kind == kF16) ? launch_consumer_f16(ca, p.shape.id, cwgs, st)
-                                 : launch_consumer_i8(ca, p.shape.id, cwgs, st);
+            e = c.kind == kF16    ? launch_consumer_f16(ca, p.shape.id, cwgs, st)
+                : c.kind == kBF16 ? launch_consumer_bf16(ca, p.shape.id, cwgs, st)
+                                  : launch_consumer_i8(ca, p.shape.id, cwgs, st);
         if (e == hipSuccess && cev[1]) e = hipEventRecord(cev[1], st);
         return e;
     };
@@ -311,6 +312,21 @@ int ag_gemm_f16_ex(const void* const* shards, int n_shards, const void* B, float
                    const agg_options* opt)
 {
     Call c{kF16, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
+           static_cast<hipStream_t>(stream), opt};
+    return run(c);
+}
+
+int ag_gemm_bf16(const void* const* shards, int n_shards, const void* B, float* C,
+                 int64_t M, int64_t K, int64_t N, int chunk_rows, void* stream)
+{
+    return ag_gemm_bf16_ex(shards, n_shards, B, C, M, K, N, chunk_rows, stream, nullptr);
+}
+
+int ag_gemm_bf16_ex(const void* const* shards, int n_shards, const void* B, float* C,
+                    int64_t M, int64_t K, int64_t N, int chunk_rows, void* stream,
+                    const agg_options* opt)
+{
+    Call c{kBF16, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
            static_cast<hipStream_t>(stream), opt};
     return run(c);
 }

@@ -1,5 +1,6 @@
-// consumer.hip -- the persistent MFMA consumer GEMM (fp16 -> fp32 and
-// int8 -> int32 + bias -> per-channel dequant -> fp16).
+// consumer.hip -- the persistent MFMA consumer GEMM (fp16 -> fp32, its
+// bf16 -> fp32 variant, and int8 -> int32 + bias -> per-channel dequant
+// -> fp16).
 //
 // One workgroup per CU walks the tile list of the shared schedule: first
 // the local shard's tiles (no wait), then the remote tiles in the order
@@ -36,6 +37,7 @@ namespace agg {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx16 __attribute__((ext_vector_type(16)));
@@ -111,6 +113,16 @@ struct F16 {
                 (LDS_PTR short4_*)(p + (16 * kk + 4 * h) * LB));
         uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+};
+
+// bfloat16: the fp16 engine (same 16-bit layout, swizzles and transpose
+// reads) with the bf16 MFMA.
+struct BF16 : F16 {
+    __device__ static Acc mma(const uint4& a, const uint4& b, const Acc& c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
 };
 
@@ -718,6 +730,11 @@ hipError_t launch_consumer_f16(const ConsumerArgs& a, int tile_id, int wgs, hipS
     return launch_kind<F16>(a, tile_id, wgs, st);
 }
 
+hipError_t launch_consumer_bf16(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
+{
+    return launch_kind<BF16>(a, tile_id, wgs, st);
+}
+
 hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
 {
     return launch_kind<I8>(a, tile_id, wgs, st);
@@ -725,7 +742,9 @@ hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs, hipSt
 
 int consumer_occupancy(int kind, int tile_id)
 {
-    return kind == 0 ? occupancy_kind<F16>(tile_id) : occupancy_kind<I8>(tile_id);
+    return kind == 0 ? occupancy_kind<F16>(tile_id)
+         : kind == 2 ? occupancy_kind<BF16>(tile_id)
+                     : occupancy_kind<I8>(tile_id);
 }
 
 }  // namespace agg

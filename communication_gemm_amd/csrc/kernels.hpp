@@ -55,6 +55,8 @@ hipError_t launch_consumer_f16(const ConsumerArgs& a, int tile_id, int wgs,
                                hipStream_t st);
 hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs,
                               hipStream_t st);
+hipError_t launch_consumer_bf16(const ConsumerArgs& a, int tile_id, int wgs,
+                                hipStream_t st);
 hipError_t launch_header_reset(uint32_t* header, size_t bytes, hipStream_t st);
 
 // Workgroups of a consumer tile shape that fit on one CU at once.

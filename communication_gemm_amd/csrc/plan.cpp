@@ -52,7 +52,7 @@ const TileShape kI8Shapes[] = {
 
 const TileShape* tile_shapes(Kind kind, int* count)
 {
-    if (kind == kF16) {
+    if (kind == kF16 || kind == kBF16) {   // bf16 runs the fp16 engine
         *count = (int)(sizeof(kF16Shapes) / sizeof(kF16Shapes[0]));
         return kF16Shapes;
     }
@@ -97,7 +97,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (M % n_shards) return AGG_E_INVALID;
     const int64_t S = M / n_shards;
     if (chunk_rows < 0 || (S > 0 && chunk_rows > S)) return AGG_E_INVALID;
-    const int kvec = (kind == kF16) ? 8 : 16;   // elements per 16-byte load
+    const int kvec = (kind == kI8) ? 16 : 8;    // elements per 16-byte load
     if (K % kvec || N % 8) return AGG_E_UNSUPPORTED;
     if (opt->local_shard < 0 || opt->local_shard >= n_shards) return AGG_E_INVALID;
     if (opt->mode < AGG_MODE_PIPELINED || opt->mode > AGG_MODE_COPY_ONLY)
@@ -130,7 +130,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
     if (n_shards > 1 && s.cps > kFlagCap) return AGG_E_UNSUPPORTED;
     // the producer moves a chunk with 32-bit buffer offsets
-    if ((int64_t)s.cr * K * (kind == kF16 ? 2 : 1) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
+    if ((int64_t)s.cr * K * (kind == kI8 ? 1 : 2) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
 
     // send order: a permutation of the remote shards
     for (int i = 0; i < kMaxShards; ++i) { s.order[i] = -1; s.slot[i] = -1; }
@@ -180,7 +180,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
     if (cw < 1) cw = 1;
     // pieces per chunk (a chunk is below 2 GiB, so at most 65536)
-    const int64_t chunk_bytes = (int64_t)s.cr * K * (kind == kF16 ? 2 : 1);
+    const int64_t chunk_bytes = (int64_t)s.cr * K * (kind == kI8 ? 1 : 2);
     const int ppc = chunk_bytes > 0 ? (int)cdiv(chunk_bytes, kPieceBytes) : 1;
     const int64_t items = chunks * ppc;
     int pw = opt->producer_wgs ? opt->producer_wgs : num_cus;
@@ -191,7 +191,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     p.ppc = ppc;
     p.mode = opt->mode;
     p.link_gbps = opt->link_gbps;
-    p.elt = (kind == kF16) ? 2 : 1;
+    p.elt = (kind == kI8) ? 1 : 2;
     p.M = M;
     p.ws_bytes = workspace_bytes(n_shards, M, K, p.elt);
     p.drop_chunk = opt->debug_drop_chunk;
@@ -243,9 +243,9 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
                  int chunk_rows, const agg_options* opt, int num_cus,
                  agg_plan_info* info, int32_t* tile_order, int32_t* chunk_order)
 {
-    if (kind != 0 && kind != 1) return AGG_E_INVALID;
+    if (kind != 0 && kind != 1 && kind != 2) return AGG_E_INVALID;
     agg::Plan p;
-    int rc = agg::make_plan(kind == 0 ? agg::kF16 : agg::kI8, n_shards, M, K,
+    int rc = agg::make_plan(static_cast<agg::Kind>(kind), n_shards, M, K,
                             N, chunk_rows, opt, num_cus, &p);
     if (rc) return rc;
     const agg::Schedule& s = p.sched;

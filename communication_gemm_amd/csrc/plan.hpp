@@ -9,7 +9,7 @@
 
 namespace agg {
 
-enum Kind { kF16 = 0, kI8 = 1 };
+enum Kind { kF16 = 0, kI8 = 1, kBF16 = 2 };
 
 struct TileShape {
     int id;         // 1-based id accepted by agg_options.tile

@@ -140,6 +140,19 @@ int ag_gemm_f16_ex(const void *const *shards, int n_shards, const void *B,
                    void *stream, const agg_options *opt);
 
 /*
+ * bf16 x bf16 -> fp32 streamed AllGather + GEMM: the fp16 operation above
+ * with bfloat16 shards and B (same layouts, alignment, size limits and
+ * errors; C fp32).  A variant of the PTO-ISA README's fp16 path in the
+ * other 16-bit input format.
+ */
+int ag_gemm_bf16(const void *const *shards, int n_shards, const void *B,
+                 float *C, int64_t M, int64_t K, int64_t N, int chunk_rows,
+                 void *stream);
+int ag_gemm_bf16_ex(const void *const *shards, int n_shards, const void *B,
+                    float *C, int64_t M, int64_t K, int64_t N, int chunk_rows,
+                    void *stream, const agg_options *opt);
+
+/*
  * int8 x int8 -> int32, + bias, x per-channel scale -> fp16
  * (catccos AllGatherMatmulDequant design doc, sections 1.2 and 2.2):
  *   v = A x B + bias[n]        exact int32
@@ -212,8 +225,8 @@ typedef struct agg_plan_info {
 
 /*
  * The schedule one call would run, for inspection and tests.
- *   kind: 0 = fp16 path, 1 = int8 path; num_cus: CUs of the device to plan
- *   for (0 = 256).  tile_order (nullable, capacity total_tiles * 4 int32):
+ *   kind: 0 = fp16 path, 1 = int8 path, 2 = bf16 path; num_cus: CUs of
+ *   the device to plan for (0 = 256).  tile_order (nullable, capacity total_tiles * 4 int32):
  *   per consumer position: shard, m-tile, n-tile, counter value waited for
  *   (0 for the local shard).  chunk_order (nullable, capacity total_chunks
  *   * 2 int32): per producer position: shard, chunk index.

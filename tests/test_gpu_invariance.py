@@ -126,3 +126,23 @@ def test_i8_invariant_across_schedules(agg, orc):
         outs.append(C)
     for C in outs[1:]:
         assert torch.equal(C, outs[0])
+
+
+def test_bf16_invariant_across_schedules(agg):
+    """The bf16 path shares the schedule machinery: its output is also
+    bitwise independent of chunking, local shard, link pacing and mode."""
+    shards, Bn = synth.make_bf16(4 * 256, 512, 384, 4, "normal", 52000)
+
+    def bdev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    ts = [bdev(s) for s in shards]
+    B = bdev(Bn)
+    outs = []
+    for kw, cr in [(dict(), 0), (dict(local_shard=2, send_order=[0, 3, 1]), 5),
+                   (dict(link_model=1, link_gbps=40.0), 64), (dict(mode=2), 3)]:
+        C = torch.full((1024, 384), float("nan"), device="cuda")
+        agg.ag_gemm_bf16(ts, B, C, cr, opts=agg.options(**kw))
+        assert agg.check() == 0
+        outs.append(C)
+    for C in outs[1:]:
+        assert torch.equal(C, outs[0])

@@ -213,3 +213,44 @@ def test_case5_sampled_rows(agg, orc):
     rows = sample_rows(c.M, c.n_shards, agg.pick_chunk_rows(c.shard_rows), extra=6)
     ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale, rows=rows)
     check_i8(acc[rows], D[rows], ao, Do, c.name)
+
+
+# ---------------------------------------------------------------- bf16 path
+
+def bf16_dev(a):
+    """uint16 bfloat16 bit patterns -> a bfloat16 CUDA tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def run_bf16(agg, shards, B, chunk_rows=0, opts=None):
+    ts = [bf16_dev(s) for s in shards]
+    M = sum(s.shape[0] for s in shards)
+    C = torch.full((M, B.shape[1]), float("nan"), dtype=torch.float32, device="cuda")
+    agg.ag_gemm_bf16(ts, bf16_dev(B), C, chunk_rows, opts=opts)
+    rc = agg.check()
+    assert rc == 0, agg.status_string(rc)
+    return C.cpu().numpy()
+
+
+def test_bf16_small_full(agg, orc):
+    shards, B = synth.make_bf16(256, 256, 128, 2, "normal", 35000)
+    C = run_bf16(agg, shards, B, 32)
+    Co, So = orc.ag_gemm_bf16(shards, B)
+    check_f16(C, Co, So, "bf16 small")
+
+
+@pytest.mark.parametrize("tile", [3, 8, 6])
+def test_bf16_ragged(agg, orc, tile):
+    shards, B = synth.make_bf16(3 * 100, 296, 168, 3, "uniform", 35100 + tile)
+    C = run_bf16(agg, shards, B, 7, agg.options(tile=tile))
+    Co, So = orc.ag_gemm_bf16(shards, B)
+    check_f16(C, Co, So, f"bf16 ragged tile {tile}")
+
+
+def test_bf16_large_sampled_rows(agg, orc):
+    n, S, K, N = 8, 1024, 4096, 4096
+    shards, B = synth.make_bf16(n * S, K, N, n, "normal", 35200)
+    C = run_bf16(agg, shards, B)
+    rows = sample_rows(n * S, n, agg.pick_chunk_rows(S))
+    Co, So = orc.ag_gemm_bf16(shards, B, rows=rows)
+    check_f16(C[rows], Co, So, "bf16 8x1024x4096x4096")
