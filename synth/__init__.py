@@ -71,6 +71,12 @@ CASES: dict[int, Case] = {
             note="8 shards of 1024 rows"),
     5: Case(5, "i8", 2, 16384, 27392, 4096,
             note="int8 + bias + per-channel dequant, 2 shards of 8192 rows"),
+    # the other two rows of the catccos test-shape table (section 8.3),
+    # read like the first: M is the gathered row count, over 2 shards
+    6: Case(6, "i8", 2, 131072, 8192, 3072,
+            note="int8 + dequant, 2 shards of 65536 rows"),
+    7: Case(7, "i8", 2, 64, 16384, 7168,
+            note="int8 + dequant, small-M (decode-like), 2 shards of 32 rows"),
 }
 
 
@@ -143,7 +149,7 @@ def make_i8(M: int, K: int, N: int, n_shards: int, seed_base: int = 0):
 
 
 def make_case(case: Case | int):
-    """Inputs of one of the five workloads, seeded by its id."""
+    """Inputs of one of the seeded workloads, seeded by its id."""
     if isinstance(case, int):
         case = CASES[case]
     base = 1000 * case.case_id

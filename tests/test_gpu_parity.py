@@ -206,13 +206,24 @@ def test_i8_debug_mode_all_ones(agg):
                           np.broadcast_to(wantD.view(np.uint16), (256, N)))
 
 
-def test_case5_sampled_rows(agg, orc):
-    c = synth.CASES[5]
+@pytest.mark.parametrize("cid", [5, 6])
+def test_i8_cases_sampled_rows(agg, orc, cid):
+    c = synth.CASES[cid]
     shards, B, bias, scale = synth.make_case(c)
     acc, D = run_i8(agg, shards, B, bias, scale)
     rows = sample_rows(c.M, c.n_shards, agg.pick_chunk_rows(c.shard_rows), extra=6)
     ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale, rows=rows)
     check_i8(acc[rows], D[rows], ao, Do, c.name)
+
+
+def test_i8_small_m_full(agg, orc):
+    """The decode-like shape: 64 gathered rows, so every shard is a
+    single, partial m-tile and the grid is set by the n-tiles."""
+    c = synth.CASES[7]
+    shards, B, bias, scale = synth.make_case(c)
+    acc, D = run_i8(agg, shards, B, bias, scale)
+    ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale)
+    check_i8(acc, D, ao, Do, c.name)
 
 
 # ---------------------------------------------------------------- bf16 path
