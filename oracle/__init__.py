@@ -13,6 +13,8 @@ Definitions followed (see ``oracle.c`` for the full statement):
     concatenation on dim 0 and matmul);
   * fp16 path: fp64 sum of exact products, rounded once to fp32;
   * bf16 path: the same with bfloat16 inputs;
+  * fp8 path: the same with OCP FP8 E4M3 inputs (the float8_e4m3fn inputs
+    of the Ascend grouped-GEMM page's FP8 variant);
   * int8 path: exact integer sum + int32 bias, fp32 conversion, fp32 product
     with the per-channel scale, fp16 rounding (catccos AllGatherMatmulDequant
     design doc, section 2.2).
@@ -57,6 +59,8 @@ def _load():
             lib.oracle_ag_gemm_f16.argtypes = [P, ctypes.c_int, P, I64, I64, I64, P, P]
             lib.oracle_ag_gemm_bf16_rows.argtypes = [P, ctypes.c_int, P, I64, I64, I64, P, I64, P, P]
             lib.oracle_bf16_to_double_n.argtypes = [P, P, I64]
+            lib.oracle_ag_gemm_fp8_rows.argtypes = [P, ctypes.c_int, P, I64, I64, I64, P, I64, P, P]
+            lib.oracle_fp8e4m3_to_double_n.argtypes = [P, P, I64]
             lib.oracle_ag_gemm_i8_rows.argtypes = [P, ctypes.c_int, P, P, P, I64, I64, I64, P, I64, P, P]
             lib.oracle_ag_gemm_i8.argtypes = [P, ctypes.c_int, P, P, P, I64, I64, I64, P, P]
             lib.oracle_half_to_double_n.argtypes = [P, P, I64]
@@ -130,6 +134,34 @@ def ag_gemm_bf16(shards, B, rows=None, with_abs: bool = True):
     if rc:
         raise RuntimeError(f"oracle_ag_gemm_bf16_rows failed ({rc})")
     return C, S_abs
+
+
+def ag_gemm_fp8(shards, B, rows=None, with_abs: bool = True):
+    """fp8 (E4M3) variant of ag_gemm_f16.  Shards and B are uint8 arrays of
+    E4M3 bit patterns."""
+    lib = _load()
+    arrs, table = _shard_table(shards, np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    M, K, N = _dims(arrs, B)
+    if rows is None:
+        rows = np.arange(M, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    C = np.empty((len(rows), N), np.float32)
+    S_abs = np.empty((len(rows), N), np.float64) if with_abs else None
+    rc = lib.oracle_ag_gemm_fp8_rows(table, len(arrs), _ptr(B), M, K, N,
+                                     _ptr(rows), len(rows), _ptr(C),
+                                     _ptr(S_abs) if with_abs else None)
+    if rc:
+        raise RuntimeError(f"oracle_ag_gemm_fp8_rows failed ({rc})")
+    return C, S_abs
+
+
+def fp8_to_double(h: np.ndarray) -> np.ndarray:
+    lib = _load()
+    h = np.ascontiguousarray(h, dtype=np.uint8)
+    out = np.empty(h.shape, np.float64)
+    lib.oracle_fp8e4m3_to_double_n(_ptr(h), _ptr(out), h.size)
+    return out
 
 
 def bf16_to_double(h: np.ndarray) -> np.ndarray:

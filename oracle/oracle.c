@@ -23,6 +23,9 @@
  *       error bound; S[i,j] = sum_k |A[i,k] * B[k,j]| is emitted for it.
  *   bf16 path:  the same with bfloat16 A and B (a variant of the fp16
  *       path: same gather, same fp32 output, a different input format).
+ *   fp8 path:   the same with OCP FP8 E4M3 A and B (the float8_e4m3fn
+ *       inputs of the Ascend grouped-GEMM page's FP8 variant); a product
+ *       of two such values (4 significant bits each) is exact in double.
  *   int8 path (catccos AllGatherMatmulDequant doc, section 2.2):
  *       v[i,j] = sum_k A[i,k] * B[k,j] + bias[j]     (exact, int64, must
  *                                                     fit in int32)
@@ -158,24 +161,62 @@ double oracle_bf16_to_double(uint16_t h)
 }
 
 /* ------------------------------------------------------------------ */
-/* 16-bit floats x 16-bit floats -> fp32 (fp16 and bf16 paths)          */
+/* OCP FP8 E4M3 ("e4m3fn"), written from the format's definition: 1    */
+/* sign bit, 4 exponent bits (bias 7), 3 fraction bits; no infinities; */
+/* exponent 15 with fraction 7 is NaN, so the largest value is 448.    */
 /* ------------------------------------------------------------------ */
 
-typedef double (*decode16_fn)(uint16_t);
+double oracle_fp8e4m3_to_double(uint8_t h)
+{
+    int sign = (h >> 7) & 1;
+    int e = (h >> 3) & 0xf;
+    int f = h & 0x7;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -9);                  /* subnormal: f * 2^-9 */
+    } else if (e == 15 && f == 7) {
+        v = NAN;
+    } else {
+        v = ldexp((double)(8 + f), e - 10);        /* (1.f) * 2^(e-7)     */
+    }
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------ */
+/* Float formats x the same format -> fp32 (fp16, bf16 and fp8 paths)   */
+/* ------------------------------------------------------------------ */
+
+/* element i of an array of the input format, as a double */
+typedef double (*decode_fn)(const void *p, int64_t i);
+
+static double dec_f16(const void *p, int64_t i)
+{
+    return oracle_half_to_double(((const uint16_t *)p)[i]);
+}
+
+static double dec_bf16(const void *p, int64_t i)
+{
+    return oracle_bf16_to_double(((const uint16_t *)p)[i]);
+}
+
+static double dec_fp8(const void *p, int64_t i)
+{
+    return oracle_fp8e4m3_to_double(((const uint8_t *)p)[i]);
+}
 
 /*
  * Rows `rows[0..n_rows)` of C = gather(shards) x B, the elements of both
- * decoded by `dec`.  C_rows: n_rows x N fp32; abs_rows (may be NULL):
- * n_rows x N double, the sum over k of |A[i,k] B[k,j]|.  A product of two
- * fp16 values (11 significant bits each) or two bf16 values (8 each) is
- * exact in double.
+ * (`elt` bytes each) decoded by `dec`.  C_rows: n_rows x N fp32; abs_rows
+ * (may be NULL): n_rows x N double, the sum over k of |A[i,k] B[k,j]|.  A
+ * product of two fp16 values (11 significant bits each), two bf16 values
+ * (8 each) or two fp8 values (4 each) is exact in double.
  */
-static int ag_gemm_16bit_rows(decode16_fn dec, const uint16_t *const *shards,
-                              int n_shards, const uint16_t *B, int64_t M,
+static int ag_gemm_float_rows(decode_fn dec, size_t elt, const void *const *shards,
+                              int n_shards, const void *B, int64_t M,
                               int64_t K, int64_t N, const int64_t *rows,
                               int64_t n_rows, float *C_rows, double *abs_rows)
 {
-    if (check_shape((const void *const *)shards, n_shards, M, K, N))
+    if (check_shape(shards, n_shards, M, K, N))
         return 1;
     int64_t S = M / n_shards;
     for (int64_t t = 0; t < n_rows; t++)
@@ -186,7 +227,7 @@ static int ag_gemm_16bit_rows(decode16_fn dec, const uint16_t *const *shards,
     if (!Bd)
         return 2;
     for (int64_t x = 0; x < K * N; x++)
-        Bd[x] = dec(B[x]);
+        Bd[x] = dec(B, x);
 
     int fail = 0;
 #pragma omp parallel
@@ -201,11 +242,10 @@ static int ag_gemm_16bit_rows(decode16_fn dec, const uint16_t *const *shards,
         for (int64_t t = 0; t < n_rows; t++) {
             if (!acc || !mag)
                 continue;
-            const uint16_t *a = (const uint16_t *)gathered_row(
-                (const void *const *)shards, S, K, rows[t], 2);
+            const void *a = gathered_row(shards, S, K, rows[t], elt);
             for (int64_t j = 0; j < N; j++) { acc[j] = 0.0; mag[j] = 0.0; }
             for (int64_t k = 0; k < K; k++) {
-                double aik = dec(a[k]);
+                double aik = dec(a, k);
                 const double *b = Bd + k * N;
                 for (int64_t j = 0; j < N; j++) {
                     double p = aik * b[j];          /* exact */
@@ -232,8 +272,8 @@ int oracle_ag_gemm_f16_rows(const uint16_t *const *shards, int n_shards,
                             const int64_t *rows, int64_t n_rows,
                             float *C_rows, double *abs_rows)
 {
-    return ag_gemm_16bit_rows(oracle_half_to_double, shards, n_shards, B, M, K,
-                              N, rows, n_rows, C_rows, abs_rows);
+    return ag_gemm_float_rows(dec_f16, 2, (const void *const *)shards, n_shards, B,
+                              M, K, N, rows, n_rows, C_rows, abs_rows);
 }
 
 /* bf16 x bf16 -> fp32: the same definition with bfloat16 inputs. */
@@ -242,8 +282,18 @@ int oracle_ag_gemm_bf16_rows(const uint16_t *const *shards, int n_shards,
                              const int64_t *rows, int64_t n_rows,
                              float *C_rows, double *abs_rows)
 {
-    return ag_gemm_16bit_rows(oracle_bf16_to_double, shards, n_shards, B, M, K,
-                              N, rows, n_rows, C_rows, abs_rows);
+    return ag_gemm_float_rows(dec_bf16, 2, (const void *const *)shards, n_shards, B,
+                              M, K, N, rows, n_rows, C_rows, abs_rows);
+}
+
+/* fp8 (E4M3) x fp8 -> fp32: the same definition with fp8 inputs. */
+int oracle_ag_gemm_fp8_rows(const uint8_t *const *shards, int n_shards,
+                            const uint8_t *B, int64_t M, int64_t K, int64_t N,
+                            const int64_t *rows, int64_t n_rows,
+                            float *C_rows, double *abs_rows)
+{
+    return ag_gemm_float_rows(dec_fp8, 1, (const void *const *)shards, n_shards, B,
+                              M, K, N, rows, n_rows, C_rows, abs_rows);
 }
 
 /* Whole C (M x N fp32) and optionally the whole |.| sum (M x N double). */
@@ -358,6 +408,12 @@ void oracle_bf16_to_double_n(const uint16_t *h, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; i++)
         out[i] = oracle_bf16_to_double(h[i]);
+}
+
+void oracle_fp8e4m3_to_double_n(const uint8_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_fp8e4m3_to_double(h[i]);
 }
 
 void oracle_float_to_half_n(const float *x, uint16_t *out, int64_t n)

@@ -27,7 +27,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Case", "CASES", "make_f16", "make_bf16", "make_i8", "make_case", "split_rows"]
+__all__ = ["Case", "CASES", "make_f16", "make_bf16", "make_fp8", "make_i8", "make_case",
+           "split_rows"]
 
 
 @dataclass(frozen=True)
@@ -133,6 +134,50 @@ def make_bf16(M: int, K: int, N: int, n_shards: int, dist: str = "normal",
         else:
             raise ValueError(dist)
         return to_bf16_bits(x)
+
+    A = draw(seed_base + 1, (M, K))
+    B = draw(seed_base + 2, (K, N))
+    return split_rows(A, n_shards), B
+
+
+def _e4m3_values() -> np.ndarray:
+    """Values of the non-negative finite OCP FP8 E4M3 codes 0x00..0x7E, in
+    code order (which is also increasing value order)."""
+    c = np.arange(0x7F)
+    e, f = c >> 3, c & 7
+    return np.where(e == 0, f * 2.0 ** -9, (8 + f) * np.exp2(e - 10.0))
+
+
+def to_fp8e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values -> OCP FP8 E4M3 bit patterns (uint8), round to nearest
+    even; finite inputs of magnitude below 464 only (464 and above would
+    round past the largest value, 448)."""
+    x = np.asarray(x, np.float32)
+    a = np.abs(x.astype(np.float64))
+    if not np.all(a < 464.0):
+        raise ValueError("value outside the E4M3 range")
+    vals = _e4m3_values()
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
+    code = np.where(a == vals[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+
+
+def make_fp8(M: int, K: int, N: int, n_shards: int, dist: str = "normal",
+             seed_base: int = 0):
+    """OCP FP8 E4M3 shards of A and B, as uint8 bit patterns; drawn like
+    make_f16, then rounded to E4M3."""
+    def draw(seed, shape):
+        g = _rng(seed)
+        if dist == "normal":
+            x = g.standard_normal(shape, dtype=np.float32)
+        elif dist == "uniform":
+            x = g.uniform(-1.0, 1.0, shape).astype(np.float32)
+        else:
+            raise ValueError(dist)
+        return to_fp8e4m3_bits(x)
 
     A = draw(seed_base + 1, (M, K))
     B = draw(seed_base + 2, (K, N))

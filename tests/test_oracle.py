@@ -322,6 +322,10 @@ MUTATIONS = [
     ("volatile float p = f * s;", "volatile float p = f * s * 1.0001f;"),
     ("if (rem > halfway || (rem == halfway && (q & 1)))", "if (rem >= halfway)"),
     ("v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),  # bf16 bias
+    ("v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 9);"),  # fp8 bias
+    ("v = ldexp((double)f, -9);", "v = ldexp((double)f, -10);"),  # fp8 subnormal scale
+    ("return oracle_fp8e4m3_to_double(((const uint8_t *)p)[i]);",
+     "return oracle_fp8e4m3_to_double(((const uint8_t *)p)[i] & 0x7f);"),  # fp8 sign dropped
 ]
 
 
@@ -358,6 +362,9 @@ def test_planted_mistake_is_caught(orc, tmp_path, idx, monkeypatch):
         lambda: test_half_encode_matches_numpy_rne(oracle_mod),
         lambda: test_bf16_decode_exhaustive(oracle_mod),
         lambda: test_bf16_brute_force_exact_rational(oracle_mod, 0),
+        lambda: test_fp8_decode_exhaustive(oracle_mod),
+        lambda: test_fp8_brute_force_exact_rational(oracle_mod, 0),
+        lambda: test_fp8_brute_force_exact_rational(oracle_mod, 3),
     ]
     caught = 0
     for chk in checks:
@@ -490,6 +497,99 @@ def test_bf16_matches_numpy_float64_and_permutation(orc):
     assert np.all(np.abs(C.astype(np.float64) - ref) <= 1e-12 * mag + 2**-24 * np.abs(ref))
     perm = [2, 0, 1]
     Cp, _ = orc.ag_gemm_bf16([shards[p] for p in perm], B)
+    S = 36
+    for dst, src in enumerate(perm):
+        assert np.array_equal(Cp[dst * S:(dst + 1) * S], C[src * S:(src + 1) * S])
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP E4M3) x fp8 -> fp32 (the fp16 definition with E4M3 inputs)
+# ----------------------------------------------------------------------------
+
+def fp8_ref(h):
+    """E4M3 bits -> float64 through torch's own float8_e4m3fn decoding."""
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.ascontiguousarray(h, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def random_fp8(rng, shape):
+    """Random E4M3 codes, NaN codes excluded."""
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c & 0xF0, c).astype(np.uint8)
+
+
+def test_fp8_decode_exhaustive(orc):
+    h = np.arange(256, dtype=np.uint8)
+    ours = orc.fp8_to_double(h)
+    ref = fp8_ref(h)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # closed forms of the format: 1.0, the largest value, the smallest
+    # normal and subnormal, negative zero
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0
+    assert ours[0x08] == 2.0 ** -6 and ours[0x01] == 2.0 ** -9
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+
+
+def test_fp8_input_rounding_matches_torch():
+    """The generator's float32 -> E4M3 rounding, against torch's
+    float8_e4m3fn cast on random values and on every tie."""
+    torch = pytest.importorskip("torch")
+    v = synth._e4m3_values()
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    x = np.concatenate([np.random.default_rng(6).standard_normal(50000).astype(np.float32) * 8,
+                        mids, -mids, np.float32([0.0, -0.0, 448.0, -448.0])])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(synth.to_fp8e4m3_bits(x), ref)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fp8_brute_force_exact_rational(orc, seed):
+    rng = np.random.default_rng(400 + seed)
+    n = int(rng.choice([1, 2, 4]))
+    S = int(rng.integers(1, 4))
+    K = int(rng.integers(1, 9))
+    N = int(rng.integers(1, 9))
+    M = n * S
+    A = random_fp8(rng, (M, K))
+    B = random_fp8(rng, (K, N))
+    C, S_abs = orc.ag_gemm_fp8(synth.split_rows(A, n), B)
+    Af = [[Fraction(float(v)) for v in row] for row in fp8_ref(A)]
+    Bf = [[Fraction(float(v)) for v in row] for row in fp8_ref(B)]
+    for i in range(M):
+        for j in range(N):
+            exact = sum((Af[i][k] * Bf[k][j] for k in range(K)), Fraction(0))
+            mag = sum((abs(Af[i][k] * Bf[k][j]) for k in range(K)), Fraction(0))
+            want = frac_to_f32(exact)
+            assert f32_bits(C[i, j]) == f32_bits(want) or \
+                (C[i, j] == 0 and want == 0), (i, j, C[i, j], want)
+            assert Fraction(float(S_abs[i, j])) == mag
+
+
+def test_fp8_closed_forms(orc):
+    """B = I gives C = A; all-ones gives K."""
+    A, _ = synth.make_fp8(48, 32, 32, 3, "normal", 5300)
+    B = synth.to_fp8e4m3_bits(np.eye(32, dtype=np.float32))
+    C, _ = orc.ag_gemm_fp8(A, B)
+    assert np.array_equal(C.astype(np.float64), fp8_ref(np.concatenate(A)))
+    K = 1000
+    ones = synth.to_fp8e4m3_bits(np.ones((8, K), np.float32))
+    C1, S1 = orc.ag_gemm_fp8([ones] * 4, synth.to_fp8e4m3_bits(np.ones((K, 24), np.float32)))
+    assert np.all(C1 == np.float32(K)) and np.all(S1 == K)
+
+
+def test_fp8_matches_numpy_float64_and_permutation(orc):
+    shards, B = synth.make_fp8(36 * 3, 45, 29, 3, "normal", 5400)
+    C, S_abs = orc.ag_gemm_fp8(shards, B)
+    A64 = fp8_ref(np.concatenate(shards))
+    B64 = fp8_ref(B)
+    ref = A64 @ B64
+    mag = np.abs(A64) @ np.abs(B64)
+    assert np.all(np.abs(C.astype(np.float64) - ref) <= 1e-12 * mag + 2**-24 * np.abs(ref))
+    perm = [1, 2, 0]
+    Cp, _ = orc.ag_gemm_fp8([shards[p] for p in perm], B)
     S = 36
     for dst, src in enumerate(perm):
         assert np.array_equal(Cp[dst * S:(dst + 1) * S], C[src * S:(src + 1) * S])
