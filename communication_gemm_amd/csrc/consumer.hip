@@ -227,7 +227,7 @@ struct Engine {
     static constexpr int kGroup = (kAInstr + kBInstr) / kWaves;   // loads per wave per slice
     static_assert(kAInstr % kWaves == 0 && kBInstr % kWaves == 0, "loads split over the waves");
     static_assert(kTM >= 1 && kTN >= 1 && kWaves % 4 == 0, "wave grid");
-    static_assert(kSteps % 2 == 0 && NS >= 2 && NS <= 4, "pipeline shape");
+    static_assert(kSteps % 2 == 0 && NS >= 2 && NS <= 8, "pipeline shape");
     static_assert(kLds + 1024 <= kLdsBytes, "LDS ring too large");
     static_assert(kGroup * (NS - 2) < 64, "vmcnt range");
 
@@ -384,15 +384,16 @@ struct Engine {
 
     // Wait until at most `behind` slices of this wave's loads are still in
     // flight (and every LDS read has returned).
+    // `behind` is at most NS - 2.
+    template <int kB = NS - 2>
     __device__ __forceinline__ static void wait_slices(int behind)
     {
-        if constexpr (NS >= 4) {
-            if (behind >= 2) { wait_vm_lgkm0<2 * kGroup>(); return; }
+        if constexpr (kB > 0) {
+            if (behind >= kB) { wait_vm_lgkm0<kB * kGroup>(); return; }
+            wait_slices<kB - 1>(behind);
+        } else {
+            wait_vm_lgkm0<0>();
         }
-        if constexpr (NS >= 3) {
-            if (behind >= 1) { wait_vm_lgkm0<kGroup>(); return; }
-        }
-        wait_vm_lgkm0<0>();
     }
 
     // One k-slice.  On entry f0 holds step 0 of `cur`; on exit it holds
@@ -652,6 +653,8 @@ template <> struct Cfg<8> { static constexpr int BM = 256, BN = 256, SB = 128, N
 template <> struct Cfg<9> { static constexpr int BM = 256, BN = 256, SB = 64, NS = 4, WM = 2, WN = 4; };
 template <> struct Cfg<10> { static constexpr int BM = 256, BN = 128, SB = 128, NS = 2, WM = 4, WN = 2; };
 template <> struct Cfg<11> { static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WM = 2, WN = 4; };
+template <> struct Cfg<12> { static constexpr int BM = 64, BN = 64, SB = 128, NS = 8, WM = 2, WN = 2; };
+template <> struct Cfg<13> { static constexpr int BM = 64, BN = 64, SB = 256, NS = 4, WM = 2, WN = 2; };
 
 template <class T, int ID>
 struct Kern {
@@ -700,6 +703,8 @@ hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t 
     case 9: return Kern<T, 9>::launch(a, wgs, st);
     case 10: return Kern<T, 10>::launch(a, wgs, st);
     case 11: return Kern<T, 11>::launch(a, wgs, st);
+    case 12: return Kern<T, 12>::launch(a, wgs, st);
+    case 13: return Kern<T, 13>::launch(a, wgs, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -719,6 +724,8 @@ int occupancy_kind(int tile_id)
     case 9: return Kern<T, 9>::occupancy();
     case 10: return Kern<T, 10>::occupancy();
     case 11: return Kern<T, 11>::occupancy();
+    case 12: return Kern<T, 12>::occupancy();
+    case 13: return Kern<T, 13>::occupancy();
     default: return 0;
     }
 }

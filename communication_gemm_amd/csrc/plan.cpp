@@ -33,6 +33,8 @@ const TileShape kF16Shapes[] = {
     {9, 256, 256, 512, false},
     {10, 256, 128, 512, false},
     {11, 128, 256, 512, false},
+    {12, 64, 64, 256, false},
+    {13, 64, 64, 256, false},
 };
 const TileShape kI8Shapes[] = {
     {8, 256, 256, 512, true},
@@ -46,6 +48,8 @@ const TileShape kI8Shapes[] = {
     {9, 256, 256, 512, false},
     {10, 256, 128, 512, false},
     {11, 128, 256, 512, false},
+    {12, 64, 64, 256, false},
+    {13, 64, 64, 256, false},
 };
 
 }  // namespace

@@ -78,7 +78,7 @@ def test_large_cases_sampled_rows(agg, orc, cid):
     check_f16(C[rows], Co, So, c.name)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
 @pytest.mark.parametrize("n,S,K,N,cr", [
     (3, 100, 296, 168, 7),     # ragged rows, k tail, n tail, ragged last chunk
     (2, 300, 520, 264, 0),
@@ -181,7 +181,7 @@ def test_i8_small_full(agg, orc):
     check_i8(acc, D, ao, Do, "int8 small")
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
 def test_i8_ragged(agg, orc, tile):
     shards, B, bias, scale = synth.make_i8(3 * 77, 16 * 37, 8 * 19, 3, 41000 + tile)
     acc, D = run_i8(agg, shards, B, bias, scale, 9, dict(tile=tile))
