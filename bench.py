@@ -53,6 +53,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOPS (2MKN/t) and % of MFMA peak for streamed AG-GEMM; overlap efficiency"
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA, published
 PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0
 # PTO-ISA AllGather+GEMM README, 8-card table, 8192x4096x4096 fp16 -> fp32 on
 # Ascend 910B1 (each rank computes all of C): other hardware, context only.
@@ -78,6 +79,7 @@ def parse():
     ap.add_argument("--no-modes", action="store_true", help="skip the overlap modes")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 workload")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 variant")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 variant")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip the pipelined chunk-size sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -345,6 +347,30 @@ def run_bf16(args, torch, agg, synth):
             "consumer_tflops": flops / (c * 1e-3) / 1e12}
 
 
+def run_fp8(args, torch, agg, synth):
+    """The fp8 (E4M3) variant on the same 8 x 1024-row workload, pipelined."""
+    case = synth.CASES[args.case]
+    shards, B = synth.make_fp8(case.M, case.K, case.N, case.n_shards, "normal",
+                               1000 * case.case_id)
+    ts = [torch.from_numpy(s).cuda() for s in shards]
+    tB = torch.from_numpy(B).cuda()
+    C = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(agg.workspace_bytes(case.n_shards, case.M, case.K, 1), dtype=torch.uint8,
+                     device="cuda")
+    agg.workspace_reset(ws)
+
+    def fn(ev):
+        agg.ag_gemm_fp8(ts, tB, C, 0, opts=agg.options(workspace=ws, consumer_events=ev))
+    t, c = timed(torch, fn, max(20, args.steps // 2), 20)
+    if agg.check():
+        raise SystemExit("fp8 run failed")
+    flops = 2.0 * case.M * case.K * case.N
+    return {"workload": case.name.replace("f16", "fp8", 1), "ms": t, "consumer_ms": c,
+            "tflops": flops / (t * 1e-3) / 1e12,
+            "consumer_tflops": flops / (c * 1e-3) / 1e12,
+            "frac_of_peak": flops / (c * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+
+
 def cpu_baseline(case, inputs, budget_s):
     """The oracle, as it stands, on a bounded sample of the workload's rows."""
     import oracle
@@ -430,6 +456,8 @@ def main():
     }
     if not args.no_bf16:
         line["bf16"] = run_bf16(args, torch, agg, synth)
+    if not args.no_fp8:
+        line["fp8"] = run_fp8(args, torch, agg, synth)
     if not args.no_int8:
         line["int8"] = run_i8(args, torch, agg, synth)
     if not args.no_cpu_baseline:

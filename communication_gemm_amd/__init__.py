@@ -4,8 +4,8 @@ C = concat(A_0, ..., A_{n-1}) x B computed while the shards arrive chunk by
 chunk: a producer kernel on a side stream moves the remote shards' chunks
 into a workspace and releases each on a per-source counter; a persistent
 MFMA GEMM starts on the local shard and consumes the remote chunks in send
-order.  fp16 -> fp32 (and its bf16 -> fp32 variant), and int8 -> int32 + bias
--> per-channel dequant -> fp16.
+order.  fp16 -> fp32 (and its bf16 -> fp32 and fp8 E4M3 -> fp32 variants), and
+int8 -> int32 + bias -> per-channel dequant -> fp16.
 
 The work runs in libaggemm.so (HIP, C ABI in include/aggemm.h); this package
 only binds it.
@@ -14,6 +14,6 @@ from ._native import (  # noqa: F401
     AGG_E_HIP, AGG_E_INVALID, AGG_E_NOMEM, AGG_E_TIMEOUT, AGG_E_UNSUPPORTED, AGG_OK,
     LIB_PATH, LINKS_PARALLEL, LINKS_SERIAL, MAX_SHARDS, MODE_COMPUTE_ONLY, MODE_COPY_ONLY,
     MODE_PIPELINED, MODE_SEQUENTIAL, AggError, Options, PlanInfo, ag_gemm_bf16, ag_gemm_f16,
-    ag_gemm_i8_dequant, check, options, pick_chunk_rows, plan, release, status_string,
+    ag_gemm_fp8, ag_gemm_i8_dequant, check, options, pick_chunk_rows, plan, release, status_string,
     workspace_bytes, workspace_reset,
 )

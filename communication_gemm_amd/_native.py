@@ -88,6 +88,13 @@ EXPORTS = {
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                        ctypes.POINTER(Options)]),
+    "ag_gemm_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]),
+    "ag_gemm_fp8_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.POINTER(Options)]),
     "ag_gemm_i8_dequant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -234,6 +241,35 @@ def ag_gemm_bf16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options |
     return C
 
 
+def _fp8_dtypes():
+    import torch
+    return (torch.uint8, torch.float8_e4m3fn)
+
+
+def ag_gemm_fp8(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None):
+    """C[M, N] (fp32) = concat(shards)[M, K] (fp8 E4M3) x B[K, N] (fp8 E4M3).
+
+    Shards and B are torch.float8_e4m3fn tensors, or uint8 tensors holding
+    E4M3 bit patterns (all of one dtype)."""
+    import torch
+    dt = B.dtype
+    if dt not in _fp8_dtypes() or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
+        raise ValueError("B must be a contiguous 2-D float8_e4m3fn (or uint8) CUDA tensor")
+    K, N = B.shape
+    table, S = _shard_ptrs(shards, dt, K)
+    M = S * len(shards)
+    _check_out(C, (M, N), torch.float32)
+    st = _stream_handle(stream)
+    if opts is None:
+        rc = lib.ag_gemm_fp8(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
+                             int(chunk_rows), st)
+    else:
+        rc = lib.ag_gemm_fp8_ex(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
+                                int(chunk_rows), st, ctypes.byref(opts))
+    _raise(rc, "ag_gemm_fp8")
+    return C
+
+
 def ag_gemm_i8_dequant(shards, B, bias, scale, C, chunk_rows: int = 0, stream=None,
                        opts: Options | None = None):
     """C[M, N] (fp16) = fp16(fp32(concat(shards) x B + bias) * scale)."""
@@ -289,7 +325,7 @@ def plan(kind: str, n_shards: int, M: int, K: int, N: int, chunk_rows: int = 0,
     """Host-only schedule query: (PlanInfo, tile_order or None, chunk_order or None)."""
     import numpy as np
     info = PlanInfo()
-    k = {"f16": 0, "i8": 1, "bf16": 2}[kind]
+    k = {"f16": 0, "i8": 1, "bf16": 2, "fp8": 3}[kind]
     o = ctypes.byref(opts) if opts is not None else None
     rc = lib.ag_gemm_plan(k, n_shards, M, K, N, chunk_rows, o, num_cus, ctypes.byref(info),
                           None, None)

@@ -36,7 +36,7 @@ struct Device {
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
-    int occ[3][16] = {{0}};   // by kind and tile id
+    int occ[4][16] = {{0}};   // by kind and tile id
 };
 
 std::mutex g_mu;
@@ -249,6 +249,7 @@ int run(const Call& c)
         if (e == hipSuccess)
             e = c.kind == kF16    ? launch_consumer_f16(ca, p.shape.id, cwgs, st)
                 : c.kind == kBF16 ? launch_consumer_bf16(ca, p.shape.id, cwgs, st)
+                : c.kind == kFP8  ? launch_consumer_fp8(ca, p.shape.id, cwgs, st)
                                   : launch_consumer_i8(ca, p.shape.id, cwgs, st);
         if (e == hipSuccess && cev[1]) e = hipEventRecord(cev[1], st);
         return e;
@@ -327,6 +328,21 @@ int ag_gemm_bf16_ex(const void* const* shards, int n_shards, const void* B, floa
                     const agg_options* opt)
 {
     Call c{kBF16, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
+           static_cast<hipStream_t>(stream), opt};
+    return run(c);
+}
+
+int ag_gemm_fp8(const void* const* shards, int n_shards, const void* B, float* C,
+                int64_t M, int64_t K, int64_t N, int chunk_rows, void* stream)
+{
+    return ag_gemm_fp8_ex(shards, n_shards, B, C, M, K, N, chunk_rows, stream, nullptr);
+}
+
+int ag_gemm_fp8_ex(const void* const* shards, int n_shards, const void* B, float* C,
+                   int64_t M, int64_t K, int64_t N, int chunk_rows, void* stream,
+                   const agg_options* opt)
+{
+    Call c{kFP8, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
            static_cast<hipStream_t>(stream), opt};
     return run(c);
 }

@@ -1,6 +1,6 @@
 // consumer.hip -- the persistent MFMA consumer GEMM (fp16 -> fp32, its
-// bf16 -> fp32 variant, and int8 -> int32 + bias -> per-channel dequant
-// -> fp16).
+// bf16 -> fp32 and fp8 (E4M3) -> fp32 variants, and int8 -> int32 + bias
+// -> per-channel dequant -> fp16).
 //
 // One workgroup per CU walks the tile list of the shared schedule: first
 // the local shard's tiles (no wait), then the remote tiles in the order
@@ -42,6 +42,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx16 __attribute__((ext_vector_type(16)));
 typedef int intx2 __attribute__((ext_vector_type(2)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef short short4_ __attribute__((ext_vector_type(4)));
 #define LDS_PTR __attribute__((address_space(3)))
 #define GLB_PTR __attribute__((address_space(1)))
@@ -54,23 +55,28 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // ---- element traits ---------------------------------------------------
 //
-// Both paths move 16-byte pieces: 8 fp16 or 16 int8 values along K.  One
-// MFMA step consumes 32 bytes of K per row (two pieces).  Inside every
+// Every path moves 16-byte pieces: 8 fp16 or 16 int8 / fp8 values along K.
+// An MFMA operand is kPair pieces per lane: lanes 0-31 and 32-63 take
+// pieces 2q and 2q + 1 of each 32-byte group q of K, for q = 0..kPair-1, in
+// A (row of the lane) and in B (column of the lane) alike, so the k that
+// one instruction sums over are the same in both operands.  Inside every
 // 16-lane group, lane i of a b16 transpose load receives element i % 4 of
 // the 8 bytes loaded by lane 4e + i/4 (e = 0..3), and of a b8 transpose
 // load byte i % 8 of lane 2e + i/8 (e = 0..7).
 
 struct F16 {
     static constexpr int kElt = 2;        // bytes per element
+    static constexpr int kPair = 1;       // 16-byte pieces per MFMA operand
+    static constexpr bool kDequant = false;
     typedef floatx16 Acc;
     typedef float Out;                    // element of C
 
     __device__ static Acc zero() { Acc z; for (int i = 0; i < 16; ++i) z[i] = 0.f; return z; }
 
-    __device__ static Acc mma(const uint4& a, const uint4& b, const Acc& c)
+    __device__ static Acc mma(const uint4 (&a)[1], const uint4 (&b)[1], const Acc& c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0, 0);
+            __builtin_bit_cast(half8, a[0]), __builtin_bit_cast(half8, b[0]), c, 0, 0, 0);
     }
 
     // B piece swizzle, LB bytes per B row in LDS.  The LDS has 64 banks of
@@ -119,24 +125,26 @@ struct F16 {
 // bfloat16: the fp16 engine (same 16-bit layout, swizzles and transpose
 // reads) with the bf16 MFMA.
 struct BF16 : F16 {
-    __device__ static Acc mma(const uint4& a, const uint4& b, const Acc& c)
+    __device__ static Acc mma(const uint4 (&a)[1], const uint4 (&b)[1], const Acc& c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+            __builtin_bit_cast(bf16x8, a[0]), __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
     }
 };
 
 struct I8 {
     static constexpr int kElt = 1;
+    static constexpr int kPair = 1;
+    static constexpr bool kDequant = true;   // + bias, x scale, -> fp16
     typedef intx16 Acc;
     typedef _Float16 Out;
 
     __device__ static Acc zero() { Acc z; for (int i = 0; i < 16; ++i) z[i] = 0; return z; }
 
-    __device__ static Acc mma(const uint4& a, const uint4& b, const Acc& c)
+    __device__ static Acc mma(const uint4 (&a)[1], const uint4 (&b)[1], const Acc& c)
     {
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(
-            __builtin_bit_cast(intx4, a), __builtin_bit_cast(intx4, b), c, 0, 0, 0);
+            __builtin_bit_cast(intx4, a[0]), __builtin_bit_cast(intx4, b[0]), c, 0, 0, 0);
     }
 
     // B piece swizzle: a b64 read's 32 lanes read 8 rows x 32 bytes, 16
@@ -172,6 +180,28 @@ struct I8 {
             v[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (LDS_PTR intx2*)(p + (32 * kk + 8 * h) * LB));
         return make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
+    }
+};
+
+// OCP FP8 E4M3: the int8 byte layout (swizzles, transpose reads), fp32
+// accumulators, and the gfx950 fp8 MFMA that sums 64 k per instruction,
+// 32 bytes per lane: two 16-byte pieces.  Format code 0 in both operands
+// selects E4M3; zero scale operands select the unscaled instruction.
+struct FP8 : I8 {
+    static constexpr int kPair = 2;
+    static constexpr bool kDequant = false;
+    typedef floatx16 Acc;
+    typedef float Out;
+
+    __device__ static Acc zero() { Acc z; for (int i = 0; i < 16; ++i) z[i] = 0.f; return z; }
+
+    __device__ static Acc mma(const uint4 (&a)[2], const uint4 (&b)[2], const Acc& c)
+    {
+        const intx8 av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                          (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+        const intx8 bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
+                          (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
     }
 };
 
@@ -215,7 +245,9 @@ struct Engine {
     static constexpr int kTM = BM / (32 * WM);      // 32x32 blocks per wave along M
     static constexpr int kTN = BN / (32 * WN);      // ... along N
     static constexpr int kPieces = SB / 16;         // 16-byte pieces per A row
-    static constexpr int kSteps = SB / 32;          // MFMA steps per slice
+    static constexpr int kP = T::kPair;             // pieces per MFMA operand
+    static constexpr int kHalfSteps = SB / 32;      // 32-byte groups of K per slice
+    static constexpr int kSteps = kHalfSteps / kP;  // MFMA steps per slice
     static constexpr int kBK = SB / T::kElt;        // k per slice
     static constexpr int kLB = BN * T::kElt;        // bytes per B row in LDS
     static constexpr int kABytes = BM * SB;         // A part of a stage
@@ -252,7 +284,7 @@ struct Engine {
     struct Lane {
         uint32_t a_ld[kAPer];   // A piece of load u: row * K + k, in bytes
         uint32_t b_ld[kBPer];   // B piece of load u: row * N + n, in bytes
-        uint32_t a_rd[kSteps];  // A operand of step s, block 0
+        uint32_t a_rd[kHalfSteps];  // A piece of 32-byte group g, block 0
         uint32_t b_rd[kTN];     // first transpose load of block j (step 0, half 0)
     };
 
@@ -276,10 +308,10 @@ struct Engine {
             L.b_ld[u] = (uint32_t)(r * N * T::kElt + p * 16);
         }
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
+        for (int g = 0; g < kHalfSteps; ++g) {
             const int r = wm + (lane & 31);
-            const int piece = 2 * st + (lane >> 5);
-            L.a_rd[st] = (uint32_t)(r * SB + ((piece ^ swz_a(r)) << 4));
+            const int piece = 2 * g + (lane >> 5);
+            L.a_rd[g] = (uint32_t)(r * SB + ((piece ^ swz_a(r)) << 4));
         }
 #pragma unroll
         for (int j = 0; j < kTN; ++j)
@@ -340,22 +372,26 @@ struct Engine {
         }
     }
 
-    // Operand fragments of one MFMA step (32 bytes of K): kTM A pieces and
-    // kTN B pieces per lane.
+    // Operand fragments of one MFMA step (32 kP bytes of K): kP pieces per
+    // lane for each of the kTM A blocks and kTN B blocks.
     struct Step {
-        uint4 a[kTM];
-        uint4 b[kTN];
+        uint4 a[kTM][kP];
+        uint4 b[kTN][kP];
     };
 
     __device__ __forceinline__ static void read_step(const char* st, const Lane& L, int kk,
                                                      Step& f)
     {
 #pragma unroll
-        for (int i = 0; i < kTM; ++i)
-            f.a[i] = *reinterpret_cast<const uint4*>(st + L.a_rd[kk] + i * 32 * SB);
+        for (int q = 0; q < kP; ++q) {
 #pragma unroll
-        for (int j = 0; j < kTN; ++j)
-            f.b[j] = T::template read_b<kLB>(st + L.b_rd[j], kk);
+            for (int i = 0; i < kTM; ++i)
+                f.a[i][q] = *reinterpret_cast<const uint4*>(st + L.a_rd[kP * kk + q] +
+                                                            i * 32 * SB);
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+                f.b[j][q] = T::template read_b<kLB>(st + L.b_rd[j], kP * kk + q);
+        }
     }
 
     __device__ __forceinline__ static void mma_step(const Step& f,
@@ -373,7 +409,7 @@ struct Engine {
     // in front of it (one wave per SIMD cannot hide a stall otherwise).
     __device__ __forceinline__ static void interleave_reads()
     {
-        constexpr int kR = kTM + 2 * kTN;   // LDS reads per step
+        constexpr int kR = kP * (kTM + 2 * kTN);   // LDS reads per step
         constexpr int kM = kTM * kTN;       // MFMAs per step
 #pragma unroll
         for (int i = 0; i < kM; ++i) {
@@ -511,7 +547,7 @@ __device__ __forceinline__ void store_tile_as(
         const uint32_t vacc = in ? lrow * row_acc + c * 4u : kOutOfRange;
         int32_t bias = 0;
         float scale = 0.f;
-        if constexpr (T::kElt == 1) {
+        if constexpr (T::kDequant) {
             if (in) {
                 bias = a.bias[col_lane + 32 * j];
                 scale = a.scale[col_lane + 32 * j];
@@ -522,7 +558,7 @@ __device__ __forceinline__ void store_tile_as(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const uint32_t roff = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
-                if constexpr (T::kElt == 2) {
+                if constexpr (!T::kDequant) {
                     // the element is copied out first: a bit cast applied
                     // to a vector element directly reads element 0
                     const float x = acc[i][j][r];
@@ -550,7 +586,7 @@ __device__ __forceinline__ void store_tile(
     const ConsumerArgs& a, int shard, int m, int n,
     typename T::Acc (&acc)[BM / (32 * WM)][BN / (32 * WN)])
 {
-    if constexpr (T::kElt == 1) {
+    if constexpr (T::kDequant) {
         if (a.acc_out) {
             store_tile_as<T, BM, BN, WM, WN, true>(a, shard, m, n, acc);
             return;
@@ -688,23 +724,58 @@ struct Kern {
     }
 };
 
+// Whether configuration ID is built for traits T.  A slice must hold an
+// even number of MFMA steps (the fp8 MFMA takes 64 bytes of K, so its
+// slices are 128 or 256 bytes), and the registers one wave needs -- its
+// accumulators, two steps' operand fragments and about 40 for addresses
+// and loop state -- times the waves per SIMD must leave 48 of the 512 for
+// a producer wave.  (The compiler's own count is checked by the tests;
+// this only keeps configurations that cannot fit from being built.)
+template <class T, int ID>
+constexpr bool supported()
+{
+    typedef Cfg<ID> C;
+    constexpr int tm = C::BM / (32 * C::WM), tn = C::BN / (32 * C::WN);
+    constexpr int regs = tm * tn * 16 + 2 * T::kPair * 4 * (tm + tn) + 40;
+    constexpr int per_simd = C::WM * C::WN / 4;
+    return C::SB % (64 * T::kPair) == 0 && per_simd * regs <= 512 - 48;
+}
+
+template <class T, int ID>
+hipError_t launch_id(const ConsumerArgs& a, int wgs, hipStream_t st)
+{
+    if constexpr (supported<T, ID>())
+        return Kern<T, ID>::launch(a, wgs, st);
+    else
+        return hipErrorInvalidValue;
+}
+
+template <class T, int ID>
+int occupancy_id()
+{
+    if constexpr (supported<T, ID>())
+        return Kern<T, ID>::occupancy();
+    else
+        return 0;
+}
+
 template <class T>
 hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
 {
     switch (tile_id) {
-    case 1: return Kern<T, 1>::launch(a, wgs, st);
-    case 2: return Kern<T, 2>::launch(a, wgs, st);
-    case 3: return Kern<T, 3>::launch(a, wgs, st);
-    case 4: return Kern<T, 4>::launch(a, wgs, st);
-    case 5: return Kern<T, 5>::launch(a, wgs, st);
-    case 6: return Kern<T, 6>::launch(a, wgs, st);
-    case 7: return Kern<T, 7>::launch(a, wgs, st);
-    case 8: return Kern<T, 8>::launch(a, wgs, st);
-    case 9: return Kern<T, 9>::launch(a, wgs, st);
-    case 10: return Kern<T, 10>::launch(a, wgs, st);
-    case 11: return Kern<T, 11>::launch(a, wgs, st);
-    case 12: return Kern<T, 12>::launch(a, wgs, st);
-    case 13: return Kern<T, 13>::launch(a, wgs, st);
+    case 1: return launch_id<T, 1>(a, wgs, st);
+    case 2: return launch_id<T, 2>(a, wgs, st);
+    case 3: return launch_id<T, 3>(a, wgs, st);
+    case 4: return launch_id<T, 4>(a, wgs, st);
+    case 5: return launch_id<T, 5>(a, wgs, st);
+    case 6: return launch_id<T, 6>(a, wgs, st);
+    case 7: return launch_id<T, 7>(a, wgs, st);
+    case 8: return launch_id<T, 8>(a, wgs, st);
+    case 9: return launch_id<T, 9>(a, wgs, st);
+    case 10: return launch_id<T, 10>(a, wgs, st);
+    case 11: return launch_id<T, 11>(a, wgs, st);
+    case 12: return launch_id<T, 12>(a, wgs, st);
+    case 13: return launch_id<T, 13>(a, wgs, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -713,19 +784,19 @@ template <class T>
 int occupancy_kind(int tile_id)
 {
     switch (tile_id) {
-    case 1: return Kern<T, 1>::occupancy();
-    case 2: return Kern<T, 2>::occupancy();
-    case 3: return Kern<T, 3>::occupancy();
-    case 4: return Kern<T, 4>::occupancy();
-    case 5: return Kern<T, 5>::occupancy();
-    case 6: return Kern<T, 6>::occupancy();
-    case 7: return Kern<T, 7>::occupancy();
-    case 8: return Kern<T, 8>::occupancy();
-    case 9: return Kern<T, 9>::occupancy();
-    case 10: return Kern<T, 10>::occupancy();
-    case 11: return Kern<T, 11>::occupancy();
-    case 12: return Kern<T, 12>::occupancy();
-    case 13: return Kern<T, 13>::occupancy();
+    case 1: return occupancy_id<T, 1>();
+    case 2: return occupancy_id<T, 2>();
+    case 3: return occupancy_id<T, 3>();
+    case 4: return occupancy_id<T, 4>();
+    case 5: return occupancy_id<T, 5>();
+    case 6: return occupancy_id<T, 6>();
+    case 7: return occupancy_id<T, 7>();
+    case 8: return occupancy_id<T, 8>();
+    case 9: return occupancy_id<T, 9>();
+    case 10: return occupancy_id<T, 10>();
+    case 11: return occupancy_id<T, 11>();
+    case 12: return occupancy_id<T, 12>();
+    case 13: return occupancy_id<T, 13>();
     default: return 0;
     }
 }
@@ -747,10 +818,16 @@ hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs, hipSt
     return launch_kind<I8>(a, tile_id, wgs, st);
 }
 
+hipError_t launch_consumer_fp8(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
+{
+    return launch_kind<FP8>(a, tile_id, wgs, st);
+}
+
 int consumer_occupancy(int kind, int tile_id)
 {
     return kind == 0 ? occupancy_kind<F16>(tile_id)
          : kind == 2 ? occupancy_kind<BF16>(tile_id)
+         : kind == 3 ? occupancy_kind<FP8>(tile_id)
                      : occupancy_kind<I8>(tile_id);
 }
 

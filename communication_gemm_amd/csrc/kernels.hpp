@@ -57,9 +57,12 @@ hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs,
                               hipStream_t st);
 hipError_t launch_consumer_bf16(const ConsumerArgs& a, int tile_id, int wgs,
                                 hipStream_t st);
+hipError_t launch_consumer_fp8(const ConsumerArgs& a, int tile_id, int wgs,
+                               hipStream_t st);
 hipError_t launch_header_reset(uint32_t* header, size_t bytes, hipStream_t st);
 
-// Workgroups of a consumer tile shape that fit on one CU at once.
+// Workgroups of a consumer tile shape that fit on one CU at once (kind:
+// 0 fp16, 1 int8, 2 bf16, 3 fp8).
 int consumer_occupancy(int kind, int tile_id);
 
 }  // namespace agg

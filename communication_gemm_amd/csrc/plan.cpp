@@ -51,6 +51,20 @@ const TileShape kI8Shapes[] = {
     {12, 64, 64, 256, false},
     {13, 64, 64, 256, false},
 };
+// fp8: the configurations whose slices hold whole 64-byte MFMA steps in
+// pairs (128- or 256-byte slices).  The 8-wave 256 x 256 tile is left out:
+// with 32-byte operands per lane, two steps' fragments and the 128
+// accumulators of a 128 x 64 wave block do not fit beside a producer wave.
+// The 4-wave 256 x 256 tile (one wave per SIMD) measured fastest.
+const TileShape kFP8Shapes[] = {
+    {6, 256, 256, 256, true},
+    {10, 256, 128, 512, true},
+    {11, 128, 256, 512, true},
+    {2, 128, 128, 256, true},
+    {3, 64, 64, 256, true},
+    {12, 64, 64, 256, false},
+    {13, 64, 64, 256, false},
+};
 
 }  // namespace
 
@@ -59,6 +73,10 @@ const TileShape* tile_shapes(Kind kind, int* count)
     if (kind == kF16 || kind == kBF16) {   // bf16 runs the fp16 engine
         *count = (int)(sizeof(kF16Shapes) / sizeof(kF16Shapes[0]));
         return kF16Shapes;
+    }
+    if (kind == kFP8) {
+        *count = (int)(sizeof(kFP8Shapes) / sizeof(kFP8Shapes[0]));
+        return kFP8Shapes;
     }
     *count = (int)(sizeof(kI8Shapes) / sizeof(kI8Shapes[0]));
     return kI8Shapes;
@@ -101,7 +119,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (M % n_shards) return AGG_E_INVALID;
     const int64_t S = M / n_shards;
     if (chunk_rows < 0 || (S > 0 && chunk_rows > S)) return AGG_E_INVALID;
-    const int kvec = (kind == kI8) ? 16 : 8;    // elements per 16-byte load
+    const int kvec = 16 / elt_bytes(kind);      // elements per 16-byte load
     if (K % kvec || N % 8) return AGG_E_UNSUPPORTED;
     if (opt->local_shard < 0 || opt->local_shard >= n_shards) return AGG_E_INVALID;
     if (opt->mode < AGG_MODE_PIPELINED || opt->mode > AGG_MODE_COPY_ONLY)
@@ -134,7 +152,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
     if (n_shards > 1 && s.cps > kFlagCap) return AGG_E_UNSUPPORTED;
     // the producer moves a chunk with 32-bit buffer offsets
-    if ((int64_t)s.cr * K * (kind == kI8 ? 1 : 2) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
+    if ((int64_t)s.cr * K * elt_bytes(kind) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
 
     // send order: a permutation of the remote shards
     for (int i = 0; i < kMaxShards; ++i) { s.order[i] = -1; s.slot[i] = -1; }
@@ -184,7 +202,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
     if (cw < 1) cw = 1;
     // pieces per chunk (a chunk is below 2 GiB, so at most 65536)
-    const int64_t chunk_bytes = (int64_t)s.cr * K * (kind == kI8 ? 1 : 2);
+    const int64_t chunk_bytes = (int64_t)s.cr * K * elt_bytes(kind);
     const int ppc = chunk_bytes > 0 ? (int)cdiv(chunk_bytes, kPieceBytes) : 1;
     const int64_t items = chunks * ppc;
     int pw = opt->producer_wgs ? opt->producer_wgs : num_cus;
@@ -195,7 +213,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     p.ppc = ppc;
     p.mode = opt->mode;
     p.link_gbps = opt->link_gbps;
-    p.elt = (kind == kI8) ? 1 : 2;
+    p.elt = elt_bytes(kind);
     p.M = M;
     p.ws_bytes = workspace_bytes(n_shards, M, K, p.elt);
     p.drop_chunk = opt->debug_drop_chunk;
@@ -247,7 +265,7 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
                  int chunk_rows, const agg_options* opt, int num_cus,
                  agg_plan_info* info, int32_t* tile_order, int32_t* chunk_order)
 {
-    if (kind != 0 && kind != 1 && kind != 2) return AGG_E_INVALID;
+    if (kind < 0 || kind > 3) return AGG_E_INVALID;
     agg::Plan p;
     int rc = agg::make_plan(static_cast<agg::Kind>(kind), n_shards, M, K,
                             N, chunk_rows, opt, num_cus, &p);

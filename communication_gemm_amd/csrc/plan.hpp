@@ -9,7 +9,10 @@
 
 namespace agg {
 
-enum Kind { kF16 = 0, kI8 = 1, kBF16 = 2 };
+enum Kind { kF16 = 0, kI8 = 1, kBF16 = 2, kFP8 = 3 };
+
+// Bytes per element of A and B.
+inline int elt_bytes(Kind k) { return (k == kI8 || k == kFP8) ? 1 : 2; }
 
 struct TileShape {
     int id;         // 1-based id accepted by agg_options.tile

@@ -153,6 +153,22 @@ int ag_gemm_bf16_ex(const void *const *shards, int n_shards, const void *B,
                     void *stream, const agg_options *opt);
 
 /*
+ * fp8 x fp8 -> fp32 streamed AllGather + GEMM: the fp16 operation above
+ * with OCP FP8 E4M3 shards and B (1 byte per element, the float8_e4m3fn
+ * format of the FP8 grouped-GEMM variant on the Ascend SHMEM blog page).
+ * Same layouts, alignment, size limits and errors as ag_gemm_f16, except
+ * that K must be a multiple of 16 (one 16-byte load holds 16 elements; N
+ * stays a multiple of 8); C fp32.  NaN inputs propagate as the matrix
+ * cores make them.
+ */
+int ag_gemm_fp8(const void *const *shards, int n_shards, const void *B,
+                float *C, int64_t M, int64_t K, int64_t N, int chunk_rows,
+                void *stream);
+int ag_gemm_fp8_ex(const void *const *shards, int n_shards, const void *B,
+                   float *C, int64_t M, int64_t K, int64_t N, int chunk_rows,
+                   void *stream, const agg_options *opt);
+
+/*
  * int8 x int8 -> int32, + bias, x per-channel scale -> fp16
  * (catccos AllGatherMatmulDequant design doc, sections 1.2 and 2.2):
  *   v = A x B + bias[n]        exact int32
@@ -225,7 +241,7 @@ typedef struct agg_plan_info {
 
 /*
  * The schedule one call would run, for inspection and tests.
- *   kind: 0 = fp16 path, 1 = int8 path, 2 = bf16 path; num_cus: CUs of
+ *   kind: 0 = fp16 path, 1 = int8 path, 2 = bf16 path, 3 = fp8 path; num_cus: CUs of
  *   the device to plan for (0 = 256).  tile_order (nullable, capacity total_tiles * 4 int32):
  *   per consumer position: shard, m-tile, n-tile, counter value waited for
  *   (0 for the local shard).  chunk_order (nullable, capacity total_chunks

@@ -146,3 +146,20 @@ def test_bf16_invariant_across_schedules(agg):
         outs.append(C)
     for C in outs[1:]:
         assert torch.equal(C, outs[0])
+
+
+def test_fp8_invariant_across_schedules(agg):
+    """The fp8 path: bitwise the same output whatever the chunking, local
+    shard, link pacing and mode."""
+    shards, Bn = synth.make_fp8(4 * 256, 512, 384, 4, "normal", 53000)
+    ts = [torch.from_numpy(s).cuda() for s in shards]
+    B = torch.from_numpy(Bn).cuda()
+    outs = []
+    for kw, cr in [(dict(), 0), (dict(local_shard=3, send_order=[2, 0, 1]), 5),
+                   (dict(link_model=1, link_gbps=40.0), 64), (dict(mode=2), 3)]:
+        C = torch.full((1024, 384), float("nan"), device="cuda")
+        agg.ag_gemm_fp8(ts, B, C, cr, opts=agg.options(**kw))
+        assert agg.check() == 0
+        outs.append(C)
+    for C in outs[1:]:
+        assert torch.equal(C, outs[0])

@@ -265,3 +265,56 @@ def test_bf16_large_sampled_rows(agg, orc):
     rows = sample_rows(n * S, n, agg.pick_chunk_rows(S))
     Co, So = orc.ag_gemm_bf16(shards, B, rows=rows)
     check_f16(C[rows], Co, So, "bf16 8x1024x4096x4096")
+
+
+# ---------------------------------------------------------------- fp8 path
+# Same bar as the fp16 path.  The fp8 matrix-core instruction does not sum
+# its 64 products in full fp32 precision; its error stays a small multiple
+# of 2^-24 sum|ab| per instruction, far inside the bound (the largest
+# ratio err / sum|ab| is printed).
+
+FP8_TILES = [2, 3, 6, 10, 11, 12, 13]
+
+
+def run_fp8(agg, shards, B, chunk_rows=0, opts=None, as_float8=False):
+    ts = [torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in shards]
+    tB = torch.from_numpy(np.ascontiguousarray(B)).cuda()
+    if as_float8:
+        ts = [t.view(torch.float8_e4m3fn) for t in ts]
+        tB = tB.view(torch.float8_e4m3fn)
+    M = sum(s.shape[0] for s in shards)
+    C = torch.full((M, B.shape[1]), float("nan"), dtype=torch.float32, device="cuda")
+    agg.ag_gemm_fp8(ts, tB, C, chunk_rows, opts=opts)
+    rc = agg.check()
+    assert rc == 0, agg.status_string(rc)
+    return C.cpu().numpy()
+
+
+def test_fp8_small_full(agg, orc):
+    shards, B = synth.make_fp8(256, 256, 128, 2, "normal", 36000)
+    C = run_fp8(agg, shards, B, 32, as_float8=True)
+    Co, So = orc.ag_gemm_fp8(shards, B)
+    print("fp8 small: max err/S", check_f16(C, Co, So, "fp8 small"))
+
+
+@pytest.mark.parametrize("tile", FP8_TILES)
+def test_fp8_ragged(agg, orc, tile):
+    shards, B = synth.make_fp8(3 * 100, 16 * 37, 8 * 21, 3, "uniform", 36100 + tile)
+    C = run_fp8(agg, shards, B, 7, agg.options(tile=tile))
+    Co, So = orc.ag_gemm_fp8(shards, B)
+    check_f16(C, Co, So, f"fp8 ragged tile {tile}")
+
+
+def test_fp8_rejects_unbuilt_tile(agg):
+    shards, B = synth.make_fp8(256, 256, 128, 2, "normal", 36050)
+    with pytest.raises(agg.AggError):
+        run_fp8(agg, shards, B, 0, agg.options(tile=8))
+
+
+def test_fp8_large_sampled_rows(agg, orc):
+    n, S, K, N = 8, 1024, 4096, 4096
+    shards, B = synth.make_fp8(n * S, K, N, n, "normal", 36200)
+    C = run_fp8(agg, shards, B)
+    rows = sample_rows(n * S, n, agg.pick_chunk_rows(S))
+    Co, So = orc.ag_gemm_fp8(shards, B, rows=rows)
+    print("fp8 8x1024x4096x4096: max err/S", check_f16(C[rows], Co, So, "fp8 large"))

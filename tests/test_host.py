@@ -172,6 +172,8 @@ def test_plan_rejects_bad_options(kw, status):
     ("f16", 2, 64, (1 << 21) + 8, 64, 0, agg.AGG_E_UNSUPPORTED),   # K limit
     ("f16", 2, 64, 64, (1 << 20) + 8, 0, agg.AGG_E_UNSUPPORTED),   # N limit
     ("i8", 2, 64, 64, (1 << 20) + 8, 0, agg.AGG_E_UNSUPPORTED),
+    ("fp8", 2, 64, 72, 64, 0, agg.AGG_E_UNSUPPORTED),     # K % 16
+    ("fp8", 2, 64, 64, 60, 0, agg.AGG_E_UNSUPPORTED),     # N % 8
 ])
 def test_plan_rejects_bad_sizes(kind, n, M, K, N, cr, status):
     with pytest.raises(agg.AggError) as e:
@@ -210,6 +212,9 @@ def test_entry_point_argument_errors():
     # int8: bias and scale are required
     assert lib.ag_gemm_i8_dequant(t, 2, FAKE, None, FAKE, FAKE, 64, 64, 64, 0, None) == agg.AGG_E_INVALID
     assert lib.ag_gemm_i8_dequant(t, 2, FAKE, FAKE, FAKE + 2, FAKE, 64, 64, 64, 0, None) == agg.AGG_E_UNSUPPORTED
+    # fp8: 16 elements per 16-byte load
+    assert lib.ag_gemm_fp8(t, 2, FAKE, FAKE, 64, 72, 64, 0, None) == agg.AGG_E_UNSUPPORTED
+    assert lib.ag_gemm_fp8(None, 2, FAKE, FAKE, 64, 64, 64, 0, None) == agg.AGG_E_INVALID
     assert lib.ag_gemm_workspace_reset(None, 1 << 20, None) == agg.AGG_E_INVALID
 
 
@@ -217,3 +222,17 @@ def test_empty_problems_are_no_ops():
     # M = 0 or N = 0: nothing to move or compute, nothing enqueued
     assert _f16([0, 0], 2, 0, 0, 0, 64, 64) == agg.AGG_OK
     assert _f16([FAKE, FAKE], 2, FAKE, 0, 64, 64, 0) == agg.AGG_OK
+
+
+def test_fp8_plans_only_tiles_built_for_it():
+    """The fp8 path runs the configurations whose slices hold pairs of
+    64-byte MFMA steps; the automatic choice stays among them."""
+    for tile in (1, 4, 5, 7, 8, 9):
+        with pytest.raises(agg.AggError) as e:
+            agg.plan("fp8", 8, 8192, 4096, 4096, 0, agg.options(tile=tile))
+        assert e.value.status == agg.AGG_E_INVALID
+    for tile in (2, 3, 6, 10, 11, 12, 13):
+        info, _, _ = agg.plan("fp8", 8, 8192, 4096, 4096, 0, agg.options(tile=tile))
+        assert info.tile_id == tile
+    info, _, _ = agg.plan("fp8", 8, 8192, 4096, 4096)
+    assert (info.tile_m, info.tile_n, info.tile_id) == (256, 256, 6)

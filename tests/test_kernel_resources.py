@@ -55,7 +55,8 @@ def shape_table():
         r"struct Cfg<(\d+)> \{ static constexpr int BM = (\d+), BN = (\d+), SB = (\d+), "
         r"NS = (\d+), WM = (\d+), WN = (\d+);", cons)}
     tables = {}
-    for kind, name in (("F16", "kF16Shapes"), ("BF16", "kF16Shapes"), ("I8", "kI8Shapes")):
+    for kind, name in (("F16", "kF16Shapes"), ("BF16", "kF16Shapes"), ("I8", "kI8Shapes"),
+                       ("FP8", "kFP8Shapes")):
         body = plan[plan.index(name):]
         body = body[:body.index("};")]
         for i, tm, tn, threads, _ in re.findall(
@@ -85,7 +86,7 @@ def test_every_consumer_leaves_room_for_the_producer(reports):
     prod_lds = pk.get("LDS Size [bytes/block]", 0)
     assert pk.get("ScratchSize [bytes/lane]", 0) == 0
     table = shape_table()
-    assert len(table) == 39
+    assert len(table) == 46
     for (kind, i), (bm, bn, sb, ns, wm, wn) in table.items():
         r = consumer_report(cons, kind, bm, bn, sb, ns, wm, wn)
         regs = align8(r["VGPRs"]) + align8(r["AGPRs"])
