@@ -32,7 +32,6 @@ struct Device {
     int num_cus = 0;
     double clock_hz = 0;       // rate of the device's constant clock
     hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
@@ -57,9 +56,6 @@ int device_state(Device** out)
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, id) != hipSuccess)
             return AGG_E_HIP;
         if (hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) != hipSuccess)
-            return AGG_E_HIP;
-        if (hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&d.join, hipEventDisableTiming) != hipSuccess)
             return AGG_E_HIP;
         d.num_cus = cus;
         d.clock_hz = (khz > 0 ? khz : 100000) * 1000.0;
@@ -257,14 +253,25 @@ int run(const Call& c)
 
     hipError_t e = hipSuccess;
     if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer) {
-        // the consumer goes first so that its persistent workgroups are all
-        // resident; the producer's small workgroups fit beside them
-        e = hipEventRecord(d->fork, c.st);
-        if (e == hipSuccess) e = consumer(c.st);
-        if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
+        // The consumer goes first so that its persistent workgroups are all
+        // resident; the producer's small workgroups fit beside them.  No
+        // event joins the two streams (a cross-stream dependency costs
+        // about 13 us on this stack, each way):
+        // - the producer waits on the device for the consumer's start word
+        //   instead of an event on the caller's stream;
+        // - the caller's stream does not wait for the producer: the
+        //   consumer waits for every chunk's release, and the producer
+        //   releases a chunk only after all of its reads of the shards and
+        //   all of its writes of the chunk, so once the consumer is done
+        //   the producer neither reads the caller's buffers nor writes
+        //   anything the caller or the next call can see.  Calls that
+        //   share a workspace stay ordered: the next producer is queued
+        //   behind this one on the side stream and waits for the next
+        //   consumer's start.
+        ca.start = header + kStartOffset / 4;
+        pa.start = header + kStartOffset / 4;
+        e = consumer(c.st);
         if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
-        if (e == hipSuccess) e = hipEventRecord(d->join, d->side);
-        if (e == hipSuccess) e = hipStreamWaitEvent(c.st, d->join, 0);
     } else {
         if (run_producer) e = launch_producer(pa, p.producer_wgs, c.st);
         if (e == hipSuccess && run_consumer) e = consumer(c.st);
@@ -389,8 +396,9 @@ int ag_gemm_check(void* stream)
     std::lock_guard<std::mutex> lock(g_mu);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return AGG_E_HIP;
-    // work on the side stream is joined into the caller's stream, but a
-    // copy-only call may have been the last thing on it
+    // a pipelined call's producer runs on the side stream, which the
+    // caller's stream does not wait for: finish it too before reading the
+    // error word (or resetting the header after a failure)
     auto it = g_dev.find(dev);
     int rc = AGG_OK;
     if (it != g_dev.end() && it->second.ready) {
@@ -422,8 +430,6 @@ void ag_gemm_release(void)
         (void)hipSetDevice(kv.first);
         (void)hipDeviceSynchronize();
         if (d.ws) (void)hipFree(d.ws);
-        if (d.fork) (void)hipEventDestroy(d.fork);
-        if (d.join) (void)hipEventDestroy(d.join);
         if (d.side) (void)hipStreamDestroy(d.side);
     }
     g_dev.clear();

@@ -606,6 +606,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     const Schedule& s = a.s;
     const int tid = threadIdx.x;
     for (int i = tid; i < kMaxShards; i += E::kThreads) seen_sh[i] = 0;
+    // tell the producer that the work ahead of the call on this stream is
+    // done (any workgroup may be the first to run)
+    if (a.start && tid == 0)
+        __hip_atomic_store(a.start, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.trace_start && blockIdx.x == 0 && tid == 0) a.trace_start[0] = ticks();
     __syncthreads();
 

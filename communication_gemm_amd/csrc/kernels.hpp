@@ -27,6 +27,8 @@ struct ProducerArgs {
     double ticks_per_byte;         // pacing; 0 = unpaced
     uint64_t limit;                // wait limit in clock ticks
     uint64_t* trace;               // optional timestamps (see agg_options.trace)
+    const uint32_t* start;         // pipelined mode: wait until it holds the epoch
+                                   // before reading a shard (nullptr: no wait)
 };
 
 // Persistent consumer GEMM.
@@ -48,6 +50,7 @@ struct ConsumerArgs {
     int32_t* acc_out;
     uint64_t* trace;               // optional timestamps, consumer part
     uint64_t* trace_start;         // word 0 of the timestamps (call start)
+    uint32_t* start;               // pipelined mode: set to the epoch on entry
 };
 
 hipError_t launch_producer(const ProducerArgs& a, int wgs, hipStream_t st);

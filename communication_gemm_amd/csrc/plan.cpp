@@ -13,8 +13,11 @@ namespace {
 // Ids 1, 6, 7, 8 and 9 are the same 256 x 256 tile with different K
 // pipelines and wave grids (see the Cfg table of the consumer); 8 (eight
 // waves, two per SIMD, 128-byte slices) measured fastest on both paths,
-// so it is the one picked automatically.
-// All use 4 waves of 64 lanes.  The big tiles keep the MFMA pipes fed at
+// so it is the one picked automatically.  Ids 3, 12 and 13 are the 64 x 64
+// tile; 13 (four 256-byte slices in the ring) keeps the most of a small
+// tile's K in flight and measured fastest whenever a 64 x 64 tile is the
+// choice, down to one tile per CU (small M).
+// Apart from 8, 9, 10 and 11 all use 4 waves of 64 lanes.  The big tiles keep the MFMA pipes fed at
 // large shapes; the smaller ones give enough tiles to fill 256 CUs and to
 // follow the chunks as they arrive at smaller shapes.  Every one of these
 // kernels, at its full occupancy, leaves registers, LDS and wave slots for
@@ -26,30 +29,30 @@ const TileShape kF16Shapes[] = {
     {4, 256, 128, 256, true},
     {5, 128, 256, 256, true},
     {2, 128, 128, 256, true},
-    {3, 64, 64, 256, true},
+    {13, 64, 64, 256, true},
     {1, 256, 256, 256, false},
+    {3, 64, 64, 256, false},
     {6, 256, 256, 256, false},
     {7, 256, 256, 256, false},
     {9, 256, 256, 512, false},
     {10, 256, 128, 512, false},
     {11, 128, 256, 512, false},
     {12, 64, 64, 256, false},
-    {13, 64, 64, 256, false},
 };
 const TileShape kI8Shapes[] = {
     {8, 256, 256, 512, true},
     {4, 256, 128, 256, true},
     {5, 128, 256, 256, true},
     {2, 128, 128, 256, true},
-    {3, 64, 64, 256, true},
+    {13, 64, 64, 256, true},
     {1, 256, 256, 256, false},
+    {3, 64, 64, 256, false},
     {6, 256, 256, 256, false},
     {7, 256, 256, 256, false},
     {9, 256, 256, 512, false},
     {10, 256, 128, 512, false},
     {11, 128, 256, 512, false},
     {12, 64, 64, 256, false},
-    {13, 64, 64, 256, false},
 };
 // fp8: the configurations whose slices hold whole 64-byte MFMA steps in
 // pairs (128- or 256-byte slices).  The 8-wave 256 x 256 tile is left out:
@@ -61,9 +64,9 @@ const TileShape kFP8Shapes[] = {
     {10, 256, 128, 512, true},
     {11, 128, 256, 512, true},
     {2, 128, 128, 256, true},
-    {3, 64, 64, 256, true},
+    {13, 64, 64, 256, true},
+    {3, 64, 64, 256, false},
     {12, 64, 64, 256, false},
-    {13, 64, 64, 256, false},
 };
 
 }  // namespace

@@ -138,6 +138,20 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     // instructions, each of which the consumer is waiting on, so they go
     // first when both are ready.
     __builtin_amdgcn_s_setprio(3);
+    // Pipelined mode: this kernel runs on a stream of its own with no
+    // dependency on the caller's stream, so it must not read a shard
+    // before the work queued ahead of the call has finished.  The consumer
+    // runs on the caller's stream, so its start proves that; each of its
+    // workgroups writes the call's epoch to the start word on entry.
+    if (a.start) {
+        if (threadIdx.x == 0)
+            stop_sh = !reached(poll_until(a.start, a.epoch, a.err, a.epoch, a.limit), a.epoch);
+        __syncthreads();
+        if (stop_sh) return;
+        // the shards were written before the consumer started; drop any
+        // stale copies of them from this CU's caches
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
     if (threadIdx.x == 0) {
         origin_sh = a.ticks_per_byte > 0.0 ? pacing_origin(a.clock, a.epoch) : 0;
         stop_sh = 0;

@@ -20,7 +20,8 @@ namespace agg {
 constexpr int kMaxShards = 64;
 
 // Workspace header: one 32-bit summary counter per source shard, each on
-// its own 128-byte line, then the error word, the pacing origin, the
+// its own 128-byte line, then the error word, the pacing origin, the start
+// word (the epoch of the last call whose consumer has started), the
 // chunk flag matrix (one 32-bit word per source and chunk: the epoch of the
 // call that released it) and the piece counters (one 64-bit word per
 // source and chunk: the call's epoch above the number of the chunk's
@@ -29,6 +30,7 @@ constexpr int kMaxShards = 64;
 constexpr int kCounterStride = 128;                       // bytes
 constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
 constexpr int kClockOffset = kErrorOffset + kCounterStride; // uint64
+constexpr int kStartOffset = kClockOffset + kCounterStride; // uint32
 constexpr int kFlagOffset = 16384;
 constexpr int kFlagCap = 1024;       // chunks per source the flag matrix holds
 constexpr int kPieceOffset = kFlagOffset + kMaxShards * kFlagCap * 4;

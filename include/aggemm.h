@@ -32,6 +32,17 @@
  * must be issued from one host thread at a time and are ordered on their
  * streams; two calls in flight on different streams of one device would
  * share the workspace and race.
+ *
+ * Streams (pipelined mode): the consumer GEMM runs on `stream`; the producer
+ * runs on a stream of the library's own, with no event between the two.
+ * The producer reads no shard before the consumer has started (the
+ * consumer's start, in `stream` order, proves that the work queued ahead of
+ * the call is done; the producer waits for it on the device, for at most
+ * the call's time limit).  `stream` does not wait for the producer: the
+ * consumer ends only after every chunk is released, which comes after all
+ * of the producer's reads of the shards and writes of the workspace.  After
+ * a failed call the producer may still be running when `stream` passes the
+ * call; ag_gemm_check() waits for it.
  */
 #ifndef AGGEMM_H
 #define AGGEMM_H
