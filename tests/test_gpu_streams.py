@@ -1,0 +1,56 @@
+"""Stream semantics of the pipelined mode: the producer runs on the
+library's own stream with no event on the caller's stream, so it must take
+its start from the consumer.  Work queued on the caller's stream before a
+call (here a long sleep, then writes of new shard contents) must be seen by
+the producer's copies."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def agg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import communication_gemm_amd as m
+    return m
+
+
+@pytest.mark.parametrize("kind", ["f16", "i8"])
+def test_producer_sees_writes_queued_before_the_call(agg, kind):
+    n, S, K, N = 4, 256, 512, 256
+    if kind == "f16":
+        shards, B = synth.make_f16(n * S, K, N, n, "normal", 60000)
+    else:
+        shards, B, bias, scale = synth.make_i8(n * S, K, N, n, 60000)
+        tb, tsc = dev(bias, torch), dev(scale, torch)
+    ts = [dev(s, torch) for s in shards]
+    tB = dev(B, torch)
+    new = [dev(s, torch) for s in shards]
+    out_dtype = torch.float32 if kind == "f16" else torch.float16
+
+    def call(C):
+        if kind == "f16":
+            agg.ag_gemm_f16(ts, tB, C, 16)
+        else:
+            agg.ag_gemm_i8_dequant(ts, tB, tb, tsc, C, 16)
+
+    ref = torch.empty((n * S, N), dtype=out_dtype, device="cuda")
+    call(ref)
+    assert agg.check() == 0
+    for t in ts:
+        t.zero_()
+    torch.cuda.synchronize()
+    # about 20 ms of stream work ahead of the call, then the real contents
+    torch.cuda._sleep(40_000_000)
+    for t, v in zip(ts, new):
+        t.copy_(v)
+    C = torch.full((n * S, N), 7, dtype=out_dtype, device="cuda")
+    call(C)
+    assert agg.check() == 0
+    assert torch.equal(C, ref)
