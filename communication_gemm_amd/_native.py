@@ -47,6 +47,7 @@ class Options(ctypes.Structure):
         ("timeout_ms", ctypes.c_double),
         ("debug_drop_chunk", ctypes.c_int),
         ("consumer_events", ctypes.c_void_p * 2),
+        ("workspace_stages", ctypes.c_int),
         ("trace", ctypes.c_void_p),
     ]
 
@@ -68,6 +69,8 @@ class PlanInfo(ctypes.Structure):
         ("producer_wgs", ctypes.c_int),
         ("tile_id", ctypes.c_int),
         ("trace_words", ctypes.c_int64),
+        ("workspace_stages", ctypes.c_int),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 

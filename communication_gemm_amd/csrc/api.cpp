@@ -32,6 +32,7 @@ struct Device {
     int num_cus = 0;
     double clock_hz = 0;       // rate of the device's constant clock
     hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr;  // orders a ring-mode producer after the consumer
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
@@ -56,6 +57,8 @@ int device_state(Device** out)
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, id) != hipSuccess)
             return AGG_E_HIP;
         if (hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) != hipSuccess)
+            return AGG_E_HIP;
+        if (hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess)
             return AGG_E_HIP;
         d.num_cus = cus;
         d.clock_hz = (khz > 0 ? khz : 100000) * 1000.0;
@@ -184,7 +187,7 @@ int run(const Call& c)
     uint32_t* header = reinterpret_cast<uint32_t*>(ws);
 
     const Schedule& s = p.sched;
-    const size_t slot = ((size_t)s.S * (size_t)s.K * p.elt + 255) & ~(size_t)255;
+    const size_t slot = p.slot_bytes;
     ConsumerArgs ca;
     memset(&ca, 0, sizeof ca);
     ProducerArgs pa;
@@ -270,7 +273,22 @@ int run(const Call& c)
         //   consumer's start.
         ca.start = header + kStartOffset / 4;
         pa.start = header + kStartOffset / 4;
-        e = consumer(c.st);
+        if (s.ring > 0) {
+            // With a workspace ring the producer also waits for consumer
+            // tiles, so consumer workgroups must not be kept off the CUs by
+            // producer workgroups dispatched ahead of them.  An event on
+            // the caller's stream, recorded before the consumer, holds the
+            // producer back until the work ahead of the call is done, by
+            // which time the consumer's grid has been dispatched.  (Should
+            // a wait still starve, it ends at the time limit as an error.)
+            ca.stages = reinterpret_cast<uint64_t*>(ws + kStageOffset);
+            pa.stages = ca.stages;
+            e = hipEventRecord(d->fork, c.st);
+            if (e == hipSuccess) e = consumer(c.st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
+        } else {
+            e = consumer(c.st);
+        }
         if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
     } else {
         if (run_producer) e = launch_producer(pa, p.producer_wgs, c.st);
@@ -430,6 +448,7 @@ void ag_gemm_release(void)
         (void)hipSetDevice(kv.first);
         (void)hipDeviceSynchronize();
         if (d.ws) (void)hipFree(d.ws);
+        if (d.fork) (void)hipEventDestroy(d.fork);
         if (d.side) (void)hipStreamDestroy(d.side);
     }
     g_dev.clear();

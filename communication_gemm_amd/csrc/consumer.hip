@@ -659,7 +659,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
 
         const int64_t row0 = (int64_t)t.m * BM;
         const int64_t rows = s.S - row0;
-        const typename E::Src src{a.a[t.shard] + row0 * s.K * T::kElt,
+        // remote rows sit in the workspace (a full slot or a ring stage)
+        const int64_t arow = t.shard == s.local ? row0 : slot_row(s, row0);
+        const typename E::Src src{a.a[t.shard] + arow * s.K * T::kElt,
                                   rows < BM ? rows : BM, a.B, s.K, s.N, (int64_t)t.n * BN};
 
         typename T::Acc acc[E::kTM][E::kTN];
@@ -669,6 +671,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
             for (int j = 0; j < E::kTN; ++j) acc[i][j] = T::zero();
 
         if (nk > 0) E::run(lds, nk, src, L, acc);
+        // every wave's loads of the tile have completed (the last slice
+        // waited for them before its barrier): the stage may be reused
+        if (a.stages && t.shard != s.local && tid == 0)
+            count_one(a.stages + t.shard * kMaxStages + t.m % s.ring, a.epoch);
         store_tile<T, BM, BN, WM, WN>(a, t.shard, t.m, t.n, acc);
         if (a.trace && tid == 0) a.trace[3 * p + 2] = ticks();
     }

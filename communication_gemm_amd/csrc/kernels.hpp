@@ -29,6 +29,8 @@ struct ProducerArgs {
     uint64_t* trace;               // optional timestamps (see agg_options.trace)
     const uint32_t* start;         // pipelined mode: wait until it holds the epoch
                                    // before reading a shard (nullptr: no wait)
+    const uint64_t* stages;        // workspace ring: tiles finished per source and
+                                   // stage, [shard][kMaxStages] (nullptr: no wait)
 };
 
 // Persistent consumer GEMM.
@@ -51,6 +53,8 @@ struct ConsumerArgs {
     uint64_t* trace;               // optional timestamps, consumer part
     uint64_t* trace_start;         // word 0 of the timestamps (call start)
     uint32_t* start;               // pipelined mode: set to the epoch on entry
+    uint64_t* stages;              // workspace ring: count each finished remote
+                                   // tile on its stage (nullptr: no count)
 };
 
 hipError_t launch_producer(const ProducerArgs& a, int wgs, hipStream_t st);

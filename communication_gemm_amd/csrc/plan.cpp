@@ -150,12 +150,11 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.S = S;
     s.K = K;
     s.N = N;
-    s.cr = chunk_rows ? chunk_rows : pick_chunk_rows(S);
-    if (s.cr < 1) s.cr = 1;
-    s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
-    if (n_shards > 1 && s.cps > kFlagCap) return AGG_E_UNSUPPORTED;
-    // the producer moves a chunk with 32-bit buffer offsets
-    if ((int64_t)s.cr * K * elt_bytes(kind) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
+    if (opt->workspace_stages < 0 || opt->workspace_stages > kMaxStages) return AGG_E_INVALID;
+    // a ring needs the consumer running beside the producer to free its
+    // stages (copy-only calls skip that wait, since nothing reads the rows)
+    if (opt->workspace_stages > 0 && opt->mode == AGG_MODE_SEQUENTIAL)
+        return AGG_E_UNSUPPORTED;
 
     // send order: a permutation of the remote shards
     for (int i = 0; i < kMaxShards; ++i) { s.order[i] = -1; s.slot[i] = -1; }
@@ -199,6 +198,26 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.mt = (int)cdiv(S, s.tm);
     s.nt = (int)cdiv(N, s.tn);
 
+    // chunks, and the workspace ring
+    s.cr = chunk_rows ? chunk_rows : pick_chunk_rows(S);
+    if (s.cr < 1) s.cr = 1;
+    s.ring = 0;
+    if (opt->workspace_stages > 0 && (int64_t)opt->workspace_stages * s.tm < S) {
+        // a chunk must lie inside one row panel of the ring
+        if (chunk_rows == 0) {
+            int d = s.cr < s.tm ? s.cr : s.tm;
+            while (s.tm % d) --d;
+            s.cr = d;
+        } else if (s.tm % s.cr) {
+            return AGG_E_UNSUPPORTED;
+        }
+        s.ring = opt->workspace_stages;
+    }
+    s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
+    if (n_shards > 1 && s.cps > kFlagCap) return AGG_E_UNSUPPORTED;
+    // the producer moves a chunk with 32-bit buffer offsets
+    if ((int64_t)s.cr * K * elt_bytes(kind) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
+
     int64_t tiles = total_tiles(s);
     int64_t chunks = total_chunks(s);
     int cw = opt->consumer_wgs ? opt->consumer_wgs : num_cus;
@@ -218,7 +237,8 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     p.link_gbps = opt->link_gbps;
     p.elt = elt_bytes(kind);
     p.M = M;
-    p.ws_bytes = workspace_bytes(n_shards, M, K, p.elt);
+    p.slot_bytes = slot_bytes(s.ring > 0 ? (int64_t)s.ring * s.tm : S, K, p.elt);
+    p.ws_bytes = (size_t)kHeaderBytes + (size_t)(n_shards - 1) * p.slot_bytes;
     p.drop_chunk = opt->debug_drop_chunk;
     *out = p;
     return AGG_OK;
@@ -288,6 +308,8 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
         info->producer_wgs = p.producer_wgs;
         info->tile_id = p.shape.id;
         info->trace_words = 1 + agg::total_chunks(s) + 3 * agg::total_tiles(s);
+        info->workspace_stages = s.ring;
+        info->workspace_bytes = (int64_t)p.ws_bytes;
     }
     if (tile_order) {
         int64_t T = agg::total_tiles(s);

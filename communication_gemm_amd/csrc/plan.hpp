@@ -36,6 +36,7 @@ struct Plan {
     int ppc;            // producer pieces per chunk
     int elt;            // bytes per A element
     int64_t M;
+    size_t slot_bytes;  // workspace bytes per remote shard (full slot or ring)
     size_t ws_bytes;    // workspace bytes this call needs
     int drop_chunk;
 };

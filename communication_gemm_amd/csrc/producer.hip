@@ -163,11 +163,25 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
         const int64_t q = it % a.ppc;                  // piece of its chunk
         const ChunkRef r = chunk_at(s, c);
         const int64_t row0 = (int64_t)r.j * s.cr;
+        // Workspace ring: the chunk's panel goes over the panel that used
+        // the stage before; wait until the consumer has finished every
+        // tile of that one (its reads of the stage are complete then).
+        if (a.stages) {
+            const int m = (int)(row0 / s.tm);
+            const int64_t before = stage_tiles_before(s, m);
+            if (before > 0) {
+                if (threadIdx.x == 0)
+                    stop_sh = !poll_count(a.stages + r.shard * kMaxStages + m % s.ring, a.epoch,
+                                          (uint32_t)before, a.err, a.limit);
+                __syncthreads();
+                if (stop_sh) break;
+            }
+        }
         const int64_t bytes = (chunk_row_end(s, r.j) - row0) * row_bytes;
         const int64_t begin = q * kPieceBytes;
         const int64_t end = begin + kPieceBytes < bytes ? begin + kPieceBytes : bytes;
         if (begin < end)
-            copy_bytes(a.dst[r.shard] + row0 * row_bytes + begin,
+            copy_bytes(a.dst[r.shard] + slot_row(s, row0) * row_bytes + begin,
                        a.src[r.shard] + row0 * row_bytes + begin, end - begin);
         // The copy's stores are device-scope stores, written through to
         // memory; a store is counted done only once it is performed there.

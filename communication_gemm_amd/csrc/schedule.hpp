@@ -23,10 +23,12 @@ constexpr int kMaxShards = 64;
 // its own 128-byte line, then the error word, the pacing origin, the start
 // word (the epoch of the last call whose consumer has started), the
 // chunk flag matrix (one 32-bit word per source and chunk: the epoch of the
-// call that released it) and the piece counters (one 64-bit word per
-// source and chunk: the call's epoch above the number of the chunk's
-// pieces copied so far).  The PTO-ISA README keeps the first two
-// structures: per-chunk flags and a per-source summary counter.
+// call that released it), the piece counters (one 64-bit word per source
+// and chunk: the call's epoch above the number of the chunk's pieces
+// copied so far) and, for a bounded workspace, the stage counters (one
+// 64-bit word per source and ring stage: the call's epoch above the number
+// of tiles finished on that stage).  The PTO-ISA README keeps the first
+// two structures: per-chunk flags and a per-source summary counter.
 constexpr int kCounterStride = 128;                       // bytes
 constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
 constexpr int kClockOffset = kErrorOffset + kCounterStride; // uint64
@@ -34,7 +36,9 @@ constexpr int kStartOffset = kClockOffset + kCounterStride; // uint32
 constexpr int kFlagOffset = 16384;
 constexpr int kFlagCap = 1024;       // chunks per source the flag matrix holds
 constexpr int kPieceOffset = kFlagOffset + kMaxShards * kFlagCap * 4;
-constexpr int kHeaderBytes = kPieceOffset + kMaxShards * kFlagCap * 8;
+constexpr int kMaxStages = 8;        // ring stages per source, at most
+constexpr int kStageOffset = kPieceOffset + kMaxShards * kFlagCap * 8;
+constexpr int kHeaderBytes = kStageOffset + kMaxShards * kMaxStages * 8;
 
 // The producer copies a chunk in pieces of up to this many bytes, dealt to
 // its workgroups in send order, so that a large chunk is shared by many
@@ -56,6 +60,9 @@ struct Schedule {
     int order[kMaxShards]; // order[0] = local, order[1..n-1] = send order
     int slot[kMaxShards];  // workspace slot of each shard (-1: local)
     int xf;                // XCD blocking: n-tile groups per round (0 = none)
+    int ring;              // workspace stages per remote source (0 = a full
+                           // slot of S rows); stage g holds the row panel
+                           // (m-tile) m with m % ring == g
 };
 
 constexpr int kXcds = 8;   // XCDs; workgroup b of a grid runs on XCD b % 8
@@ -209,6 +216,24 @@ AGG_HD int64_t wg_position(const Schedule& s, int64_t b, int64_t G)
     const int64_t panel = g * bp + slot / bn;
     const int64_t n = h * bn + slot % bn;
     return panel * s.nt + n;
+}
+
+// Workspace row of source row `row` in its shard's slot.  A full slot
+// keeps the shard's layout; a ring of `ring` panels of tm rows puts panel
+// m in stage m % ring (chunks never straddle panels in that case).
+AGG_HD int64_t slot_row(const Schedule& s, int64_t row)
+{
+    if (s.ring <= 0) return row;
+    return ((row / s.tm) % s.ring) * s.tm + row % s.tm;
+}
+
+// Tiles finished on a ring stage that the producer must see before it
+// writes panel m there: every tile of the panels that used the stage
+// before (m - ring, m - 2 ring, ...).  0 for the first `ring` panels.
+AGG_HD int64_t stage_tiles_before(const Schedule& s, int m)
+{
+    if (s.ring <= 0 || m < s.ring) return 0;
+    return (int64_t)(m / s.ring) * s.nt;
 }
 
 // Rows of chunk j: [j*cr, min((j+1)*cr, S)).

@@ -89,6 +89,51 @@ __device__ inline bool poll_flag(const uint32_t* flag, uint32_t epoch, uint32_t*
     return true;
 }
 
+// An epoch-tagged count: the call's epoch in the upper half, the count in
+// the lower; a word left by an earlier call counts as zero, so it needs no
+// reset between calls.
+__device__ inline uint32_t tagged_count(uint64_t w, uint32_t epoch)
+{
+    return (uint32_t)(w >> 32) == epoch ? (uint32_t)w : 0u;
+}
+
+// Add one to an epoch-tagged count (relaxed, device scope).
+__device__ inline void count_one(uint64_t* word, uint32_t epoch)
+{
+    uint64_t cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const uint64_t next = ((uint64_t)epoch << 32) | (tagged_count(cur, epoch) + 1u);
+        if (__hip_atomic_compare_exchange_strong(word, &cur, next, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return;
+    }
+}
+
+// Wait (relaxed) until an epoch-tagged count reaches `target`; false after
+// a time-out or a failure elsewhere in the call.
+__device__ inline bool poll_count(const uint64_t* word, uint32_t epoch, uint32_t target,
+                                  uint32_t* err, uint64_t limit)
+{
+    auto seen = [&]() {
+        return tagged_count(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                            epoch);
+    };
+    if (seen() >= target) return true;
+    const uint64_t t0 = ticks();
+    uint32_t spins = 0;
+    while (seen() < target) {
+        __builtin_amdgcn_s_sleep(2);
+        if ((++spins & 31u) == 0) {
+            if (reached(load_agent(err), epoch)) return false;
+            if (ticks() - t0 > limit) {
+                raise_error(err, epoch);
+                return false;
+            }
+        }
+    }
+    return true;
+}
+
 // Pacing origin shared by all producer workgroups of one call: the first
 // one to arrive stamps the clock, tagged with the call's epoch.
 __device__ inline uint64_t pacing_origin(uint64_t* slot, uint32_t epoch)

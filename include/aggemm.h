@@ -109,6 +109,21 @@ typedef struct agg_options {
     void *consumer_events[2]; /* optional hipEvent_t pair recorded right
                                  before and after the consumer kernel, on
                                  the stream it runs on                       */
+    int workspace_stages;   /* 0 (default): the workspace holds every remote
+                               shard whole (S rows each).  1..8: a ring of
+                               that many row panels (one consumer tile high)
+                               per remote shard; the producer writes panel m
+                               over panel m - stages only after the consumer
+                               has finished every tile of that panel
+                               (catccos page: a double-buffered workspace with
+                               per-slot flags; Triton-distributed tutorial:
+                               WORKSPACE_STAGES).  Needs chunks inside one
+                               panel: an explicit chunk_rows must divide the
+                               tile height (AGG_E_UNSUPPORTED otherwise); the
+                               automatic one is cut to a divisor of it.  Not
+                               with AGG_MODE_SEQUENTIAL (AGG_E_UNSUPPORTED);
+                               a copy-only call does not wait for stages.
+                               agg_plan_info.workspace_bytes gives the size. */
     uint64_t *trace;        /* optional DEVICE buffer of at least
                                agg_plan_info.trace_words uint64, 8-byte
                                aligned, receiving 100 MHz device timestamps:
@@ -208,8 +223,10 @@ int ag_gemm_i8_dequant_ex(const int8_t *const *shards, int n_shards,
  */
 int ag_gemm_pick_chunk_rows(int64_t shard_rows);
 
-/* Bytes of workspace one call needs: a counter header plus one slot of
- * S x K elements for every remote shard. 0 on invalid sizes. */
+/* Bytes of workspace one call needs with full slots (workspace_stages 0):
+ * a counter header plus one slot of S x K elements for every remote shard.
+ * 0 on invalid sizes.  A call with a workspace ring needs less, as
+ * ag_gemm_plan reports in agg_plan_info.workspace_bytes. */
 size_t ag_gemm_workspace_bytes(int n_shards, int64_t M, int64_t K,
                                int elt_bytes);
 
@@ -248,6 +265,9 @@ typedef struct agg_plan_info {
     int producer_wgs;       /* producer grid */
     int tile_id;            /* consumer tile configuration (agg_options.tile) */
     int64_t trace_words;    /* 1 + total_chunks + 3 * total_tiles          */
+    int workspace_stages;   /* ring stages per remote shard (0: full slots) */
+    int64_t workspace_bytes; /* workspace this call needs (a caller-owned
+                                workspace must be at least this large)     */
 } agg_plan_info;
 
 /*

@@ -236,3 +236,45 @@ def test_fp8_plans_only_tiles_built_for_it():
         assert info.tile_id == tile
     info, _, _ = agg.plan("fp8", 8, 8192, 4096, 4096)
     assert (info.tile_m, info.tile_n, info.tile_id) == (256, 256, 6)
+
+
+def test_workspace_ring_plan():
+    """A ring of W row panels per remote shard: the workspace shrinks to
+    W x tile-height rows per remote shard; W panels covering the shard
+    fall back to full slots."""
+    header = agg.workspace_bytes(1, 100, 64, 2)
+    full, _, _ = agg.plan("f16", 8, 8192, 4096, 4096)
+    assert full.workspace_stages == 0
+    assert full.workspace_bytes == agg.workspace_bytes(8, 8192, 4096, 2)
+    for w in (1, 2, 3):
+        info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(workspace_stages=w))
+        assert info.workspace_stages == w
+        assert info.workspace_bytes == header + 7 * w * info.tile_m * 4096 * 2
+    info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(workspace_stages=4))
+    assert info.workspace_stages == 0 and info.workspace_bytes == full.workspace_bytes
+    c5, _, _ = agg.plan("i8", 2, 16384, 27392, 4096, 0, agg.options(workspace_stages=2))
+    assert c5.workspace_bytes == header + 2 * 256 * 27392
+
+
+def test_workspace_ring_chunks_stay_inside_panels():
+    # automatic chunk: the largest divisor of the tile height not above S/64
+    info, _, _ = agg.plan("f16", 4, 4 * 1000, 256, 200, 0,
+                          agg.options(workspace_stages=2, tile=13))
+    assert info.tile_m == 64 and info.chunk_rows == 8       # S/64 = 15 -> 8
+    ok, _, _ = agg.plan("f16", 4, 4 * 1000, 256, 200, 16, agg.options(workspace_stages=2, tile=13))
+    assert ok.chunk_rows == 16
+    for cr in (24, 128):                                    # 64 % cr != 0
+        with pytest.raises(agg.AggError) as e:
+            agg.plan("f16", 4, 4 * 1000, 256, 200, cr, agg.options(workspace_stages=2, tile=13))
+        assert e.value.status == agg.AGG_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(workspace_stages=9), agg.AGG_E_INVALID),
+    (dict(workspace_stages=-1), agg.AGG_E_INVALID),
+    (dict(workspace_stages=2, mode=agg.MODE_SEQUENTIAL), agg.AGG_E_UNSUPPORTED),
+])
+def test_workspace_ring_rejects(kw, status):
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(**kw))
+    assert e.value.status == status
