@@ -36,7 +36,7 @@ struct Device {
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
-    int occ[4][16] = {{0}};   // by kind and tile id
+    int occ[4][32] = {{0}};   // by kind and tile id
 };
 
 std::mutex g_mu;
@@ -72,7 +72,7 @@ int device_state(Device** out)
 
 int occupancy(Device& d, int kind, int tile)
 {
-    int& o = d.occ[kind][tile & 15];
+    int& o = d.occ[kind][tile & 31];
     if (!o) o = consumer_occupancy(kind, tile);
     return o;
 }
