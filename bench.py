@@ -251,6 +251,22 @@ def run_f16(args, torch, agg, synth):
         if agg.check():
             raise SystemExit("chunk sweep failed")
         res["chunk_sweep_ms"] = sweep
+    if modes and not args.no_chunk_sweep:
+        # the comparison scheme: a barrier per iteration of pvalue row panels
+        # over every shard (no local-first, no per-source counters), with
+        # full workspace slots or double-buffered panels
+        barrier = {}
+        for name, kw in (("pvalue1", dict(pvalue=1)), ("pvalue2", dict(pvalue=2)),
+                         ("pvalue1_stages2", dict(pvalue=1, workspace_stages=2))):
+            def fn(ev, kw=kw):
+                agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(
+                    workspace=ws, link_gbps=gbps, tile=args.tile,
+                    scheme=agg.SCHEME_BARRIER, **kw))
+            t, _ = timed(torch, fn, max(20, args.steps // 2), 10, with_consumer=False)
+            barrier[name] = round(t, 5)
+        if agg.check():
+            raise SystemExit("barrier-scheme runs failed")
+        res["barrier_scheme_ms"] = barrier
     info, _, _ = agg.plan("f16", case.n_shards, case.M, case.K, case.N, cr,
                           agg.options(tile=args.tile))
     if args.mode == "pipelined":

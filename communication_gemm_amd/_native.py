@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libaggemm.so")
 
 AGG_OK, AGG_E_INVALID, AGG_E_UNSUPPORTED, AGG_E_NOMEM, AGG_E_HIP, AGG_E_TIMEOUT = range(6)
 MODE_PIPELINED, MODE_COMPUTE_ONLY, MODE_SEQUENTIAL, MODE_COPY_ONLY = range(4)
+SCHEME_COUNTERS, SCHEME_BARRIER = range(2)
 LINKS_PARALLEL, LINKS_SERIAL = range(2)
 MAX_SHARDS = 64
 
@@ -48,6 +49,8 @@ class Options(ctypes.Structure):
         ("debug_drop_chunk", ctypes.c_int),
         ("consumer_events", ctypes.c_void_p * 2),
         ("workspace_stages", ctypes.c_int),
+        ("scheme", ctypes.c_int),
+        ("pvalue", ctypes.c_int),
         ("trace", ctypes.c_void_p),
     ]
 

@@ -595,6 +595,36 @@ __device__ __forceinline__ void store_tile(
     store_tile_as<T, BM, BN, WM, WN, false>(a, shard, m, n, acc);
 }
 
+// Wave 0 of a workgroup: wait until chunks [0, need) of source `shard` are
+// released, and acquire them.  What the workgroup has already seen of the
+// source is kept in seen[shard], so a satisfied wait touches no memory.
+// Returns 0 after a time-out or a failure elsewhere in the call.
+__device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int need,
+                                           uint32_t* seen, int tid)
+{
+    const uint32_t have = seen[shard];
+    if (have >= (uint32_t)need) return 1;
+    const uint32_t base = a.base[shard];
+    const uint32_t target = base + (uint32_t)need;
+    uint32_t v = target;
+    if (tid == 0)
+        v = poll_until(a.counters + shard * (kCounterStride / 4), target, a.err, a.epoch,
+                       a.limit);
+    v = __builtin_amdgcn_readfirstlane(v);
+    if (!reached(v, target)) return 0;
+    // the chunks the counter vouches for carry their copier's flag;
+    // reading them, then acquiring, pairs with each copier's release
+    const uint32_t upto = v - base;
+    const uint32_t* fl = a.flags + shard * kFlagCap;
+    bool mine = true;
+    for (uint32_t c = have + tid; c < upto; c += 64)
+        mine = mine && poll_flag(fl + c, a.epoch, a.err, a.limit);
+    const int ok = __builtin_amdgcn_ballot_w64(!mine) == 0;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (tid == 0 && ok) seen[shard] = upto;
+    return ok;
+}
+
 template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs a)
 {
@@ -624,31 +654,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
         if (t.need > 0 && !a.no_wait) {
             // wave 0 waits; the other waves hold at the barrier
             if (tid < 64) {
-                const uint32_t have = seen_sh[t.shard];
                 int ok = 1;
-                if (have < (uint32_t)t.need) {
-                    const uint32_t base = a.base[t.shard];
-                    const uint32_t target = base + (uint32_t)t.need;
-                    uint32_t v = target;
-                    if (tid == 0)
-                        v = poll_until(a.counters + t.shard * (kCounterStride / 4), target,
-                                       a.err, a.epoch, a.limit);
-                    v = __builtin_amdgcn_readfirstlane(v);
-                    if (!reached(v, target)) {
-                        ok = 0;
-                    } else {
-                        // the chunks the counter vouches for carry their
-                        // copier's flag; reading them, then acquiring,
-                        // pairs with each copier's release
-                        const uint32_t upto = v - base;
-                        const uint32_t* fl = a.flags + t.shard * kFlagCap;
-                        bool mine = true;
-                        for (uint32_t c = have + tid; c < upto; c += 64)
-                            mine = mine && poll_flag(fl + c, a.epoch, a.err, a.limit);
-                        ok = __builtin_amdgcn_ballot_w64(!mine) == 0;
-                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                        if (tid == 0 && ok) seen_sh[t.shard] = upto;
-                    }
+                if (s.pv > 0) {
+                    // barrier scheme: the iteration's rows of every source
+                    for (int q = 1; q < s.n_shards && ok; ++q)
+                        ok = wait_source(a, s.order[q], t.need, seen_sh, tid);
+                } else {
+                    ok = wait_source(a, t.shard, t.need, seen_sh, tid);
                 }
                 if (tid == 0) ok_sh = ok;
             }

@@ -151,6 +151,9 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.K = K;
     s.N = N;
     if (opt->workspace_stages < 0 || opt->workspace_stages > kMaxStages) return AGG_E_INVALID;
+    if (opt->scheme != AGG_SCHEME_COUNTERS && opt->scheme != AGG_SCHEME_BARRIER)
+        return AGG_E_INVALID;
+    if (opt->pvalue < 0) return AGG_E_INVALID;
     // a ring needs the consumer running beside the producer to free its
     // stages (copy-only calls skip that wait, since nothing reads the rows)
     if (opt->workspace_stages > 0 && opt->mode == AGG_MODE_SEQUENTIAL)
@@ -215,6 +218,12 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     }
     s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
     if (n_shards > 1 && s.cps > kFlagCap) return AGG_E_UNSUPPORTED;
+    s.pv = opt->scheme == AGG_SCHEME_BARRIER ? (opt->pvalue > 0 ? opt->pvalue : 1) : 0;
+    if (s.pv > s.mt) s.pv = s.mt > 0 ? s.mt : 1;
+    // a tile of iteration i waits for every panel of the iteration, so a
+    // ring must hold at least one iteration per source, or the producer
+    // would wait for tiles that wait for it
+    if (s.pv > 0 && s.ring > 0 && s.ring < s.pv) return AGG_E_UNSUPPORTED;
     // the producer moves a chunk with 32-bit buffer offsets
     if ((int64_t)s.cr * K * elt_bytes(kind) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
 

@@ -63,6 +63,10 @@ struct Schedule {
     int ring;              // workspace stages per remote source (0 = a full
                            // slot of S rows); stage g holds the row panel
                            // (m-tile) m with m % ring == g
+    int pv;                // 0: per-source counters, local shard first.
+                           // >= 1: the barrier scheme, iterations of pv
+                           // m-tiles over every shard, each tile waiting
+                           // for the whole iteration of every source
 };
 
 constexpr int kXcds = 8;   // XCDs; workgroup b of a grid runs on XCD b % 8
@@ -99,9 +103,30 @@ struct TileRef {
 // arrival order: with parallel links every source delivers its rows at the
 // same time, so tiles go m-tile by m-tile across sources; with one serial
 // link sources arrive one after the other.
+//
+// The barrier scheme (the Triton-distributed tutorial's comparison point:
+// each iteration gathers pvalue row blocks of every rank, then a
+// barrier_all, then every core computes the gathered block): iteration i
+// holds m-tiles [i pv, (i + 1) pv) of every shard, in shard order, and each
+// of its tiles, the local shard's included, waits until every remote source
+// has delivered the iteration's last row.
 AGG_HD TileRef tile_at(const Schedule& s, int64_t p)
 {
     TileRef t;
+    if (s.pv > 0) {
+        const int64_t full = (int64_t)s.n_shards * s.pv * s.nt;   // tiles per iteration
+        const int64_t i = p / full;
+        const int64_t q = p - i * full;
+        const int64_t m0 = i * s.pv;
+        const int64_t cm = (s.mt - m0) < s.pv ? (s.mt - m0) : s.pv;   // m-tiles in it
+        const int64_t per_shard = cm * s.nt;
+        t.shard = (int)(q / per_shard);
+        const int64_t r = q % per_shard;
+        t.m = (int)(m0 + r / s.nt);
+        t.n = (int)(r % s.nt);
+        t.need = s.n_shards > 1 ? need_chunks(s, (int)(m0 + cm - 1)) : 0;
+        return t;
+    }
     int64_t local_tiles = (int64_t)s.mt * s.nt;
     if (p < local_tiles) {
         t.shard = s.local;

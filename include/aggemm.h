@@ -76,6 +76,20 @@ enum agg_mode {
     AGG_MODE_COPY_ONLY = 3     /* producer only; C is not written            */
 };
 
+/* How the consumer learns that rows are there. */
+enum agg_scheme {
+    AGG_SCHEME_COUNTERS = 0, /* per-source summary counters; the local shard
+                                first, then remote tiles as their rows
+                                arrive (PTO-ISA README)                   */
+    AGG_SCHEME_BARRIER = 1   /* comparison scheme after the Triton-distributed
+                                AllGather GEMM tutorial: iterations of
+                                `pvalue` row panels of every shard; each
+                                tile of an iteration, the local shard's
+                                included, waits until every source has
+                                delivered the iteration (a barrier in place
+                                of per-source counters)                  */
+};
+
 /* How the emulated links are paced when link_gbps > 0. */
 enum agg_link_model {
     AGG_LINKS_PARALLEL = 0,  /* one link per source, all in parallel (full
@@ -124,6 +138,13 @@ typedef struct agg_options {
                                with AGG_MODE_SEQUENTIAL (AGG_E_UNSUPPORTED);
                                a copy-only call does not wait for stages.
                                agg_plan_info.workspace_bytes gives the size. */
+    int scheme;             /* enum agg_scheme (default COUNTERS)             */
+    int pvalue;             /* barrier scheme: row panels (consumer tiles
+                               high) per iteration; 0 = 1.  With a workspace
+                               ring, workspace_stages must be at least this
+                               (AGG_E_UNSUPPORTED otherwise): a stage is
+                               reused only after the tiles of its panel,
+                               which wait for their whole iteration.         */
     uint64_t *trace;        /* optional DEVICE buffer of at least
                                agg_plan_info.trace_words uint64, 8-byte
                                aligned, receiving 100 MHz device timestamps:

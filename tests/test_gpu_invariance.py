@@ -163,3 +163,21 @@ def test_fp8_invariant_across_schedules(agg):
         outs.append(C)
     for C in outs[1:]:
         assert torch.equal(C, outs[0])
+
+
+@pytest.mark.parametrize("kw", [dict(scheme=1), dict(scheme=1, pvalue=2),
+                                dict(scheme=1, pvalue=2, workspace_stages=2),
+                                dict(scheme=1, link_gbps=150.0)])
+def test_barrier_scheme_gives_the_same_bits(agg, kw):
+    """The barrier scheme changes only when tiles wait and in what order
+    they run, so its output is bitwise that of the counter scheme."""
+    shards, Bn = synth.make_f16(4 * 1024, 1024, 512, 4, "normal", 54000)
+    ts = [dev(s, torch) for s in shards]
+    B = dev(Bn, torch)
+    ref = torch.full((4096, 512), float("nan"), device="cuda")
+    agg.ag_gemm_f16(ts, B, ref, 0)
+    assert agg.check() == 0
+    C = torch.full((4096, 512), float("nan"), device="cuda")
+    agg.ag_gemm_f16(ts, B, C, 0, opts=agg.options(**kw))
+    assert agg.check() == 0
+    assert torch.equal(C, ref)

@@ -91,6 +91,16 @@ def test_ragged_shapes(agg, orc, tile, n, S, K, N, cr):
     check_f16(C, Co, So, f"tile {tile} n={n} S={S} K={K} N={N}")
 
 
+@pytest.mark.parametrize("pv,stages", [(1, 0), (2, 0), (3, 3)])
+def test_barrier_scheme_ragged(agg, orc, pv, stages):
+    shards, B = synth.make_f16(3 * 300, 296, 168, 3, "normal", 37000 + pv)
+    # 8-row chunks: a ring needs chunks inside the 64-row panels
+    C = run_f16(agg, shards, B, 8 if stages else 7,
+                agg.options(scheme=agg.SCHEME_BARRIER, pvalue=pv, workspace_stages=stages, tile=3))
+    Co, So = orc.ag_gemm_f16(shards, B)
+    check_f16(C, Co, So, f"barrier pvalue {pv} stages {stages}")
+
+
 @pytest.mark.parametrize("kind,tile", [("f16", 6), ("f16", 3), ("f16", 8), ("i8", 6), ("i8", 2), ("i8", 9)])
 def test_no_store_outside_c(agg, kind, tile):
     """Rows past the last shard's end and columns past N are dropped by

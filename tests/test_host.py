@@ -278,3 +278,41 @@ def test_workspace_ring_rejects(kw, status):
     with pytest.raises(agg.AggError) as e:
         agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(**kw))
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("n,M,pv,cr", [(4, 4096, 1, 0), (4, 4096, 3, 0), (3, 300, 2, 7),
+                                       (8, 8192, 2, 0), (2, 256, 1, 32)])
+def test_schedule_barrier_scheme(n, M, pv, cr):
+    """Iterations of pv m-tiles over every shard in shard order; every tile
+    of an iteration, the local one's too, waits for the chunk holding the
+    iteration's last row (on every source)."""
+    K, N = 256, 512
+    info, tiles, chunks = agg.plan("f16", n, M, K, N, cr, agg.options(
+        scheme=agg.SCHEME_BARRIER, pvalue=pv, tile=2), orders=True)
+    S = M // n
+    mt, nt = info.m_tiles_per_shard, info.n_tiles
+    assert len({tuple(t[:3]) for t in tiles}) == len(tiles) == n * mt * nt
+    p = 0
+    for i in range(-(-mt // pv)):
+        ms = list(range(i * pv, min((i + 1) * pv, mt)))
+        last_row = min((ms[-1] + 1) * info.tile_m, S)
+        need = -(-last_row // info.chunk_rows)
+        for sh in range(n):
+            for m in ms:
+                for nn in range(nt):
+                    assert tuple(tiles[p]) == (sh, m, nn, need)
+                    p += 1
+    assert p == len(tiles)
+
+
+def test_barrier_scheme_ring_must_hold_an_iteration():
+    kw = dict(scheme=agg.SCHEME_BARRIER, pvalue=2)
+    info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(workspace_stages=2, **kw))
+    assert info.workspace_stages == 2
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(workspace_stages=1, **kw))
+    assert e.value.status == agg.AGG_E_UNSUPPORTED
+    for bad in (dict(scheme=2), dict(scheme=agg.SCHEME_BARRIER, pvalue=-1)):
+        with pytest.raises(agg.AggError) as e:
+            agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(**bad))
+        assert e.value.status == agg.AGG_E_INVALID
