@@ -224,6 +224,10 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     // ring must hold at least one iteration per source, or the producer
     // would wait for tiles that wait for it
     if (s.pv > 0 && s.ring > 0 && s.ring < s.pv) return AGG_E_UNSUPPORTED;
+    // nor with one serial link: sources arrive one after the other, so the
+    // producer would wait on a stage of the first source for tiles that
+    // wait for the next source's rows
+    if (s.pv > 0 && s.ring > 0 && s.link_model == AGG_LINKS_SERIAL) return AGG_E_UNSUPPORTED;
     // the producer moves a chunk with 32-bit buffer offsets
     if ((int64_t)s.cr * K * elt_bytes(kind) >= (1LL << 31)) return AGG_E_UNSUPPORTED;
 

@@ -144,7 +144,10 @@ typedef struct agg_options {
                                ring, workspace_stages must be at least this
                                (AGG_E_UNSUPPORTED otherwise): a stage is
                                reused only after the tiles of its panel,
-                               which wait for their whole iteration.         */
+                               which wait for their whole iteration; and a
+                               ring is refused with AGG_LINKS_SERIAL, whose
+                               source-by-source order would have the
+                               producer wait on tiles that wait for it.     */
     uint64_t *trace;        /* optional DEVICE buffer of at least
                                agg_plan_info.trace_words uint64, 8-byte
                                aligned, receiving 100 MHz device timestamps:

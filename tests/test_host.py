@@ -312,6 +312,10 @@ def test_barrier_scheme_ring_must_hold_an_iteration():
     with pytest.raises(agg.AggError) as e:
         agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(workspace_stages=1, **kw))
     assert e.value.status == agg.AGG_E_UNSUPPORTED
+    with pytest.raises(agg.AggError) as e:       # found by the liveness simulation
+        agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(workspace_stages=2,
+                                                            link_model=agg.LINKS_SERIAL, **kw))
+    assert e.value.status == agg.AGG_E_UNSUPPORTED
     for bad in (dict(scheme=2), dict(scheme=agg.SCHEME_BARRIER, pvalue=-1)):
         with pytest.raises(agg.AggError) as e:
             agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(**bad))
