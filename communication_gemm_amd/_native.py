@@ -3,7 +3,7 @@
 Every step of the operation runs in the library's HIP kernels; this module
 turns torch tensors into device pointers and sizes, passes the current
 stream, and raises on a non-zero status.  The library must have been built
-(``python -m communication_gemm_amd.build``); importing this module without
+(``python communication_gemm_amd/build.py``); importing this module without
 it fails loudly, there is no fallback.
 """
 from __future__ import annotations
@@ -130,7 +130,11 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m communication_gemm_amd.build` (hipcc, gfx950)")
+            "`python communication_gemm_amd/build.py` (hipcc, gfx950)")
+    # torch first: it brings its own HIP runtime, and the library must bind
+    # to that one.  Loaded the other way round, the process ends up with the
+    # system runtime under torch, and torch's first device allocation fails.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in EXPORTS.items():
         fn = getattr(lib, name)

@@ -3,6 +3,10 @@ import sys
 
 import pytest
 
+# torch before the library in every test process (the library binds to the
+# HIP runtime already loaded; see communication_gemm_amd/_native.py)
+import torch  # noqa: F401,E402
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

@@ -54,3 +54,24 @@ def test_producer_sees_writes_queued_before_the_call(agg, kind):
     call(C)
     assert agg.check() == 0
     assert torch.equal(C, ref)
+
+
+def test_package_imported_before_torch_still_runs(tmp_path):
+    """A fresh process that imports the package before torch: the library
+    must still share torch's HIP runtime, so torch's allocations and the
+    library's calls both work."""
+    import subprocess
+    import sys
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__file__))
+    code = ("import communication_gemm_amd as agg\n"
+            "import torch\n"
+            "ts = [torch.ones((64, 64), dtype=torch.float16, device='cuda') for _ in range(2)]\n"
+            "B = torch.ones((64, 32), dtype=torch.float16, device='cuda')\n"
+            "C = torch.empty((128, 32), device='cuda')\n"
+            "agg.ag_gemm_f16(ts, B, C)\n"
+            "assert agg.check() == 0\n"
+            "assert (C == 64).all()\n"
+            "print('ok')\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0 and "ok" in out.stdout, out.stdout + out.stderr
