@@ -52,6 +52,7 @@ class Options(ctypes.Structure):
         ("scheme", ctypes.c_int),
         ("pvalue", ctypes.c_int),
         ("trace", ctypes.c_void_p),
+        ("producer_piece_bytes", ctypes.c_int64),
     ]
 
 

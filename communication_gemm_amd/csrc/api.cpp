@@ -220,7 +220,8 @@ int run(const Call& c)
     pa.trace = opt->trace;
     pa.counters = header;
     pa.flags = header + kFlagOffset / 4;
-    pa.pieces = reinterpret_cast<uint64_t*>(ws + kPieceOffset);
+    pa.pieces = reinterpret_cast<uint32_t*>(ws + kPieceOffset);
+    pa.piece = p.piece;
     pa.ppc = p.ppc;
     pa.err = header + kErrorOffset / 4;
     pa.clock = reinterpret_cast<uint64_t*>(ws + kClockOffset);

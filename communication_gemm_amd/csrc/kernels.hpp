@@ -16,8 +16,9 @@ struct ProducerArgs {
     char* dst[kMaxShards];         // workspace slot of each remote shard
     uint32_t* counters;            // header base; counter of shard i at i * 32
     uint32_t* flags;               // chunk flag matrix: [shard][kFlagCap]
-    uint64_t* pieces;              // piece counters: [shard][kFlagCap]
+    uint32_t* pieces;              // piece running totals: [shard][kFlagCap]
     int ppc;                       // pieces per chunk (the last chunk's may be empty)
+    int64_t piece;                 // bytes per piece, a multiple of kWaveSweepBytes
     uint32_t* err;
     uint64_t* clock;               // pacing origin slot
     uint32_t base[kMaxShards];     // counter values at the start of the call

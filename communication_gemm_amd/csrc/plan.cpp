@@ -131,6 +131,8 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (opt->link_model != AGG_LINKS_PARALLEL && opt->link_model != AGG_LINKS_SERIAL)
         return AGG_E_INVALID;
     if (opt->producer_wgs < 0 || opt->consumer_wgs < 0) return AGG_E_INVALID;
+    if (opt->producer_piece_bytes < 0 || opt->producer_piece_bytes % kWaveSweepBytes)
+        return AGG_E_INVALID;
     if (!(opt->timeout_ms >= 0.0)) return AGG_E_INVALID;
     if (num_cus <= 0) num_cus = 256;
     // Row and element offsets are formed in 64-bit; per-tile loop counters
@@ -236,9 +238,12 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     int cw = opt->consumer_wgs ? opt->consumer_wgs : num_cus;
     if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
     if (cw < 1) cw = 1;
-    // pieces per chunk (a chunk is below 2 GiB, so at most 65536)
+    // pieces per chunk
     const int64_t chunk_bytes = (int64_t)s.cr * K * elt_bytes(kind);
-    const int ppc = chunk_bytes > 0 ? (int)cdiv(chunk_bytes, kPieceBytes) : 1;
+    const int64_t piece = opt->producer_piece_bytes ? opt->producer_piece_bytes : kPieceAuto;
+    const int64_t ppc64 = chunk_bytes > 0 ? cdiv(chunk_bytes, piece) : 1;
+    if (ppc64 > kMaxPiecesPerChunk) return AGG_E_UNSUPPORTED;
+    const int ppc = (int)ppc64;
     const int64_t items = chunks * ppc;
     int pw = opt->producer_wgs ? opt->producer_wgs : num_cus;
     if (pw > items) pw = (int)(items > 0 ? items : 1);
@@ -246,6 +251,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     p.consumer_wgs = cw;
     p.producer_wgs = pw;
     p.ppc = ppc;
+    p.piece = piece;
     p.mode = opt->mode;
     p.link_gbps = opt->link_gbps;
     p.elt = elt_bytes(kind);

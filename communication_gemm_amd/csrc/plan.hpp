@@ -34,6 +34,7 @@ struct Plan {
     int consumer_wgs;
     int producer_wgs;
     int ppc;            // producer pieces per chunk
+    int64_t piece;      // bytes per producer piece
     int elt;            // bytes per A element
     int64_t M;
     size_t slot_bytes;  // workspace bytes per remote shard (full slot or ring)

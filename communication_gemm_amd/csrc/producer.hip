@@ -6,16 +6,17 @@
 // summary counter; several communication blocks per destination; chunks
 // sent in the order they are consumed).
 //
-// Each chunk is cut into 512 KiB pieces; piece q of producer position c is
-// item c * P + q, and workgroup w copies items w, w + G, w + 2G, ..., so
-// all workgroups work on the earliest chunks first and chunks complete in
-// about the order they are sent.  A finished chunk is published in three
-// steps, none of which waits for another workgroup:
-//   * each piece's copier waits until its device-scope (write-through)
-//     stores are performed in memory, then counts the piece in the chunk's
-//     piece counter;
-//   * the copier of the chunk's last piece stores the call's epoch in the
-//     chunk's flag (the chunk flag matrix);
+// Each chunk is cut into pieces (32 KiB by default); piece q of producer
+// position c is item c * P + q, and wave w of the producer grid copies items
+// w, w + W, w + 2W, ..., so every wave works on the earliest chunks first
+// and chunks complete in about the order they are sent.  Waves run on
+// their own, with no workgroup barrier after the start.  A finished chunk
+// is published in three steps, none of which waits for another wave:
+//   * each piece's wave waits until its device-scope (write-through) stores
+//     are performed in memory, then adds the piece's weight to the chunk's
+//     running total; the add that completes the chunk's total is the last;
+//   * that wave stores the call's epoch in the chunk's flag (the chunk flag
+//     matrix);
 //   * it then advances the source's summary counter over every flagged
 //     chunk contiguous with it, in one compare-and-swap.
 // So a counter value c means "chunks 0..c-1 are flagged", and the counter
@@ -25,6 +26,12 @@
 // workspace): a flag it sees was stored after the chunk's data reached
 // memory.  Counter and flags are updated with relaxed device-scope
 // atomics only, and the producer does no cache maintenance at all.
+//
+// A wave's memory operations are waited for at one point per sweep, where
+// its loads must land before they are stored: the stores of the previous
+// piece are complete there too, so the piece's add is issued then, and its
+// result is looked at the next such point.  Copy, count and release of
+// consecutive pieces thus overlap instead of queueing.
 //
 // Pacing: with ticks_per_byte > 0 a chunk is not flagged before the
 // emulated link could have carried it (parallel links: its own source's
@@ -41,49 +48,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned int)))) unsigned int v4u32;
 
 constexpr int kProducerThreads = 256;
+constexpr int kProducerWaves = kProducerThreads / 64;
 constexpr int kRsrcWord3 = 0x00020000;   // untyped 32-bit buffer accesses
-// Cache policy of the copy's stores: device scope (written through to
-// memory), so that their completion alone publishes them.
-constexpr int kStoreDevice = 16;
-constexpr int kUnroll = 8;   // 16-byte vectors in flight per lane
-
-// Copy `bytes` (a multiple of 16, both ends 16-byte aligned) with buffer
-// accesses: lane offsets stay fixed, the step goes into the scalar offset,
-// so eight 16-byte loads per lane are in flight on a handful of registers.
-__device__ __forceinline__ void copy_bytes(char* __restrict__ dst,
-                                           const char* __restrict__ src,
-                                           int64_t bytes)
-{
-    const int32_t n = (int32_t)bytes;   // a chunk is far below 2 GiB
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, n, kRsrcWord3);
-    const int32_t lane_off = threadIdx.x * 16;
-    constexpr int32_t kStep = kProducerThreads * 16;          // bytes per sweep
-    int32_t base = 0;
-    for (; base + kUnroll * kStep <= n; base += kUnroll * kStep) {
-        u32x4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rs, lane_off, base + u * kStep, 0));
-        // every load is issued before the first store: the compiler would
-        // otherwise pair each load with its store and keep one in flight
-        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]),
-                          "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[u]), rd,
-                                                   lane_off, base + u * kStep, kStoreDevice);
-    }
-    // the tail: lanes past the end are out of range and do nothing.  The
-    // whole offset goes into the lane offset, which the range check covers
-    for (; base < n; base += kStep) {
-        const int32_t off = base + lane_off;
-        v4u32 t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(t, rd, off, 0, kStoreDevice);
-    }
-}
+// Cache policy of the copy's loads and stores: device scope.  The loads
+// read what is coherent at that scope (no stale cached line of a shard);
+// the stores are written through, so that their completion alone
+// publishes them.
+constexpr int kDevice = 16;
+constexpr int kUnroll = 8;               // 16-byte vectors in flight per lane
+constexpr int kLaneStep = 64 * 16;       // bytes per vector across a wave
+static_assert(kUnroll * kLaneStep == kWaveSweepBytes, "sweep size");
 
 // Advance the summary counter of one source over the flagged chunks that
 // follow it.  Runs on one lane after that lane's own flag store has been
@@ -108,20 +82,43 @@ __device__ void advance(uint32_t* ctr, const uint32_t* flags, uint32_t base, int
     }
 }
 
-// Count one copied piece of a chunk; true for the piece that completes it.
-// The word holds the call's epoch above the count, so it needs no reset: a
-// word left by an earlier call restarts at one.
-__device__ bool count_piece(uint64_t* word, uint32_t epoch, int ppc)
+__device__ __forceinline__ int32_t uniform(int32_t x)
 {
-    uint64_t cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-        const uint64_t next = (uint32_t)(cur >> 32) == epoch
-                                  ? cur + 1
-                                  : ((uint64_t)epoch << 32) | 1u;
-        if (__hip_atomic_compare_exchange_strong(word, &cur, next, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-            return (uint32_t)next == (uint32_t)ppc;
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ __forceinline__ void* uniform_ptr(const void* p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Release chunk c (lane 0 of the wave whose add completed it): wait for the
+// emulated link if paced, stamp, flag, advance the summary counter.
+__device__ void release_chunk(const ProducerArgs& a, int64_t c, uint64_t origin)
+{
+    const ChunkRef r = chunk_at(a.s, c);
+    if (a.ticks_per_byte > 0.0) {
+        const double b = (double)paced_bytes(a.s, r, a.elt);
+        const double delta = b * a.ticks_per_byte;
+        // a pace slower than the wait limit is a failed call, not a hang
+        if (delta > (double)a.limit) {
+            raise_error(a.err, a.epoch);
+            return;
+        }
+        wait_until(origin, (uint64_t)delta);
     }
+    uint32_t* flags = a.flags + r.shard * kFlagCap;
+    // stamped before the flag, so a consumer that saw the flag started
+    // after this time
+    if (a.trace) a.trace[1 + c] = ticks();
+    __hip_atomic_store(flags + r.j, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the flag store is performed before the counter is read
+    __builtin_amdgcn_s_waitcnt(0);
+    advance(a.counters + r.shard * (kCounterStride / 4), flags, a.base[r.shard], a.s.cps,
+            a.epoch);
 }
 
 }  // namespace
@@ -129,7 +126,7 @@ __device__ bool count_piece(uint64_t* word, uint32_t epoch, int ppc)
 __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs a)
 {
     const Schedule& s = a.s;
-    const int64_t items = total_chunks(s) * a.ppc;
+    const int64_t chunks = total_chunks(s);
     const int64_t row_bytes = s.K * a.elt;
     __shared__ uint64_t origin_sh;
     __shared__ int stop_sh;
@@ -143,14 +140,17 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     // before the work queued ahead of the call has finished.  The consumer
     // runs on the caller's stream, so its start proves that; each of its
     // workgroups writes the call's epoch to the start word on entry.
+    // The shards were written before the consumer started, but this kernel
+    // may have been resident since before that, and the caches of its CU
+    // and XCD may hold lines of an earlier call's shards: the copy's loads
+    // are device-scope loads, which are coherent at that scope and take no
+    // such line (so no cache invalidation, which cost the consumer its
+    // cached panels, is needed here).
     if (a.start) {
         if (threadIdx.x == 0)
             stop_sh = !reached(poll_until(a.start, a.epoch, a.err, a.epoch, a.limit), a.epoch);
         __syncthreads();
         if (stop_sh) return;
-        // the shards were written before the consumer started; drop any
-        // stale copies of them from this CU's caches
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     if (threadIdx.x == 0) {
         origin_sh = a.ticks_per_byte > 0.0 ? pacing_origin(a.clock, a.epoch) : 0;
@@ -158,72 +158,166 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     }
     __syncthreads();
 
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int64_t c = it / a.ppc;                  // producer position
-        const int64_t q = it % a.ppc;                  // piece of its chunk
-        const ChunkRef r = chunk_at(s, c);
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * kProducerWaves;
+    const int32_t lane_off = lane * 16;
+
+    // Piece bookkeeping of this wave (uniform across its lanes): `pend`,
+    // the chunk of the piece whose stores were issued last and are not
+    // counted yet (-1: none), with its running total and weight; `cnt`,
+    // the chunk of the piece whose add is in flight (-1: none), with its
+    // weight.  `old` is the running total the add returned (lane 0).
+    // (Positions and total indices fit 32 bits: at most kMaxShards x
+    // kFlagCap chunks.)
+    int32_t pend = -1, cnt = -1;
+    uint32_t pend_total = 0, pend_w = 0, cnt_w = 0, old = 0;
+
+    // The piece being copied: item chunk * ppc + q (producer position
+    // `chunk`, piece q of it), stepped by `waves` items without dividing;
+    // its running total and weight, its bytes and descriptors, and the
+    // next sweep's offset.
+    const int64_t first = (int64_t)blockIdx.x * kProducerWaves +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ppc = (uint32_t)a.ppc;
+    const int32_t nchunks = (int32_t)chunks;
+    // steps past the last chunk are clamped: the wave is done then anyway
+    const int64_t sc = waves / ppc;
+    const int32_t step_c = sc < nchunks ? (int32_t)sc : nchunks;
+    const uint32_t step_q = (uint32_t)(waves % ppc);
+    const int64_t c0 = first / ppc;
+    int32_t chunk = c0 < nchunks ? (int32_t)c0 : nchunks;
+    uint32_t q = (uint32_t)(first % ppc);
+    uint32_t total = 0, weight = 0;
+    int32_t n = 0, off = 0;
+    const char* src = nullptr;
+    char* dst = nullptr;
+    bool timed_out = false;   // a stage wait timed out (reported at the end)
+    // Workspace ring: the current item may be copied once the stage counter
+    // `wait_word` reaches `wait_for` (null: no wait); polls so far, and the
+    // time of the first.
+    const uint64_t* wait_word = nullptr;
+    uint32_t wait_for = 0, wait_spins = 0;
+    uint32_t wait_t0 = 0;   // low half of the clock: waits stay below 2^32 ticks
+    const uint32_t wait_limit = a.limit < 0xffffffffull ? (uint32_t)a.limit : 0xffffffffu;
+    // Set up the current item; false when there is none.
+    auto setup = [&]() -> bool {
+        if (chunk >= nchunks) return false;
+        const ChunkRef r = chunk_at(s, chunk);
         const int64_t row0 = (int64_t)r.j * s.cr;
         // Workspace ring: the chunk's panel goes over the panel that used
         // the stage before; wait until the consumer has finished every
         // tile of that one (its reads of the stage are complete then).
+        // The wait itself happens in the copy loop, once this wave has
+        // counted every piece it copied (the consumer may need them to
+        // finish those tiles).
         if (a.stages) {
             const int m = (int)(row0 / s.tm);
             const int64_t before = stage_tiles_before(s, m);
             if (before > 0) {
-                if (threadIdx.x == 0)
-                    stop_sh = !poll_count(a.stages + r.shard * kMaxStages + m % s.ring, a.epoch,
-                                          (uint32_t)before, a.err, a.limit);
-                __syncthreads();
-                if (stop_sh) break;
+                wait_word = a.stages + r.shard * kMaxStages + m % s.ring;
+                wait_for = (uint32_t)before;
+                wait_spins = 0;
             }
         }
+        total = (uint32_t)(r.shard * kFlagCap + r.j);
+        weight = piece_weight((int)q, a.ppc);
         const int64_t bytes = (chunk_row_end(s, r.j) - row0) * row_bytes;
-        const int64_t begin = q * kPieceBytes;
-        const int64_t end = begin + kPieceBytes < bytes ? begin + kPieceBytes : bytes;
-        if (begin < end)
-            copy_bytes(a.dst[r.shard] + slot_row(s, row0) * row_bytes + begin,
-                       a.src[r.shard] + row0 * row_bytes + begin, end - begin);
-        // The copy's stores are device-scope stores, written through to
-        // memory; a store is counted done only once it is performed there.
-        // Waiting for them is what makes the piece visible to every CU, so
-        // no cache write-back (what a release fence would add, for the
-        // whole L2) is needed before the piece is counted.
+        const int64_t begin = q * a.piece;
+        const int64_t end = begin + a.piece < bytes ? begin + a.piece : bytes;
+        // an empty piece of a short last chunk copies nothing but counts
+        n = end > begin ? (int32_t)(end - begin) : 0;  // a chunk is below 2 GiB
+        off = 0;
+        src = a.src[r.shard] + row0 * row_bytes + begin;
+        dst = a.dst[r.shard] + slot_row(s, row0) * row_bytes + begin;
+        return true;
+    };
+
+    bool have = setup();
+    for (;;) {
+        u32x4 v[kUnroll];
+        const bool copy = have && !wait_word && off < n;
+        // Buffer accesses: lane offsets stay fixed, the sweep's step goes
+        // into the scalar offset; the descriptors end where the piece ends
+        // (a multiple of 16 bytes), so lanes past it load zeros and store
+        // nothing.  Built from first-lane copies, which are uniform to the
+        // compiler (loop-carried, it would take them as per-lane values).
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(src), 0, uniform(n), kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rd =
+            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(dst), 0, uniform(n), kRsrcWord3);
+        if (copy) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rs, lane_off, uniform(off) + u * kLaneStep, kDevice));
+        }
+        // The one wait point of a sweep: this wave's loads have landed, and
+        // its earlier stores and add are performed.  Store the sweep (its
+        // registers are free once the stores are issued), look at the add
+        // that was in flight, then count the piece whose stores were last.
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (threadIdx.x == 0 &&
-            count_piece(a.pieces + r.shard * kFlagCap + r.j, a.epoch, a.ppc) && c != a.drop) {
-            // every piece of the chunk is in memory: release it
-            bool ok = true;
-            if (a.ticks_per_byte > 0.0) {
-                const double b = (double)paced_bytes(s, r, a.elt);
-                const double delta = b * a.ticks_per_byte;
-                // a pace slower than the wait limit is a failed call, not a hang
-                if (delta > (double)a.limit) {
-                    raise_error(a.err, a.epoch);
-                    ok = false;
+        if (copy) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[u]), rd,
+                                                       lane_off, uniform(off) + u * kLaneStep,
+                                                       kDevice);
+            off += kWaveSweepBytes;
+        }
+        if (cnt >= 0) {
+            if (lane == 0 && ((old + cnt_w) & (kPieceTotal - 1)) == 0 && cnt != a.drop)
+                release_chunk(a, cnt, origin_sh);
+            cnt = -1;
+        }
+        if (pend >= 0) {
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(a.pieces + pend_total, pend_w, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+            cnt = pend;
+            cnt_w = pend_w;
+            pend = -1;
+        }
+        if (have && wait_word) {
+            // Poll the stage once this wave holds no uncounted piece.  The
+            // wait is bounded: it fails after the call's limit, or when
+            // another workgroup of the call has failed; the wave then
+            // stops copying.
+            if (pend < 0 && cnt < 0) {
+                const uint64_t w =
+                    __hip_atomic_load(wait_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)w);
+                const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
+                if (tagged_count(((uint64_t)hi << 32) | lo, a.epoch) >= wait_for) {
+                    wait_word = nullptr;
                 } else {
-                    wait_until(origin_sh, (uint64_t)delta);
+                    if (wait_spins == 0) wait_t0 = (uint32_t)ticks();
+                    __builtin_amdgcn_s_sleep(2);
+                    if ((++wait_spins & 31u) == 0) {
+                        if (reached(__builtin_amdgcn_readfirstlane(load_agent(a.err)), a.epoch)) {
+                            have = false;
+                        } else if ((uint32_t)ticks() - wait_t0 > wait_limit) {
+                            timed_out = true;
+                            have = false;
+                        }
+                    }
                 }
             }
-            if (ok) {
-                uint32_t* flags = a.flags + r.shard * kFlagCap;
-                // stamped before the flag, so a consumer that saw the flag
-                // started after this time
-                if (a.trace) a.trace[1 + c] = ticks();
-                __hip_atomic_store(flags + r.j, a.epoch, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                // the flag store is performed before the counter is read
-                __builtin_amdgcn_s_waitcnt(0);
-                advance(a.counters + r.shard * (kCounterStride / 4), flags,
-                        a.base[r.shard], s.cps, a.epoch);
+        } else if (have && off >= n) {        // the piece's stores are all issued
+            pend = chunk;
+            pend_total = total;
+            pend_w = weight;
+            chunk += step_c;
+            q += step_q;
+            if (q >= ppc) {
+                q -= ppc;
+                ++chunk;
             }
+            have = setup();
+        } else if (!have && cnt < 0) {
+            break;                     // drained: nothing stored or added is left
         }
-        // stop early once a workgroup of this call has failed; one lane
-        // decides for the whole workgroup, so every wave leaves together
-        if (threadIdx.x == 0) stop_sh = reached(load_agent(a.err), a.epoch);
-        __syncthreads();
-        if (stop_sh) break;
     }
+    if (timed_out && lane == 0) raise_error(a.err, a.epoch);
 }
 
 // Zero `bytes` bytes of a workspace header (counters, error word, pacing

@@ -23,9 +23,10 @@ constexpr int kMaxShards = 64;
 // its own 128-byte line, then the error word, the pacing origin, the start
 // word (the epoch of the last call whose consumer has started), the
 // chunk flag matrix (one 32-bit word per source and chunk: the epoch of the
-// call that released it), the piece counters (one 64-bit word per source
-// and chunk: the call's epoch above the number of the chunk's pieces
-// copied so far) and, for a bounded workspace, the stage counters (one
+// call that released it), the piece counters (one 32-bit running total per
+// source and chunk, to which every call adds exactly kPieceTotal in
+// weighted piece counts; the region keeps 64-bit slots) and, for a
+// bounded workspace, the stage counters (one
 // 64-bit word per source and ring stage: the call's epoch above the number
 // of tiles finished on that stage).  The PTO-ISA README keeps the first
 // two structures: per-chunk flags and a per-source summary counter.
@@ -40,12 +41,29 @@ constexpr int kMaxStages = 8;        // ring stages per source, at most
 constexpr int kStageOffset = kPieceOffset + kMaxShards * kFlagCap * 8;
 constexpr int kHeaderBytes = kStageOffset + kMaxShards * kMaxStages * 8;
 
-// The producer copies a chunk in pieces of up to this many bytes, dealt to
-// its workgroups in send order, so that a large chunk is shared by many
-// workgroups and all of them work on the earliest chunks first.  Each
-// piece ends in a wait for its stores and an atomic count, so pieces are
-// kept large enough (16 sweeps of a workgroup) for that to stay small.
-constexpr int kPieceBytes = 524288;
+// The producer copies a chunk in pieces, dealt to its waves in send order,
+// so that a chunk is shared by many waves and all of them work on the
+// earliest chunks first.  A wave moves 8 KiB per sweep (64 lanes x 8
+// vectors of 16 bytes).  The automatic piece is four sweeps: one-sweep
+// pieces copied slower (one count per sweep, and more waves per chunk to
+// wait for), larger ones made the first chunks land later.
+constexpr int kWaveSweepBytes = 8192;
+constexpr int kPieceAuto = 4 * kWaveSweepBytes;
+
+// Completion of a chunk without a per-call reset: the pieces of a chunk add
+// weights that sum to kPieceTotal, every weight at least 1, to the chunk's
+// running total.  A call starts from a multiple of kPieceTotal (the header
+// is zeroed when made and after a failed call), so exactly one add, the
+// last, brings the total back to a multiple of it, whatever the order of
+// the adds; modulo 2^32, which kPieceTotal divides, this still holds.
+constexpr uint32_t kPieceTotal = 1u << 20;
+constexpr int kMaxPiecesPerChunk = 1 << 18;   // weights stay >= 4
+
+AGG_HD uint32_t piece_weight(int q, int ppc)
+{
+    const uint32_t w = kPieceTotal / (uint32_t)ppc;
+    return q == ppc - 1 ? kPieceTotal - (uint32_t)(ppc - 1) * w : w;
+}
 
 struct Schedule {
     int n_shards;
@@ -163,32 +181,36 @@ struct ChunkRef {
 };
 
 // Producer position c -> chunk, in the order the consumer needs them.
-AGG_HD ChunkRef chunk_at(const Schedule& s, int64_t c)
+// Parallel links: group g holds the chunks first needed by m-tile g (chunk
+// j of a source belongs to group j * cr / tm), every source in send order,
+// chunks ascending inside a source.  Group g starts at source chunk
+// f = ceil(g tm / cr); as f * remotes <= c exactly when f <= c / remotes,
+// the group of position c is the group of source chunk c / remotes.
+// 32-bit arithmetic: positions stay below kMaxShards * kFlagCap, and
+// j * cr below S (at most 2^30).
+AGG_HD ChunkRef chunk_at(const Schedule& s, int64_t c64)
 {
     ChunkRef r;
-    int remotes = s.n_shards - 1;
-    if (s.link_model == 0) {
-        // group g = chunks first needed by m-tile g, every source in send
-        // order, chunks ascending inside a source
-        int prev = 0;
-        for (int g = 0; g < s.mt; ++g) {
-            int cur = need_chunks(s, g);
-            int64_t gs = cur - prev;
-            int64_t span = gs * remotes;
-            if (c < span) {
-                r.src = (int)(c / gs);
-                r.j = prev + (int)(c % gs);
-                r.shard = s.order[1 + r.src];
-                return r;
-            }
-            c -= span;
-            prev = cur;
-        }
+    const uint32_t remotes = (uint32_t)(s.n_shards - 1);
+    const uint32_t cps = (uint32_t)s.cps, cr = (uint32_t)s.cr, tm = (uint32_t)s.tm;
+    if (c64 < 0 || remotes == 0 || c64 >= (int64_t)remotes * cps) {
         r.src = -1; r.j = -1; r.shard = -1;   // out of range
         return r;
     }
-    r.src = (int)(c / s.cps);
-    r.j = (int)(c % s.cps);
+    const uint32_t c = (uint32_t)c64;
+    if (s.link_model == 0) {
+        const uint32_t g = (c / remotes) * cr / tm;
+        const uint32_t f = (g * tm + cr - 1) / cr;           // first chunk of group g
+        uint32_t e = ((g + 1) * tm + cr - 1) / cr;           // first chunk after it
+        if (e > cps) e = cps;
+        const uint32_t gs = e - f;                           // chunks per source in g
+        const uint32_t rel = c - f * remotes;
+        r.src = (int)(rel / gs);
+        r.j = (int)(f + rel % gs);
+    } else {
+        r.src = (int)(c / cps);
+        r.j = (int)(c % cps);
+    }
     r.shard = s.order[1 + r.src];
     return r;
 }

@@ -161,6 +161,14 @@ typedef struct agg_options {
                                reach keep their contents; the caller clears
                                the buffer.  A chunk's release is stamped
                                before its flag is published.                 */
+    int64_t producer_piece_bytes; /* bytes a producer wave copies before it
+                               counts them towards their chunk: a multiple
+                               of 8192; 0 = automatic (32768).  Smaller pieces
+                               spread a chunk over more waves, so chunks
+                               land closer to their send order.  Invalid
+                               (AGG_E_INVALID) if negative or not a
+                               multiple of 8192; a chunk may be cut into at
+                               most 2^18 pieces (AGG_E_UNSUPPORTED).        */
 } agg_options;
 
 /* Fill *opt with the defaults above. */

@@ -2,8 +2,9 @@
 
 Chunking cuts A along M only and never changes the order of the K sum, so
 the HIP output must be bit-identical whatever the chunk size, local shard,
-send order, link pacing, link model, producer width or mode (the gathered
-result is the same C: PTO-ISA AllGather+GEMM README, "compute function").
+send order, link pacing, link model, producer width, producer piece size
+or mode (the gathered result is the same C: PTO-ISA AllGather+GEMM README,
+"compute function").
 A consumer that read a chunk before its release would see the NaN planted
 in the workspace.  A withheld release must end in a reported time-out, not
 a hang.
@@ -57,6 +58,11 @@ def ref(agg, data, orc):
     dict(link_gbps=50.0), dict(link_gbps=20.0, link_model=1),
     dict(producer_wgs=1), dict(producer_wgs=3), dict(consumer_wgs=7),
     dict(mode=2),
+    # producer pieces: one sweep; one sweep with 100-row chunks (25 pieces a
+    # chunk, the short last chunk mostly empty pieces); a piece larger than
+    # every chunk; one sweep on a single producer workgroup
+    dict(producer_piece_bytes=8192), dict(producer_piece_bytes=8192, chunk_rows=100),
+    dict(producer_piece_bytes=1 << 20), dict(producer_piece_bytes=8192, producer_wgs=1),
 ])
 def test_bitwise_invariant(agg, data, ref, kw):
     kw = dict(kw)

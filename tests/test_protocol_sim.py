@@ -1,9 +1,11 @@
 """Liveness of the chunk protocol, checked by simulation on the CPU.
 
 A g++ program builds real plans with the library's own plan.cpp and
-schedule.hpp, then runs every workgroup of both kernels as the kernels do:
-producer workgroup w takes items w, w + P, ... in order, and before a piece
-of a ring panel it waits for the stage's finished tiles; consumer workgroup
+schedule.hpp, then runs every agent of both kernels as the kernels do:
+producer wave w takes items w, w + P, ... in order, and before a piece of a
+ring panel it waits for the stage's finished tiles, having counted every
+piece it copied before (a wave that waited on a stage while holding an
+uncounted piece could stall the tiles it waits for); consumer workgroup
 b takes positions wg_position(b) + r G in order, and before a tile it waits
 for its source's counter (every source's, in the barrier scheme), then
 counts the tile on its ring stage.  Counters advance over contiguous

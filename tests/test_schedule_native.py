@@ -74,3 +74,67 @@ def test_xcd_placement_is_a_blocked_permutation(tmp_path):
     checked, split, f = map(int, out.stdout.split())
     assert checked == 64 * 1024 and split > 1000
     assert f in (2, 4)          # 16 panels x 16 n-tiles: 4 x 8 or 8 x 4 blocks
+
+
+CHUNK_ORDER = r"""
+#include <cstdio>
+#include "schedule.hpp"
+using namespace agg;
+// The send order by its definition: m-tile group after m-tile group, the
+// chunks each group needs first, source after source (parallel links), or
+// source after source (one serial link).
+static bool by_definition(const Schedule& s, long c, int* src, int* j) {
+    int remotes = s.n_shards - 1;
+    if (s.link_model != 0) { *src = (int)(c / s.cps); *j = (int)(c % s.cps); return c < (long)remotes * s.cps; }
+    int prev = 0;
+    for (int g = 0; g < s.mt; ++g) {
+        int cur = need_chunks(s, g);
+        long span = (long)(cur - prev) * remotes;
+        if (c < span) { *src = (int)(c / (cur - prev)); *j = prev + (int)(c % (cur - prev)); return true; }
+        c -= span; prev = cur;
+    }
+    return false;
+}
+int main() {
+    long checked = 0;
+    const int Ss[] = {1, 7, 63, 64, 100, 128, 1000, 1024, 4096, 8192, 65536};
+    const int tms[] = {32, 64, 128, 256};
+    for (int S : Ss) for (int tm : tms) for (int n = 2; n <= 9; n += 3) for (int lm = 0; lm < 2; ++lm)
+    for (int cr = 1; cr <= S; cr = cr < 8 ? cr + 1 : cr * 2 + (cr % 3)) {
+        Schedule s{};
+        s.n_shards = n; s.link_model = lm; s.cr = cr; s.S = S; s.tm = tm;
+        s.cps = (int)cdiv(S, cr); s.mt = (int)cdiv(S, tm);
+        if (s.cps > kFlagCap) continue;
+        for (int i = 0; i < n; ++i) s.order[i] = (i * 5 + 1) % n;
+        long total = (long)(n - 1) * s.cps;
+        for (long c = -1; c <= total; ++c) {
+            int src = -1, j = -1;
+            bool in = c >= 0 && by_definition(s, c, &src, &j);
+            ChunkRef r = chunk_at(s, c);
+            if (!in) { if (r.src != -1) { printf("range S=%d cr=%d tm=%d c=%ld\n", S, cr, tm, c); return 1; } continue; }
+            if (r.src != src || r.j != j || r.shard != s.order[1 + src]) {
+                printf("S=%d cr=%d tm=%d n=%d lm=%d c=%ld: %d/%d vs %d/%d\n", S, cr, tm, n, lm, c, r.src, r.j, src, j);
+                return 1;
+            }
+            ++checked;
+        }
+    }
+    printf("%ld\n", checked);
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ needed")
+def test_chunk_order_closed_form_matches_definition(tmp_path):
+    """chunk_at's constant-time form (used for every producer piece) gives
+    the send order defined group by group: for many shard, chunk and tile
+    heights, both link models, every position and one past each end."""
+    src = tmp_path / "chunks.cpp"
+    src.write_text(CHUNK_ORDER)
+    exe = tmp_path / "chunks"
+    subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout
+    assert int(out.stdout) > 100000
