@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 workload")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 variant")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 variant")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="skip the ring-variant runs (D = 2, 4, 8)")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip the pipelined chunk-size sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -311,6 +313,57 @@ def run_f16(args, torch, agg, synth):
     return case, res, flops, (shards, B)
 
 
+# Pallas:MGPU collective matmul page: per-device (1024 D) x 4096 x 4096 fp16
+# with the LHS all-gathered around a ring, on H100s (other hardware, context
+# only): the ring kernel, its model lower bound and the all-gather + matmul
+# reference, in microseconds for D = 2, 4, 8.
+PAGE_RING_US = {2: (102, 92, 147), 4: (212, 190, 290), 8: (436, 386, 565)}
+XGMI_LINK_GBPS = 153.0   # one MI355X xGMI link, per direction
+
+
+def run_ring(args, torch, agg, synth):
+    """The ring variant on one GPU: device 0's view of a D-device ring, the
+    shards arriving one after the other over one emulated link in ring order
+    (own shard, then d+1, d+2, ...), each consumed as its chunks land; beside
+    it the copy-then-GEMM reference (sequential mode), the same ring paced
+    at one xGMI link's rate, and the full mesh (one link per source) at that
+    rate."""
+    out = {}
+    n = max(20, args.steps // 2)
+    for D in (2, 4, 8):
+        M, K, N = 1024 * D, 4096, 4096
+        shards, B = synth.make_f16(M, K, N, D, "normal", 90000 + D)
+        ts = [torch.from_numpy(x).cuda() for x in shards]
+        tB = torch.from_numpy(B).cuda()
+        del shards, B
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(agg.workspace_bytes(D, M, K, 2), dtype=torch.uint8, device="cuda")
+        agg.workspace_reset(ws)
+
+        def timed_call(**kw):
+            def fn(ev):
+                agg.ag_gemm_f16(ts, tB, C, 0, opts=agg.options(workspace=ws, **kw))
+            return round(timed(torch, fn, n, 10, with_consumer=False)[0] * 1e3, 1)
+
+        timed_call(mode=agg.MODE_COPY_ONLY)
+        r = {"workload": f"f16 {D}x1024 rows M={M} K={K} N={N}, ring order, one serial link",
+             "ring_us": timed_call(link_model=agg.LINKS_SERIAL),
+             "copy_then_gemm_us": timed_call(link_model=agg.LINKS_SERIAL, mode=agg.MODE_SEQUENTIAL),
+             "compute_only_us": timed_call(mode=agg.MODE_COMPUTE_ONLY),
+             "ring_xgmi_paced_us": timed_call(link_model=agg.LINKS_SERIAL,
+                                              link_gbps=XGMI_LINK_GBPS),
+             "mesh_xgmi_paced_us": timed_call(link_model=agg.LINKS_PARALLEL,
+                                              link_gbps=XGMI_LINK_GBPS)}
+        if agg.check():
+            raise SystemExit("ring runs failed")
+        r["tflops"] = round(2.0 * M * K * N / (r["ring_us"] * 1e-6) / 1e12, 1)
+        page = PAGE_RING_US[D]
+        r["page_h100_us"] = {"ring": page[0], "model_bound": page[1], "allgather_then_matmul": page[2]}
+        out[str(D)] = r
+        del ts, tB, C, ws
+    return out
+
+
 def run_i8(args, torch, agg, synth):
     case = synth.CASES[5]
     shards, B, bias, scale = synth.make_case(case)
@@ -476,6 +529,8 @@ def main():
         line["fp8"] = run_fp8(args, torch, agg, synth)
     if not args.no_int8:
         line["int8"] = run_i8(args, torch, agg, synth)
+    if not args.no_ring:
+        line["ring"] = run_ring(args, torch, agg, synth)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)

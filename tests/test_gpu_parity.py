@@ -260,7 +260,7 @@ def test_bf16_small_full(agg, orc):
     check_f16(C, Co, So, "bf16 small")
 
 
-@pytest.mark.parametrize("tile", [3, 8, 6])
+@pytest.mark.parametrize("tile", [3, 8, 6, 11])
 def test_bf16_ragged(agg, orc, tile):
     shards, B = synth.make_bf16(3 * 100, 296, 168, 3, "uniform", 35100 + tile)
     C = run_bf16(agg, shards, B, 7, agg.options(tile=tile))

@@ -227,6 +227,23 @@ def test_empty_problems_are_no_ops():
     assert _f16([FAKE, FAKE], 2, FAKE, 0, 64, 64, 0) == agg.AGG_OK
 
 
+@pytest.mark.parametrize("kind,n,S,K,N,tile", [
+    ("f16", 8, 1024, 4096, 4096, 8),     # 512 tiles of 256 x 256
+    ("f16", 4, 1024, 4096, 4096, 8),     # 256 of them: one per CU
+    ("f16", 2, 1024, 4096, 4096, 11),    # 128 x 256, eight waves
+    ("bf16", 2, 1024, 4096, 4096, 11),
+    ("f16", 2, 1024, 2048, 1024, 13),    # 2 x 1024 rows, N = 1024: 64 x 64
+    ("i8", 2, 8192, 27392, 4096, 8),
+    ("i8", 2, 32, 16384, 7168, 13),
+])
+def test_automatic_tile(kind, n, S, K, N, tile):
+    """The automatic tile: the first of the planner's list (largest first,
+    eight-wave before four-wave at equal size) that gives every one of the
+    256 CUs a tile."""
+    info, _, _ = agg.plan(kind, n, n * S, K, N)
+    assert info.tile_id == tile
+
+
 def test_fp8_plans_only_tiles_built_for_it():
     """The fp8 path runs the configurations whose slices hold pairs of
     64-byte MFMA steps; the automatic choice stays among them."""
