@@ -53,6 +53,7 @@ class Options(ctypes.Structure):
         ("pvalue", ctypes.c_int),
         ("trace", ctypes.c_void_p),
         ("producer_piece_bytes", ctypes.c_int64),
+        ("k_splits", ctypes.c_int),
     ]
 
 
@@ -75,6 +76,7 @@ class PlanInfo(ctypes.Structure):
         ("trace_words", ctypes.c_int64),
         ("workspace_stages", ctypes.c_int),
         ("workspace_bytes", ctypes.c_int64),
+        ("k_splits", ctypes.c_int),
     ]
 
 

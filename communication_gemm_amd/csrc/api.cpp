@@ -216,6 +216,8 @@ int run(const Call& c)
     ca.scale = c.scale;
     ca.acc_out = opt->acc_out;
     ca.trace = opt->trace ? opt->trace + 1 + total_chunks(s) : nullptr;
+    ca.partials = s.ks > 1 ? ws + p.part_off : nullptr;
+    ca.tickets = header + kTicketOffset / 4;
     ca.trace_start = opt->trace;
     pa.trace = opt->trace;
     pa.counters = header;

@@ -275,6 +275,7 @@ struct Engine {
         int64_t rows_valid;  // A rows that exist
         const char* B;
         int64_t K, N, n0;
+        int64_t kb;          // first k of the tile's K range (split-K part)
     };
 
     // Per-lane byte offsets, computed once per kernel: where this lane's
@@ -473,7 +474,7 @@ struct Engine {
     {
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
-            if (s < nk) load_slice(ring + s * kStage, src, L, (int64_t)s * kBK);
+            if (s < nk) load_slice(ring + s * kStage, src, L, src.kb + (int64_t)s * kBK);
         // slice 0 has landed; the rest of the prologue may still be loading
         wait_slices((nk < NS - 1 ? nk : NS - 1) - 1);
         bare_barrier();
@@ -485,7 +486,7 @@ struct Engine {
             const int last = l < nk ? l : nk - 1;
             const int behind = last - (kt + 1) > 0 ? last - (kt + 1) : 0;
             slice(ring + (kt % NS) * kStage, ring + ((kt + 1) % NS) * kStage,
-                  ring + (l % NS) * kStage, l < nk, (int64_t)l * kBK, behind, kt + 1 < nk,
+                  ring + (l % NS) * kStage, l < nk, src.kb + (int64_t)l * kBK, behind, kt + 1 < nk,
                   src, L, f0, f1, acc);
         }
     }
@@ -625,6 +626,82 @@ __device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int
     return ok;
 }
 
+// Split-K: one part of a tile's K range is done.  Its accumulators go to
+// the tile's partial sums (register-major: each store of a wave writes 256
+// contiguous bytes), written through at device scope; once they are
+// performed, thread 0 adds the part's weight to the tile's ticket.  The
+// part whose add completes the ticket's total (the last to finish) reads
+// every part back in part order, with device-scope loads that take no
+// stale cached line, and adds them: the sum order is fixed, whichever part
+// finishes last.  Returns true in the workgroup that then runs the tile's
+// epilogue.
+template <class T, class E>
+__device__ bool split_reduce(const ConsumerArgs& a, const TileRef& t, int tid, int* last,
+                             typename T::Acc (&acc)[E::kTM][E::kTN])
+{
+    constexpr int R = E::kTM * E::kTN * 16;   // accumulators per thread
+    constexpr int TH = E::kThreads;
+    constexpr int kDevice = 16;               // device-scope cache policy
+    constexpr bool kInt = T::kDequant;        // int32 accumulators
+    const Schedule& s = a.s;
+    const int64_t tb = ((int64_t)t.shard * s.mt + t.m) * s.nt + t.n;
+    // the tile's parts: ks x R x TH words, far below 2^31 bytes
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        a.partials + tb * s.ks * R * TH * 4, 0, s.ks * R * TH * 4, kRsrcWord3);
+    const int own = t.kp * R * TH * 4 + tid * 4;
+#pragma unroll
+    for (int i = 0; i < E::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < E::kTN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                // the element is copied out first, as in the epilogue: a bit
+                // cast applied to a vector element directly reads element 0
+                uint32_t bits;
+                if constexpr (kInt) {
+                    bits = acc_read(acc[i][j][e]);
+                } else {
+                    const float x = acc[i][j][e];
+                    bits = __builtin_bit_cast(uint32_t, x);
+                }
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    bits, rp, own + ((i * E::kTN + j) * 16 + e) * TH * 4, 0, kDevice);
+            }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t w = piece_weight(t.kp, s.ks);
+        const uint32_t old = __hip_atomic_fetch_add(a.tickets + tb, w, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        *last = ((old + w) & (kPieceTotal - 1)) == 0;
+    }
+    __syncthreads();
+    if (!*last) return false;
+    // pairs with the other parts' performed stores, seen through the ticket
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+    for (int i = 0; i < E::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < E::kTN; ++j) acc[i][j] = T::zero();
+    for (int kp = 0; kp < s.ks; ++kp) {
+        const int at = kp * R * TH * 4 + tid * 4;
+#pragma unroll
+        for (int i = 0; i < E::kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < E::kTN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(
+                        rp, at + ((i * E::kTN + j) * 16 + e) * TH * 4, 0, kDevice);
+                    if constexpr (kInt)
+                        acc[i][j][e] = (int)((uint32_t)acc[i][j][e] + v);
+                    else
+                        acc[i][j][e] += __builtin_bit_cast(float, v);
+                }
+    }
+    return true;
+}
+
 template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs a)
 {
@@ -632,6 +709,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ uint32_t seen_sh[kMaxShards];
     __shared__ int ok_sh;
+    __shared__ int last_sh;
 
     const Schedule& s = a.s;
     const int tid = threadIdx.x;
@@ -644,7 +722,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     __syncthreads();
 
     const int64_t tiles = total_tiles(s);
-    const int nk = (int)cdiv(s.K, E::kBK);
     typename E::Lane L;
     E::lane_offsets(L, s.K, s.N);
 
@@ -673,8 +750,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
         const int64_t rows = s.S - row0;
         // remote rows sit in the workspace (a full slot or a ring stage)
         const int64_t arow = t.shard == s.local ? row0 : slot_row(s, row0);
+        // K range: all of K, or part kp of a split-K tile (parts hold a
+        // multiple of 256 k, a whole number of slices)
+        const int64_t kb = (int64_t)t.kp * s.kc;
+        const int64_t ke = kb + s.kc < s.K ? kb + s.kc : s.K;
+        const int nk = ke > kb ? (int)cdiv(ke - kb, E::kBK) : 0;
         const typename E::Src src{a.a[t.shard] + arow * s.K * T::kElt,
-                                  rows < BM ? rows : BM, a.B, s.K, s.N, (int64_t)t.n * BN};
+                                  rows < BM ? rows : BM, a.B, s.K, s.N, (int64_t)t.n * BN, kb};
 
         typename T::Acc acc[E::kTM][E::kTN];
 #pragma unroll
@@ -687,6 +769,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
         // waited for them before its barrier): the stage may be reused
         if (a.stages && t.shard != s.local && tid == 0)
             count_one(a.stages + t.shard * kMaxStages + t.m % s.ring, a.epoch);
+        // split-K is planned only on tiles of one or two 32 x 32 blocks
+        // per wave (ids 3, 12, 13, 14); the others are built without it,
+        // which keeps their registers as they were
+        if constexpr (E::kTM * E::kTN <= 2) {
+            if (s.ks > 1 && !split_reduce<T, E>(a, t, tid, &last_sh, acc)) {
+                if (a.trace && tid == 0) a.trace[3 * p + 2] = ticks();
+                continue;   // another part of the tile adds the parts
+            }
+        }
         store_tile<T, BM, BN, WM, WN>(a, t.shard, t.m, t.n, acc);
         if (a.trace && tid == 0) a.trace[3 * p + 2] = ticks();
     }
@@ -713,6 +804,9 @@ template <> struct Cfg<10> { static constexpr int BM = 256, BN = 128, SB = 128, 
 template <> struct Cfg<11> { static constexpr int BM = 128, BN = 256, SB = 128, NS = 2, WM = 2, WN = 4; };
 template <> struct Cfg<12> { static constexpr int BM = 64, BN = 64, SB = 128, NS = 8, WM = 2, WN = 2; };
 template <> struct Cfg<13> { static constexpr int BM = 64, BN = 64, SB = 256, NS = 4, WM = 2, WN = 2; };
+// 32 rows x 256 columns for decode-like shapes (split-K): B is read in rows
+// of 256 elements, one 32 x 64 block per wave, three slices in flight.
+template <> struct Cfg<14> { static constexpr int BM = 32, BN = 256, SB = 128, NS = 4, WM = 1, WN = 4; };
 
 template <class T, int ID>
 struct Kern {
@@ -798,6 +892,7 @@ hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t 
     case 11: return launch_id<T, 11>(a, wgs, st);
     case 12: return launch_id<T, 12>(a, wgs, st);
     case 13: return launch_id<T, 13>(a, wgs, st);
+    case 14: return launch_id<T, 14>(a, wgs, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -819,6 +914,7 @@ int occupancy_kind(int tile_id)
     case 11: return occupancy_id<T, 11>();
     case 12: return occupancy_id<T, 12>();
     case 13: return occupancy_id<T, 13>();
+    case 14: return occupancy_id<T, 14>();
     default: return 0;
     }
 }

@@ -56,6 +56,10 @@ struct ConsumerArgs {
     uint32_t* start;               // pipelined mode: set to the epoch on entry
     uint64_t* stages;              // workspace ring: count each finished remote
                                    // tile on its stage (nullptr: no count)
+    // split-K (s.ks > 1): partial sums, [tile][part][register][thread] of 4
+    // bytes, and one ticket (running total of part weights) per tile
+    char* partials;
+    uint32_t* tickets;
 };
 
 hipError_t launch_producer(const ProducerArgs& a, int wgs, hipStream_t st);

@@ -41,6 +41,7 @@ const TileShape kF16Shapes[] = {
     {7, 256, 256, 256, false},
     {9, 256, 256, 512, false},
     {12, 64, 64, 256, false},
+    {14, 32, 256, 256, false},
 };
 const TileShape kI8Shapes[] = {
     {8, 256, 256, 512, true},
@@ -56,6 +57,7 @@ const TileShape kI8Shapes[] = {
     {10, 256, 128, 512, false},
     {11, 128, 256, 512, false},
     {12, 64, 64, 256, false},
+    {14, 32, 256, 256, false},
 };
 // fp8: the configurations whose slices hold whole 64-byte MFMA steps in
 // pairs (128- or 256-byte slices).  The 8-wave 256 x 256 tile is left out:
@@ -70,6 +72,7 @@ const TileShape kFP8Shapes[] = {
     {13, 64, 64, 256, true},
     {3, 64, 64, 256, false},
     {12, 64, 64, 256, false},
+    {14, 32, 256, 256, false},
 };
 
 }  // namespace
@@ -136,6 +139,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (opt->producer_wgs < 0 || opt->consumer_wgs < 0) return AGG_E_INVALID;
     if (opt->producer_piece_bytes < 0 || opt->producer_piece_bytes % kWaveSweepBytes)
         return AGG_E_INVALID;
+    if (opt->k_splits < 0) return AGG_E_INVALID;
     if (!(opt->timeout_ms >= 0.0)) return AGG_E_INVALID;
     if (num_cus <= 0) num_cus = 256;
     // Row and element offsets are formed in 64-bit; per-tile loop counters
@@ -200,6 +204,24 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         }
         if (!pick) pick = smallest;
     }
+    // Split-K, on request only.  On the decode-like int8 shape (2 x 32 rows,
+    // K 16384, N 7168) it lost to the unsplit 64 x 64 tile (59-64 against
+    // 50-55 us compute-only with 4 parts on the 32 x 256 tile), so the
+    // automatic choice does not split.
+    const bool can_split = opt->scheme == AGG_SCHEME_COUNTERS && opt->workspace_stages == 0 &&
+                           S > 0 && K > 0 && N > 0;
+    const int ks_req = opt->k_splits;
+    s.ks = 1;
+    s.kc = K;
+    if (ks_req > 1) {
+        const int id = pick->id;
+        if (!can_split || (id != 3 && id != 12 && id != 13 && id != kSplitTile))
+            return AGG_E_UNSUPPORTED;
+        if ((int64_t)n_shards * cdiv(S, pick->tm) * cdiv(N, pick->tn) > kMaxSplitTiles)
+            return AGG_E_UNSUPPORTED;
+        s.kc = cdiv(cdiv(K, ks_req), 256) * 256;
+        s.ks = (int)cdiv(K, s.kc);
+    }
     p.shape = *pick;
     s.tm = pick->tm;
     s.tn = pick->tn;
@@ -261,6 +283,11 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     p.M = M;
     p.slot_bytes = slot_bytes(s.ring > 0 ? (int64_t)s.ring * s.tm : S, K, p.elt);
     p.ws_bytes = (size_t)kHeaderBytes + (size_t)(n_shards - 1) * p.slot_bytes;
+    p.part_off = p.ws_bytes;
+    if (s.ks > 1) {
+        // partial sums: every part of every tile, tm x tn values of 4 bytes
+        p.ws_bytes += (size_t)((int64_t)n_shards * s.mt * s.nt * s.ks * s.tm * s.tn * 4);
+    }
     p.drop_chunk = opt->debug_drop_chunk;
     *out = p;
     return AGG_OK;
@@ -332,6 +359,7 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
         info->trace_words = 1 + agg::total_chunks(s) + 3 * agg::total_tiles(s);
         info->workspace_stages = s.ring;
         info->workspace_bytes = (int64_t)p.ws_bytes;
+        info->k_splits = s.ks;
     }
     if (tile_order) {
         int64_t T = agg::total_tiles(s);

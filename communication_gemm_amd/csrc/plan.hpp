@@ -23,6 +23,10 @@ struct TileShape {
     bool auto_pick;
 };
 
+// A tile for split-K: 32 rows x 256 columns, so B is read in 256-element
+// row segments.
+constexpr int kSplitTile = 14;
+
 // Output tiles the consumer kernels are built for, per path.
 const TileShape* tile_shapes(Kind kind, int* count);
 
@@ -39,6 +43,7 @@ struct Plan {
     int64_t M;
     size_t slot_bytes;  // workspace bytes per remote shard (full slot or ring)
     size_t ws_bytes;    // workspace bytes this call needs
+    size_t part_off;    // split-K partial sums: offset in the workspace
     int drop_chunk;
 };
 

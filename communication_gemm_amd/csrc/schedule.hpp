@@ -28,7 +28,8 @@ constexpr int kMaxShards = 64;
 // weighted piece counts; the region keeps 64-bit slots) and, for a
 // bounded workspace, the stage counters (one
 // 64-bit word per source and ring stage: the call's epoch above the number
-// of tiles finished on that stage).  The PTO-ISA README keeps the first
+// of tiles finished on that stage), then the split-K tickets.  The PTO-ISA
+// README keeps the first
 // two structures: per-chunk flags and a per-source summary counter.
 constexpr int kCounterStride = 128;                       // bytes
 constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
@@ -39,7 +40,12 @@ constexpr int kFlagCap = 1024;       // chunks per source the flag matrix holds
 constexpr int kPieceOffset = kFlagOffset + kMaxShards * kFlagCap * 4;
 constexpr int kMaxStages = 8;        // ring stages per source, at most
 constexpr int kStageOffset = kPieceOffset + kMaxShards * kFlagCap * 8;
-constexpr int kHeaderBytes = kStageOffset + kMaxShards * kMaxStages * 8;
+// Split-K tickets: one 32-bit running total per output tile, to which each
+// K part adds its weight (piece_weight over ks parts); the part whose add
+// completes the total sums the parts.
+constexpr int kTicketOffset = kStageOffset + kMaxShards * kMaxStages * 8;
+constexpr int kMaxSplitTiles = 4096;
+constexpr int kHeaderBytes = kTicketOffset + kMaxSplitTiles * 4;
 
 // The producer copies a chunk in pieces, dealt to its waves in send order,
 // so that a chunk is shared by many waves and all of them work on the
@@ -85,6 +91,8 @@ struct Schedule {
                            // >= 1: the barrier scheme, iterations of pv
                            // m-tiles over every shard, each tile waiting
                            // for the whole iteration of every source
+    int ks;                // K parts per output tile (split-K; 1 = none)
+    int64_t kc;            // elements of K per part (a multiple of 256)
 };
 
 constexpr int kXcds = 8;   // XCDs; workgroup b of a grid runs on XCD b % 8
@@ -102,7 +110,7 @@ AGG_HD int need_chunks(const Schedule& s, int m)
 
 AGG_HD int64_t total_tiles(const Schedule& s)
 {
-    return (int64_t)s.n_shards * s.mt * s.nt;
+    return (int64_t)s.n_shards * s.mt * s.ks * s.nt;
 }
 
 AGG_HD int64_t total_chunks(const Schedule& s)
@@ -115,6 +123,7 @@ struct TileRef {
     int m;       // m-tile within the shard
     int n;       // n-tile
     int need;    // counter value to wait for (0 = local, no wait)
+    int kp;      // part of K (split-K; 0 otherwise)
 };
 
 // Consumer position p -> tile.  Local tiles first; then remote tiles in
@@ -143,7 +152,17 @@ AGG_HD TileRef tile_at(const Schedule& s, int64_t p)
         t.m = (int)(m0 + r / s.nt);
         t.n = (int)(r % s.nt);
         t.need = s.n_shards > 1 ? need_chunks(s, (int)(m0 + cm - 1)) : 0;
+        t.kp = 0;   // the barrier scheme runs without split-K
         return t;
+    }
+    // Split-K: part after part, each part's tiles in the order below, so
+    // that the row panels of one part (which read the same B rows) are
+    // neighbours and share an XCD's L2.
+    t.kp = 0;
+    if (s.ks > 1) {
+        const int64_t base = (int64_t)s.n_shards * s.mt * s.nt;
+        t.kp = (int)(p / base);
+        p -= (int64_t)t.kp * base;
     }
     int64_t local_tiles = (int64_t)s.mt * s.nt;
     if (p < local_tiles) {

@@ -169,6 +169,23 @@ typedef struct agg_options {
                                (AGG_E_INVALID) if negative or not a
                                multiple of 8192; a chunk may be cut into at
                                most 2^18 pieces (AGG_E_UNSUPPORTED).        */
+    int k_splits;           /* parts K is cut into per output tile (split-K):
+                               each part's workgroup writes its partial sums
+                               to the workspace and the last to finish adds
+                               the parts in part order, then runs the
+                               epilogue.  0 or 1 = no split (the automatic
+                               choice; on the decode-like shapes measured
+                               the unsplit small tile was faster).  > 1
+                               needs the counters scheme, no workspace
+                               ring, tile 3, 12, 13 or 14 (14: 32 x 256),
+                               and at most 4096 output tiles
+                               (AGG_E_UNSUPPORTED otherwise).  Parts hold a
+                               multiple of 256 of K, so the count used may
+                               be lower (agg_plan_info.k_splits), and the
+                               workspace grows by the partial sums
+                               (agg_plan_info.workspace_bytes).  The sum
+                               order is fixed, so results do not depend on
+                               which part finishes last.                   */
 } agg_options;
 
 /* Fill *opt with the defaults above. */
@@ -300,6 +317,7 @@ typedef struct agg_plan_info {
     int workspace_stages;   /* ring stages per remote shard (0: full slots) */
     int64_t workspace_bytes; /* workspace this call needs (a caller-owned
                                 workspace must be at least this large)     */
+    int k_splits;           /* parts of K per output tile (1: no split-K)   */
 } agg_plan_info;
 
 /*

@@ -234,7 +234,7 @@ def test_empty_problems_are_no_ops():
     ("bf16", 2, 1024, 4096, 4096, 11),
     ("f16", 2, 1024, 2048, 1024, 13),    # 2 x 1024 rows, N = 1024: 64 x 64
     ("i8", 2, 8192, 27392, 4096, 8),
-    ("i8", 2, 32, 16384, 7168, 13),
+    ("i8", 2, 32, 16384, 7168, 13),    # decode-like: 64 x 64, no split
 ])
 def test_automatic_tile(kind, n, S, K, N, tile):
     """The automatic tile: the first of the planner's list (largest first,
@@ -242,6 +242,46 @@ def test_automatic_tile(kind, n, S, K, N, tile):
     256 CUs a tile."""
     info, _, _ = agg.plan(kind, n, n * S, K, N)
     assert info.tile_id == tile
+
+
+def test_split_k_plan():
+    """Split-K on request: K parts of a multiple of 256, every (shard,
+    m-tile, n-tile) once per part, part after part; the workspace grows by
+    the partial sums.  The automatic choice does not split."""
+    auto, _, _ = agg.plan("i8", 2, 64, 16384, 7168)
+    assert auto.k_splits == 1
+    info, tiles, _ = agg.plan("i8", 2, 64, 16384, 7168, 0, agg.options(tile=14, k_splits=4),
+                              orders=True)
+    assert (info.tile_id, info.tile_m, info.tile_n, info.k_splits) == (14, 32, 256, 4)
+    base = 2 * 1 * 28
+    assert info.total_tiles == base * 4
+    plain, _, _ = agg.plan("i8", 2, 64, 16384, 7168, 0, agg.options(k_splits=1))
+    assert plain.k_splits == 1 and plain.tile_id == 13
+    assert info.workspace_bytes == plain.workspace_bytes + base * 4 * 32 * 256 * 4
+    # every (shard, m-tile, n-tile) once per part
+    keys, counts = np.unique(tiles[:, :3], axis=0, return_counts=True)
+    assert len(keys) == base and (counts == 4).all()
+    # part after part; inside a part, the local shard first, with no wait
+    assert (tiles[:28, 0] == 0).all() and (tiles[:28, 3] == 0).all()
+    assert (tiles[28:56, 0] == 1).all() and (tiles[28:56, 3] > 0).all()
+    assert (tiles[56:84, 0] == 0).all()
+    # parts hold multiples of 256 of K: 5000 in 3 parts -> 1792, 1792, 1416
+    info, _, _ = agg.plan("f16", 2, 40, 5000, 1000, 0, agg.options(k_splits=3, tile=13))
+    assert info.k_splits == 3
+    info, _, _ = agg.plan("f16", 2, 40, 600, 1000, 0, agg.options(k_splits=8, tile=13))
+    assert info.k_splits == 3          # ceil(600 / 256) parts of 256
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_splits=-1), agg.AGG_E_INVALID),
+    (dict(k_splits=2, tile=8), agg.AGG_E_UNSUPPORTED),      # big tiles are built without it
+    (dict(k_splits=2, tile=13, scheme=agg.SCHEME_BARRIER), agg.AGG_E_UNSUPPORTED),
+    (dict(k_splits=2, tile=13, workspace_stages=1), agg.AGG_E_UNSUPPORTED),
+])
+def test_split_k_rejected(kw, status):
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 2, 2048, 4096, 512, 0, agg.options(**kw))
+    assert e.value.status == status
 
 
 def test_fp8_plans_only_tiles_built_for_it():

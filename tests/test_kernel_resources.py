@@ -86,7 +86,7 @@ def test_every_consumer_leaves_room_for_the_producer(reports):
     prod_lds = pk.get("LDS Size [bytes/block]", 0)
     assert pk.get("ScratchSize [bytes/lane]", 0) == 0
     table = shape_table()
-    assert len(table) == 46
+    assert len(table) == 50
     for (kind, i), (bm, bn, sb, ns, wm, wn) in table.items():
         r = consumer_report(cons, kind, bm, bn, sb, ns, wm, wn)
         regs = align8(r["VGPRs"]) + align8(r["AGPRs"])
