@@ -490,6 +490,11 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
+    # the ring variant first: its fp16 consumers are the same kernels as the
+    # timed steps', which a kernel trace then finds as their last launches
+    ring = None
+    if not args.no_ring and not args.no_modes and args.mode == "pipelined":
+        ring = run_ring(args, torch, agg, synth)
     case, res, flops, inputs = run_f16(args, torch, agg, synth)
     cons_ms = res["consumer_ms"]
     achieved = flops / (cons_ms * 1e-3) / 1e12 if cons_ms else None
@@ -529,8 +534,11 @@ def main():
         line["fp8"] = run_fp8(args, torch, agg, synth)
     if not args.no_int8:
         line["int8"] = run_i8(args, torch, agg, synth)
-    if not args.no_ring:
-        line["ring"] = run_ring(args, torch, agg, synth)
+    # (run only when the timed mode is pipelined, like the overlap figures:
+    # counter runs serialize kernels, so a pipelined consumer there would
+    # wait out its chunk time-out)
+    if ring is not None:
+        line["ring"] = ring
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
