@@ -14,9 +14,11 @@ size (16 rows, 64 chunks per source), unpaced producer.
 
 Printed: ONE JSON line with the metric (TFLOPS = 2MKN/t), the roofline of the
 consumer kernel (its own average duration, taken with HIP events recorded
-around it on the stream it runs on), the oracle's CPU throughput on a bounded
-sample of the same workload, and the overlap figures (compute-only,
-copy-only, sequential and pipelined times).
+around it on the stream it runs on; also the median and minimum over the
+timed steps), the oracle's CPU throughput on a bounded sample of the same
+workload, the overlap figures (compute-only, copy-only, sequential and
+pipelined times) and the GFX clocks that amd-smi reads while pipelined calls
+keep the GPU busy.
 
 The roofline's "traffic" (HBM bytes per consumer launch) comes from hardware
 counters, which this script cannot read itself: rocprofv3 --pmc runs of
@@ -80,6 +82,8 @@ def parse():
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 workload")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 variant")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 variant")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip reading the GFX clocks with amd-smi under load")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the ring-variant runs (D = 2, 4, 8)")
     ap.add_argument("--no-chunk-sweep", action="store_true",
@@ -172,8 +176,9 @@ def copy_calibration(torch):
                       "expected_write_KiB": COPY_CALIBRATION_BYTES / 1024}), flush=True)
 
 
-def timed(torch, fn, steps, warmup, with_consumer=True):
-    """Run fn(events) warmup+steps times; return (ms per call, consumer ms)."""
+def timed(torch, fn, steps, warmup, with_consumer=True, per_call=None):
+    """Run fn(events) warmup+steps times; return (ms per call, consumer ms).
+    per_call, if a list, receives the consumer's ms of every timed call."""
     for _ in range(warmup):
         fn(None)
     torch.cuda.synchronize()
@@ -196,8 +201,55 @@ def timed(torch, fn, steps, warmup, with_consumer=True):
     total = start.elapsed_time(end) / steps
     cons = None
     if with_consumer:
-        cons = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+        each = [a.elapsed_time(b) for a, b in pairs]
+        cons = float(np.mean(each))
+        if per_call is not None:
+            per_call.extend(each)
     return total, cons
+
+
+def gfx_clocks_under_load(torch, fn, max_s=30.0):
+    """GFX clocks (MHz, one per XCD) read with amd-smi while fn keeps the GPU
+    busy: about a second of calls is queued first (the clocks take some
+    tenths of a second to rise from their idle level), and calls keep being
+    queued until the tool returns.  None without the tool."""
+    import shutil
+    import subprocess
+    import threading
+    tool = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi"
+                                       if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if tool is None:
+        return None
+    out = {}
+
+    def sample():
+        try:
+            out["text"] = subprocess.run([tool, "metric", "--clock", "--json"],
+                                         capture_output=True, text=True, timeout=max_s).stdout
+        except (OSError, subprocess.SubprocessError):
+            out["text"] = ""
+
+    th = threading.Thread(target=sample)
+    t0 = time.time()
+    while time.time() - t0 < 1.0:          # about a second of queued work
+        for _ in range(50):
+            fn(None)
+    th.start()
+    while th.is_alive() and time.time() - t0 < max_s:
+        for _ in range(50):
+            fn(None)
+    th.join()
+    torch.cuda.synchronize()
+    text = out.get("text", "")
+    try:
+        data, _ = json.JSONDecoder().raw_decode(text[text.index("["):])
+        clocks = [v["clk"]["value"] for k, v in data[0]["clock"].items() if k.startswith("gfx_")]
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+    if not clocks:
+        return None
+    return {"mean": round(float(np.mean(clocks)), 1), "min": min(clocks), "max": max(clocks),
+            "xcds": len(clocks), "tool": "amd-smi metric --clock, during pipelined calls"}
 
 
 def run_f16(args, torch, agg, synth):
@@ -269,6 +321,10 @@ def run_f16(args, torch, agg, synth):
         if agg.check():
             raise SystemExit("barrier-scheme runs failed")
         res["barrier_scheme_ms"] = barrier
+    if args.mode == "pipelined" and not args.no_clocks:
+        # before the timed steps, whose launches then stay the consumer
+        # kernel's last ones in a kernel trace
+        res["gfx_clock_mhz"] = gfx_clocks_under_load(torch, call(MODES[args.mode]))
     info, _, _ = agg.plan("f16", case.n_shards, case.M, case.K, case.N, cr,
                           agg.options(tile=args.tile))
     if args.mode == "pipelined":
@@ -289,8 +345,13 @@ def run_f16(args, torch, agg, synth):
             "max_tile_wait_us": round(float(waits.max()) / 100.0, 2),
             "last_release_us": round(float(rel.max() - start) / 100.0, 2) if nc else 0.0,
             "consumer_span_us": round(float(cons[:, 2].max() - start) / 100.0, 2)}
+    each = []
     t_pipe, c_pipe = timed(torch, call(MODES[args.mode]), args.steps, args.warmup,
-                           with_consumer=args.mode != "copy")
+                           with_consumer=args.mode != "copy", per_call=each)
+    if each:
+        res["consumer_ms_median"] = float(np.median(each))
+        res["consumer_ms_min"] = float(np.min(each))
+
     rc = agg.check()
     if rc:
         raise SystemExit(f"{args.mode} run failed: {agg.status_string(rc)}")
