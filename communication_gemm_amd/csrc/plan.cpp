@@ -214,6 +214,9 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.ks = 1;
     s.kc = K;
     if (ks_req > 1) {
+        // at most 64 parts: a tile's parts then span at most 2 MiB (32-bit
+        // offsets in the kernel)
+        if (ks_req > 64) return AGG_E_UNSUPPORTED;
         const int id = pick->id;
         if (!can_split || (id != 3 && id != 12 && id != 13 && id != kSplitTile))
             return AGG_E_UNSUPPORTED;

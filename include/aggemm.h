@@ -178,7 +178,7 @@ typedef struct agg_options {
                                the unsplit small tile was faster).  > 1
                                needs the counters scheme, no workspace
                                ring, tile 3, 12, 13 or 14 (14: 32 x 256),
-                               and at most 4096 output tiles
+                               at most 64 parts and 4096 output tiles
                                (AGG_E_UNSUPPORTED otherwise).  Parts hold a
                                multiple of 256 of K, so the count used may
                                be lower (agg_plan_info.k_splits), and the

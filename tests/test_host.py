@@ -277,6 +277,7 @@ def test_split_k_plan():
     (dict(k_splits=2, tile=8), agg.AGG_E_UNSUPPORTED),      # big tiles are built without it
     (dict(k_splits=2, tile=13, scheme=agg.SCHEME_BARRIER), agg.AGG_E_UNSUPPORTED),
     (dict(k_splits=2, tile=13, workspace_stages=1), agg.AGG_E_UNSUPPORTED),
+    (dict(k_splits=65, tile=13), agg.AGG_E_UNSUPPORTED),
 ])
 def test_split_k_rejected(kw, status):
     with pytest.raises(agg.AggError) as e:
