@@ -6,7 +6,7 @@
 // summary counter; several communication blocks per destination; chunks
 // sent in the order they are consumed).
 //
-// Each chunk is cut into pieces (32 KiB by default); piece q of producer
+// Each chunk is cut into pieces (8-32 KiB, planned); piece q of producer
 // position c is item c * P + q, and wave w of the producer grid copies items
 // w, w + W, w + 2W, ..., so every wave works on the earliest chunks first
 // and chunks complete in about the order they are sent.  Waves run on

@@ -50,9 +50,10 @@ constexpr int kHeaderBytes = kTicketOffset + kMaxSplitTiles * 4;
 // The producer copies a chunk in pieces, dealt to its waves in send order,
 // so that a chunk is shared by many waves and all of them work on the
 // earliest chunks first.  A wave moves 8 KiB per sweep (64 lanes x 8
-// vectors of 16 bytes).  The automatic piece is four sweeps: one-sweep
-// pieces copied slower (one count per sweep, and more waves per chunk to
-// wait for), larger ones made the first chunks land later.
+// vectors of 16 bytes).  The automatic piece is at most four sweeps:
+// one-sweep pieces copied slower on large copies (one count per sweep, and
+// more waves per chunk to wait for), larger ones made the first chunks
+// land later; small copies take smaller pieces so that every wave has one.
 constexpr int kWaveSweepBytes = 8192;
 constexpr int kPieceAuto = 4 * kWaveSweepBytes;
 
