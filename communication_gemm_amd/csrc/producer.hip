@@ -17,8 +17,9 @@
 //     running total; the add that completes the chunk's total is the last;
 //   * that wave stores the call's epoch in the chunk's flag (the chunk flag
 //     matrix);
-//   * it then advances the source's summary counter over every flagged
-//     chunk contiguous with it, in one compare-and-swap.
+//   * the wave then advances the source's summary counter over every
+//     flagged chunk contiguous with it (64 flags per read, one lane each),
+//     in one compare-and-swap.
 // So a counter value c means "chunks 0..c-1 are flagged", and the counter
 // moves as soon as the lowest missing chunk lands, whoever copied it.  The
 // consumer waits on the counter, then reads the flags of the chunks it
@@ -60,25 +61,33 @@ constexpr int kLaneStep = 64 * 16;       // bytes per vector across a wave
 static_assert(kUnroll * kLaneStep == kWaveSweepBytes, "sweep size");
 
 // Advance the summary counter of one source over the flagged chunks that
-// follow it.  Runs on one lane after that lane's own flag store has been
-// performed at device scope.  Two lanes racing: the compare-and-swap lets
-// one win and the other re-read; a flag stored before a lane reads the
-// counter is seen either by that lane or by the lane that moved the
-// counter past the chunk before it.
+// follow it, a wave at a time: lane i reads the flag i places past the
+// counter, and the run of set flags from lane 0 on is how far the counter
+// can move (one memory round trip per 64 flags, where a single lane walking
+// them paid one per flag).  Runs after the wave's own flag store has been
+// performed at device scope.  Two waves racing: the compare-and-swap lets
+// one win and the other re-read; a flag stored before a wave reads the
+// counter is seen either by that wave or by the wave that moved the counter
+// past the chunk before it.
 __device__ void advance(uint32_t* ctr, const uint32_t* flags, uint32_t base, int cps,
-                        uint32_t epoch)
+                        uint32_t epoch, int lane)
 {
     for (;;) {
-        uint32_t cur = load_agent(ctr);
-        int rel = (int)(cur - base);
-        int k = 0;
-        while (rel + k < cps && load_agent(flags + rel + k) == epoch) ++k;
+        const uint32_t cur = __builtin_amdgcn_readfirstlane(load_agent(ctr));
+        const int i = (int)(cur - base) + lane;
+        const bool set = i < cps && load_agent(flags + i) == epoch;
+        const uint64_t run = __builtin_amdgcn_ballot_w64(set);
+        const int k = run == ~0ull ? 64 : __builtin_ctzll(~run);
         if (k == 0) return;
-        uint32_t want = cur;
-        __hip_atomic_compare_exchange_strong(ctr, &want, cur + (uint32_t)k,
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-        // success or not, look again: more chunks may have landed
+        if (lane == 0) {
+            uint32_t want = cur;
+            __hip_atomic_compare_exchange_strong(ctr, &want, cur + (uint32_t)k,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // success or not, look again once the swap is done: more chunks may
+        // have landed
+        __builtin_amdgcn_s_waitcnt(0);
     }
 }
 
@@ -95,9 +104,10 @@ __device__ __forceinline__ void* uniform_ptr(const void* p)
     return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Release chunk c (lane 0 of the wave whose add completed it): wait for the
-// emulated link if paced, stamp, flag, advance the summary counter.
-__device__ void release_chunk(const ProducerArgs& a, int64_t c, uint64_t origin)
+// Release chunk c (the wave whose add completed it): wait for the emulated
+// link if paced, stamp, flag (lane 0), advance the summary counter (the
+// whole wave).
+__device__ void release_chunk(const ProducerArgs& a, int64_t c, uint64_t origin, int lane)
 {
     const ChunkRef r = chunk_at(a.s, c);
     if (a.ticks_per_byte > 0.0) {
@@ -105,20 +115,22 @@ __device__ void release_chunk(const ProducerArgs& a, int64_t c, uint64_t origin)
         const double delta = b * a.ticks_per_byte;
         // a pace slower than the wait limit is a failed call, not a hang
         if (delta > (double)a.limit) {
-            raise_error(a.err, a.epoch);
+            if (lane == 0) raise_error(a.err, a.epoch);
             return;
         }
         wait_until(origin, (uint64_t)delta);
     }
     uint32_t* flags = a.flags + r.shard * kFlagCap;
-    // stamped before the flag, so a consumer that saw the flag started
-    // after this time
-    if (a.trace) a.trace[1 + c] = ticks();
-    __hip_atomic_store(flags + r.j, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+        // stamped before the flag, so a consumer that saw the flag started
+        // after this time
+        if (a.trace) a.trace[1 + c] = ticks();
+        __hip_atomic_store(flags + r.j, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // the flag store is performed before the counter is read
     __builtin_amdgcn_s_waitcnt(0);
     advance(a.counters + r.shard * (kCounterStride / 4), flags, a.base[r.shard], a.s.cps,
-            a.epoch);
+            a.epoch, lane);
 }
 
 }  // namespace
@@ -265,8 +277,10 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
             off += kWaveSweepBytes;
         }
         if (cnt >= 0) {
-            if (lane == 0 && ((old + cnt_w) & (kPieceTotal - 1)) == 0 && cnt != a.drop)
-                release_chunk(a, cnt, origin_sh);
+            // lane 0's add returned the running total before it
+            const uint32_t total = __builtin_amdgcn_readfirstlane(old + cnt_w);
+            if ((total & (kPieceTotal - 1)) == 0 && cnt != a.drop)
+                release_chunk(a, cnt, origin_sh, lane);
             cnt = -1;
         }
         if (pend >= 0) {
