@@ -268,14 +268,20 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (cw < 1) cw = 1;
     // pieces per chunk
     const int64_t chunk_bytes = (int64_t)s.cr * K * elt_bytes(kind);
-    // automatic piece: the copy's bytes over the producer's waves, in whole
-    // sweeps, at most kPieceAuto (small copies then keep every wave busy:
-    // 2 x 1024 rows at K = 2048 ran 39 instead of 41 us pipelined)
+    // Automatic piece, in whole sweeps, between one sweep and kPieceMax.
+    // Pipelined: about kPiecesPerChunk pieces a chunk, so that chunks land
+    // close to their send order (the consumer takes them as they land)
+    // while one chunk's pieces do not all contend for its running total.
+    // Copy-only and sequential calls, where nothing waits for the order:
+    // the copy's bytes over the producer's waves, the best throughput.
     int64_t piece = opt->producer_piece_bytes;
     if (!piece) {
         const int64_t waves = 4 * (int64_t)(opt->producer_wgs ? opt->producer_wgs : num_cus);
-        piece = cdiv(cdiv(chunks * chunk_bytes, waves), kWaveSweepBytes) * kWaveSweepBytes;
-        if (piece > kPieceAuto) piece = kPieceAuto;
+        const int64_t want = opt->mode == AGG_MODE_PIPELINED
+                                 ? cdiv(chunk_bytes, kPiecesPerChunk)
+                                 : cdiv(chunks * chunk_bytes, waves);
+        piece = cdiv(want, kWaveSweepBytes) * kWaveSweepBytes;
+        if (piece > kPieceMax) piece = kPieceMax;
         if (piece < kWaveSweepBytes) piece = kWaveSweepBytes;
     }
     const int64_t ppc64 = chunk_bytes > 0 ? cdiv(chunk_bytes, piece) : 1;

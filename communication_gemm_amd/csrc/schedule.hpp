@@ -50,12 +50,14 @@ constexpr int kHeaderBytes = kTicketOffset + kMaxSplitTiles * 4;
 // The producer copies a chunk in pieces, dealt to its waves in send order,
 // so that a chunk is shared by many waves and all of them work on the
 // earliest chunks first.  A wave moves 8 KiB per sweep (64 lanes x 8
-// vectors of 16 bytes).  The automatic piece is at most four sweeps:
-// one-sweep pieces copied slower on large copies (one count per sweep, and
-// more waves per chunk to wait for), larger ones made the first chunks
-// land later; small copies take smaller pieces so that every wave has one.
+// vectors of 16 bytes).  The planner's automatic piece is between one
+// sweep and kPieceMax: in pipelined calls about kPiecesPerChunk pieces a
+// chunk (chunks then land close to their send order, and one chunk's
+// pieces do not all contend for its running total), in copy-only and
+// sequential calls the copy's bytes over the producer's waves.
 constexpr int kWaveSweepBytes = 8192;
-constexpr int kPieceAuto = 4 * kWaveSweepBytes;
+constexpr int kPieceMax = 8 * kWaveSweepBytes;
+constexpr int kPiecesPerChunk = 4;
 
 // Completion of a chunk without a per-call reset: the pieces of a chunk add
 // weights that sum to kPieceTotal, every weight at least 1, to the chunk's

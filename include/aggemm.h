@@ -163,9 +163,10 @@ typedef struct agg_options {
                                before its flag is published.                 */
     int64_t producer_piece_bytes; /* bytes a producer wave copies before it
                                counts them towards their chunk: a multiple
-                               of 8192; 0 = automatic: the copy's bytes
-                               over the producer's waves, rounded up to
-                               8192, at most 32768.  Smaller pieces
+                               of 8192; 0 = automatic, 8192 to 65536:
+                               pipelined calls about 4 pieces a chunk,
+                               copy-only and sequential calls the copy's
+                               bytes over the producer's waves.  Smaller pieces
                                spread a chunk over more waves, so chunks
                                land closer to their send order.  Invalid
                                (AGG_E_INVALID) if negative or not a
