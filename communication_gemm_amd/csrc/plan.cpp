@@ -277,10 +277,17 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     int64_t piece = opt->producer_piece_bytes;
     if (!piece) {
         const int64_t waves = 4 * (int64_t)(opt->producer_wgs ? opt->producer_wgs : num_cus);
-        const int64_t want = opt->mode == AGG_MODE_PIPELINED
-                                 ? cdiv(chunk_bytes, kPiecesPerChunk)
-                                 : cdiv(chunks * chunk_bytes, waves);
+        const bool pipelined = opt->mode == AGG_MODE_PIPELINED;
+        const int64_t want = pipelined ? cdiv(chunk_bytes, kPiecesPerChunk)
+                                       : cdiv(chunks * chunk_bytes, waves);
         piece = cdiv(want, kWaveSweepBytes) * kWaveSweepBytes;
+        // copy-only and sequential: a power-of-two number of sweeps, which
+        // divides the chunks that are powers of two (no short tail piece)
+        if (!pipelined) {
+            int64_t p2 = kWaveSweepBytes;
+            while (p2 < piece) p2 *= 2;
+            piece = p2;
+        }
         if (piece > kPieceMax) piece = kPieceMax;
         if (piece < kWaveSweepBytes) piece = kWaveSweepBytes;
     }
