@@ -311,7 +311,8 @@ typedef struct agg_plan_info {
     int tile_m, tile_n;     /* consumer output tile */
     int m_tiles_per_shard;  /* ceil(S / tile_m) */
     int n_tiles;            /* ceil(N / tile_n) */
-    int64_t total_tiles;    /* n_shards * m_tiles_per_shard * n_tiles */
+    int64_t total_tiles;    /* n_shards * m_tiles_per_shard * n_tiles
+                               (times k_splits with split-K)             */
     int64_t total_chunks;   /* (n_shards - 1) * chunks_per_source */
     int consumer_wgs;       /* persistent consumer grid */
     int producer_wgs;       /* producer grid */
@@ -328,8 +329,10 @@ typedef struct agg_plan_info {
  *   kind: 0 = fp16 path, 1 = int8 path, 2 = bf16 path, 3 = fp8 path; num_cus: CUs of
  *   the device to plan for (0 = 256).  tile_order (nullable, capacity total_tiles * 4 int32):
  *   per consumer position: shard, m-tile, n-tile, counter value waited for
- *   (0 for the local shard).  chunk_order (nullable, capacity total_chunks
- *   * 2 int32): per producer position: shard, chunk index.
+ *   (0 for the local shard); with split-K the positions run part after
+ *   part, each part's positions in the same order, so each (shard, m-tile,
+ *   n-tile) appears once per part.  chunk_order (nullable, capacity
+ *   total_chunks * 2 int32): per producer position: shard, chunk index.
  */
 int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
                  int chunk_rows, const agg_options *opt, int num_cus,
