@@ -79,15 +79,17 @@ __device__ void advance(uint32_t* ctr, const uint32_t* flags, uint32_t base, int
         const uint64_t run = __builtin_amdgcn_ballot_w64(set);
         const int k = run == ~0ull ? 64 : __builtin_ctzll(~run);
         if (k == 0) return;
+        uint32_t won = 0;
         if (lane == 0) {
             uint32_t want = cur;
-            __hip_atomic_compare_exchange_strong(ctr, &want, cur + (uint32_t)k,
-                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+            won = __hip_atomic_compare_exchange_strong(ctr, &want, cur + (uint32_t)k,
+                                                       __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
         }
-        // success or not, look again once the swap is done: more chunks may
-        // have landed
-        __builtin_amdgcn_s_waitcnt(0);
+        // Done once the counter moved over a run that ended at an unset
+        // flag: whoever sets it advances past it (by the argument above).
+        // Otherwise (a lost swap, or all 64 flags set) look again.
+        if (__builtin_amdgcn_readfirstlane(won) && k < 64) return;
     }
 }
 
