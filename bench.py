@@ -178,12 +178,20 @@ def copy_calibration(torch):
 
 def timed(torch, fn, steps, warmup, with_consumer=True, per_call=None):
     """Run fn(events) warmup+steps times; return (ms per call, consumer ms).
-    per_call, if a list, receives the consumer's ms of every timed call."""
+
+    The consumer's time comes from a pair of HIP events that the library
+    records on its stream around the consumer launch, in one timed call of
+    every max(1, steps // 20).  Recorded around every call, the pairs made
+    the pipelined C4 step about 9 us (3%) longer than the same calls
+    without them, so the step time is not made to carry them on every
+    call.  per_call, if a list, receives the consumer's ms of every
+    bracketed call."""
     for _ in range(warmup):
         fn(None)
     torch.cuda.synchronize()
+    stride = max(1, steps // 20)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(steps)] if with_consumer else [None] * steps
+             if with_consumer and i % stride == 0 else None for i in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     # torch creates an event's HIP handle at its first record; do that now so
@@ -201,7 +209,7 @@ def timed(torch, fn, steps, warmup, with_consumer=True, per_call=None):
     total = start.elapsed_time(end) / steps
     cons = None
     if with_consumer:
-        each = [a.elapsed_time(b) for a, b in pairs]
+        each = [pr[0].elapsed_time(pr[1]) for pr in pairs if pr is not None]
         cons = float(np.mean(each))
         if per_call is not None:
             per_call.extend(each)
@@ -287,8 +295,25 @@ def run_f16(args, torch, agg, synth):
         t_copy, _ = timed(torch, call(agg.MODE_COPY_ONLY), n, 10, with_consumer=False)
         t_comp, c_comp = timed(torch, call(agg.MODE_COMPUTE_ONLY), n, 10)
         t_seq, _ = timed(torch, call(agg.MODE_SEQUENTIAL), n, 10)
+        # the four modes again, interleaved in short runs: the board's
+        # clocks drift with its load over a run of several seconds, so runs
+        # taken next to each other compare the modes more fairly than the
+        # blocks above and the timed steps at the end
+        inter = {"compute": [], "copy": [], "sequential": [], "pipelined": []}
+        for _ in range(5):
+            for name in inter:
+                t, _ = timed(torch, call(MODES[name]), 20, 2, with_consumer=False)
+                inter[name].append(t)
         if agg.check():
             raise SystemExit("mode runs failed")
+        mi = {k: float(np.median(v)) for k, v in inter.items()}
+        res["interleaved"] = {
+            **{f"{k}_ms": round(v, 5) for k, v in mi.items()},
+            "hidden_fraction": round((mi["compute"] + mi["copy"] - mi["pipelined"]) / mi["copy"], 4),
+            "overlap_eff": round((mi["sequential"] - mi["pipelined"])
+                                 / min(mi["copy"], mi["compute"]), 4),
+            "speedup_vs_sequential": round(mi["sequential"] / mi["pipelined"], 4),
+            "note": "medians of 5 rounds of 20 calls per mode, the modes taken in turn"}
     if modes and not args.no_chunk_sweep:
         # pipelined step time over chunk sizes (16 to 256 rows; 16 is the
         # automatic size here), each after its own warm-up
