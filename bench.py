@@ -12,13 +12,20 @@ Workload (default): fp16 x fp16 -> fp32, 8 shards of 1024 rows, M=8192,
 K=4096, N=4096, A and B ~ N(0,1) from the seeded generator, automatic chunk
 size (16 rows, 64 chunks per source), unpaced producer.
 
+Order of the run: the timed steps come first (after about 0.3 s of untimed
+calls that bring the clocks out of idle, then W warm-up steps), so that no
+earlier measurement has heated the board; then every workload's entry
+(C1-C5: pipelined steps and the four modes taken in turn), the variants,
+the ring runs, the vendor-GEMM reference and, last, the same pipelined
+steps again after all of that ("sustained").
+
 Printed: ONE JSON line with the metric (TFLOPS = 2MKN/t), the roofline of the
 consumer kernel (its own average duration, taken with HIP events recorded
-around it on the stream it runs on; also the median and minimum over the
-timed steps), the oracle's CPU throughput on a bounded sample of the same
-workload, the overlap figures (compute-only, copy-only, sequential and
-pipelined times) and the GFX clocks that amd-smi reads while pipelined calls
-keep the GPU busy.
+around every fifth timed launch on the stream it runs on; also the median
+and minimum), the oracle's CPU throughput on a bounded sample of the same
+workload (plus one-thread rates on C1-C3), the overlap figures of every
+workload and the GFX clocks that amd-smi reads while pipelined calls keep
+the GPU busy.
 
 The roofline's "traffic" (HBM bytes per consumer launch) comes from hardware
 counters, which this script cannot read itself: rocprofv3 --pmc runs of
@@ -33,8 +40,8 @@ Helpers for those runs:
                                             and kernel, from rocprofv3 CSVs
     python bench.py --trace-summary DIR     per-kernel durations from a
                                             rocprofv3 kernel trace, over all
-                                            dispatches and over the last
-                                            --steps ones (the timed steps)
+                                            dispatches and over the first
+                                            --steps ones after --skip
 """
 from __future__ import annotations
 
@@ -78,7 +85,8 @@ def parse():
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--link-gbps", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-modes", action="store_true", help="skip the overlap modes")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="only the timed steps (and the CPU baseline)")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 workload")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 variant")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 variant")
@@ -89,6 +97,10 @@ def parse():
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip the pipelined chunk-size sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ramp-calls", type=int, default=1000,
+                    help="untimed calls before the warm-up that bring the clocks out of idle")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="--trace-summary: dispatches of each kernel before the timed ones")
     ap.add_argument("--mode", choices=sorted(MODES), default="pipelined",
                     help="mode of the timed calls; hardware-counter runs use 'compute' "
                          "because counter collection serializes the two kernels")
@@ -140,11 +152,12 @@ def pmc_summary(root):
         print(f"{ctr:16s} {s / n:18.1f}  dispatches={n:4d}  {kern}")
 
 
-def trace_summary(root, last):
+def trace_summary(root, steps, skip=0):
     """Per-kernel dispatch durations from rocprofv3's kernel_trace CSV: all
-    dispatches, and the last `last` ones of each kernel (in dispatch order,
-    which for the default run are the timed pipelined steps of the fp16
-    kernels)."""
+    dispatches, and the `steps` dispatches of each kernel that follow its
+    first `skip` (in dispatch order; for the default run, the timed steps of
+    the timed workload's consumer come after --ramp-calls + --warmup of
+    its launches)."""
     rows = []
     for path in sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"),
                                  recursive=True)):
@@ -157,10 +170,11 @@ def trace_summary(root, last):
     for _, name, ns in rows:
         by.setdefault(name, []).append(ns)
     for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        tail = d[-last:]
+        part = d[skip:skip + steps] or d[-steps:]
         print(f"{len(d):5d} dispatches  mean {np.mean(d) / 1e3:9.1f} us  "
-              f"last {len(tail)}: mean {np.mean(tail) / 1e3:9.1f} us  "
-              f"min {min(tail) / 1e3:8.1f}  max {max(tail) / 1e3:8.1f}  {name[:110]}")
+              f"[{skip}, {skip + len(part)}): mean {np.mean(part) / 1e3:9.1f} us  "
+              f"median {np.median(part) / 1e3:8.1f}  min {min(part) / 1e3:8.1f}  "
+              f"max {max(part) / 1e3:8.1f}  {name[:110]}")
 
 
 def copy_calibration(torch):
@@ -176,34 +190,38 @@ def copy_calibration(torch):
                       "expected_write_KiB": COPY_CALIBRATION_BYTES / 1024}), flush=True)
 
 
-def timed(torch, fn, steps, warmup, with_consumer=True, per_call=None):
-    """Run fn(events) warmup+steps times; return (ms per call, consumer ms).
+TIMED_STRIDE = 5     # one timed call in five carries a consumer event pair
 
-    The consumer's time comes from a pair of HIP events that the library
-    records on its stream around the consumer launch, in one timed call of
-    every max(1, steps // 20).  Recorded around every call, the pairs made
-    the pipelined C4 step about 9 us (3%) longer than the same calls
-    without them, so the step time is not made to carry them on every
-    call.  per_call, if a list, receives the consumer's ms of every
-    bracketed call."""
+
+def timed(torch, make, steps, warmup, with_consumer=True, per_call=None):
+    """Run `warmup` untimed calls, then time `steps` calls back to back.
+
+    make(events) returns a zero-argument call; events is None or a pair of
+    torch events that the library records around the consumer launch, on
+    the stream the consumer runs on.  One timed call in TIMED_STRIDE (the
+    first of every five) carries a pair: recorded around every call, the
+    pairs made the pipelined C4 step about 9 us (3%) longer.  Returns (ms
+    per call, mean consumer ms or None); per_call, if a list, receives the
+    consumer ms of every bracketed call."""
+    plain = make(None)
     for _ in range(warmup):
-        fn(None)
+        plain()
     torch.cuda.synchronize()
-    stride = max(1, steps // 20)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             if with_consumer and i % stride == 0 else None for i in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+             if with_consumer and i % TIMED_STRIDE == 0 else None for i in range(steps)]
     # torch creates an event's HIP handle at its first record; do that now so
     # the library can record the consumer pairs itself
     for pr in pairs:
         if pr is not None:
             pr[0].record()
             pr[1].record()
+    calls = [plain if pr is None else make(pr) for pr in pairs]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(steps):
-        fn(pairs[i])
+    for c in calls:
+        c()
     end.record()
     torch.cuda.synchronize()
     total = start.elapsed_time(end) / steps
@@ -216,9 +234,64 @@ def timed(torch, fn, steps, warmup, with_consumer=True, per_call=None):
     return total, cons
 
 
-def gfx_clocks_under_load(torch, fn, max_s=30.0):
-    """GFX clocks (MHz, one per XCD) read with amd-smi while fn keeps the GPU
-    busy: about a second of calls is queued first (the clocks take some
+def ramp(torch, call, calls=0, seconds=0.0):
+    """Untimed calls that bring the clocks out of their idle state (after a
+    pause, such as the host drawing a workload's inputs, the first tens of
+    calls run at lower clocks): `calls` of them, or as many as take about
+    `seconds`."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < calls or (seconds > 0 and time.perf_counter() - t0 < seconds):
+        call()
+        i += 1
+        if i % 100 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def interleaved(torch, calls, rounds=5, n=20):
+    """The four modes taken in turn: `rounds` rounds of `n` calls of each
+    mode, then the medians.  Runs taken next to each other compare the
+    modes more fairly than long blocks, over which the board's clocks drift
+    with its load.  Hidden fraction, overlap efficiency and speedup follow
+    the readings of the PTO-ISA README's benchmark output (it prints an
+    "overlap eff" without a formula)."""
+    inter = {"compute": [], "copy": [], "sequential": [], "pipelined": []}
+    for _ in range(rounds):
+        for name in inter:
+            t, _ = timed(torch, lambda ev, c=calls[name]: c, n, 2, with_consumer=False)
+            inter[name].append(t)
+    mi = {k: float(np.median(v)) for k, v in inter.items()}
+    return {**{f"{k}_ms": round(v, 5) for k, v in mi.items()},
+            "hidden_fraction": round((mi["compute"] + mi["copy"] - mi["pipelined"]) / mi["copy"], 4),
+            "overlap_eff": round((mi["sequential"] - mi["pipelined"])
+                                 / min(mi["copy"], mi["compute"]), 4),
+            "speedup_vs_sequential": round(mi["sequential"] / mi["pipelined"], 4),
+            "note": f"medians of {rounds} rounds of {n} calls per mode, the modes taken in turn"}
+
+
+def device_trace(torch, agg, call_with_trace, info):
+    """One pipelined call with the device trace on: how long consumer tiles
+    waited for chunks and when the last chunk landed."""
+    trace = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
+    call_with_trace(trace)
+    if agg.check():
+        raise SystemExit("traced run failed")
+    tr = trace.cpu().numpy().view(np.uint64).astype(np.float64)
+    nc = info.total_chunks
+    start, rel, cons = tr[0], tr[1:1 + nc], tr[1 + nc:].reshape(-1, 3)
+    waits = cons[:, 1] - cons[:, 0]
+    return {
+        "tile_wait_share": round(float(waits.sum() / (cons[:, 2] - cons[:, 0]).sum()), 4),
+        "mean_tile_wait_us": round(float(waits.mean()) / 100.0, 2),
+        "max_tile_wait_us": round(float(waits.max()) / 100.0, 2),
+        "last_release_us": round(float(rel.max() - start) / 100.0, 2) if nc else 0.0,
+        "consumer_span_us": round(float(cons[:, 2].max() - start) / 100.0, 2)}
+
+
+def gfx_clocks_under_load(torch, call, max_s=30.0):
+    """GFX clocks (MHz, one per XCD) read with amd-smi while `call` keeps the
+    GPU busy: about a second of calls is queued first (the clocks take some
     tenths of a second to rise from their idle level), and calls keep being
     queued until the tool returns.  None without the tool."""
     import shutil
@@ -241,11 +314,11 @@ def gfx_clocks_under_load(torch, fn, max_s=30.0):
     t0 = time.time()
     while time.time() - t0 < 1.0:          # about a second of queued work
         for _ in range(50):
-            fn(None)
+            call()
     th.start()
     while th.is_alive() and time.time() - t0 < max_s:
         for _ in range(50):
-            fn(None)
+            call()
     th.join()
     torch.cuda.synchronize()
     text = out.get("text", "")
@@ -260,143 +333,118 @@ def gfx_clocks_under_load(torch, fn, max_s=30.0):
             "xcds": len(clocks), "tool": "amd-smi metric --clock, during pipelined calls"}
 
 
-def run_f16(args, torch, agg, synth):
-    case = synth.CASES[args.case]
-    if case.kind != "f16":
-        raise SystemExit("--case must name an fp16 workload")
-    shards, B = synth.make_case(case)
-    ts = [torch.from_numpy(s).cuda() for s in shards]
-    tB = torch.from_numpy(B).cuda()
-    C = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
-    wsb = agg.workspace_bytes(case.n_shards, case.M, case.K, 2)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    agg.workspace_reset(ws)
-    gbps = case.link_gbps if args.link_gbps is None else args.link_gbps
-    cr = args.chunk_rows or case.chunk_rows
+class F16Workload:
+    """One fp16 workload on the device: inputs, output, a caller-owned
+    workspace (nothing is allocated inside timed loops) and prepared calls
+    in every mode."""
 
-    def call(mode):
-        def fn(ev):
-            o = agg.options(workspace=ws, mode=mode, link_gbps=gbps, tile=args.tile,
-                            consumer_events=ev)
-            agg.ag_gemm_f16(ts, tB, C, cr, opts=o)
-        return fn
+    def __init__(self, torch, agg, case, inputs, tile=0, link_gbps=None, chunk_rows=None):
+        self.torch, self.agg, self.case = torch, agg, case
+        shards, B = inputs
+        self.ts = [torch.from_numpy(x).cuda() for x in shards]
+        self.tB = torch.from_numpy(B).cuda()
+        self.C = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(agg.workspace_bytes(case.n_shards, case.M, case.K, 2),
+                              dtype=torch.uint8, device="cuda")
+        agg.workspace_reset(self.ws)
+        self.tile = tile
+        self.gbps = case.link_gbps if link_gbps is None else link_gbps
+        self.cr = case.chunk_rows if chunk_rows is None else chunk_rows
+        self.calls = {name: self.prep(mode) for name, mode in MODES.items()}
+        # the remote slots get the real rows before anything reads them (a
+        # compute-only call on an unwritten workspace multiplies whatever it
+        # holds, often zeros, which draws less power and runs faster)
+        self.calls["copy"]()
+        torch.cuda.synchronize()
 
-    flops = 2.0 * case.M * case.K * case.N
-    res = {}
-    # The remote slots get the real rows before anything reads them (a
-    # compute-only call on an unwritten workspace multiplies whatever it
-    # holds, often zeros, which draws less power and runs faster).
-    timed(torch, call(agg.MODE_COPY_ONLY), 1, 0, with_consumer=False)
-    modes = not args.no_modes and args.mode == "pipelined"
-    if modes:
-        # the mode measurements run first and so also bring the clocks to
-        # their loaded steady state before the timed steps
-        n = max(args.steps, 50)
-        t_copy, _ = timed(torch, call(agg.MODE_COPY_ONLY), n, 10, with_consumer=False)
-        t_comp, c_comp = timed(torch, call(agg.MODE_COMPUTE_ONLY), n, 10)
-        t_seq, _ = timed(torch, call(agg.MODE_SEQUENTIAL), n, 10)
-        # the four modes again, interleaved in short runs: the board's
-        # clocks drift with its load over a run of several seconds, so runs
-        # taken next to each other compare the modes more fairly than the
-        # blocks above and the timed steps at the end
-        inter = {"compute": [], "copy": [], "sequential": [], "pipelined": []}
-        for _ in range(5):
-            for name in inter:
-                t, _ = timed(torch, call(MODES[name]), 20, 2, with_consumer=False)
-                inter[name].append(t)
-        if agg.check():
-            raise SystemExit("mode runs failed")
-        mi = {k: float(np.median(v)) for k, v in inter.items()}
-        res["interleaved"] = {
-            **{f"{k}_ms": round(v, 5) for k, v in mi.items()},
-            "hidden_fraction": round((mi["compute"] + mi["copy"] - mi["pipelined"]) / mi["copy"], 4),
-            "overlap_eff": round((mi["sequential"] - mi["pipelined"])
-                                 / min(mi["copy"], mi["compute"]), 4),
-            "speedup_vs_sequential": round(mi["sequential"] / mi["pipelined"], 4),
-            "note": "medians of 5 rounds of 20 calls per mode, the modes taken in turn"}
-    if modes and not args.no_chunk_sweep:
-        # pipelined step time over chunk sizes (16 to 256 rows; 16 is the
-        # automatic size here), each after its own warm-up
-        sweep = {}
-        for rows in (16, 32, 64, 128, 256):
-            if rows > case.shard_rows:
-                continue
+    def prep(self, mode, ev=None, chunk_rows=None, **kw):
+        o = dict(workspace=self.ws, mode=mode, link_gbps=self.gbps, tile=self.tile,
+                 consumer_events=ev)
+        o.update(kw)
+        return self.agg.ag_gemm_f16(
+            self.ts, self.tB, self.C, self.cr if chunk_rows is None else chunk_rows,
+            opts=self.agg.options(**o), prepare=True)
 
-            def fn(ev, rows=rows):
-                agg.ag_gemm_f16(ts, tB, C, rows, opts=agg.options(
-                    workspace=ws, link_gbps=gbps, tile=args.tile))
-            t, _ = timed(torch, fn, max(20, args.steps // 2), 10, with_consumer=False)
-            sweep[str(rows)] = round(t, 5)
-        if agg.check():
-            raise SystemExit("chunk sweep failed")
-        res["chunk_sweep_ms"] = sweep
-    if modes and not args.no_chunk_sweep:
-        # the comparison scheme: a barrier per iteration of pvalue row panels
-        # over every shard (no local-first, no per-source counters), with
-        # full workspace slots or double-buffered panels
-        barrier = {}
-        for name, kw in (("pvalue1", dict(pvalue=1)), ("pvalue2", dict(pvalue=2)),
-                         ("pvalue1_stages2", dict(pvalue=1, workspace_stages=2))):
-            def fn(ev, kw=kw):
-                agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(
-                    workspace=ws, link_gbps=gbps, tile=args.tile,
-                    scheme=agg.SCHEME_BARRIER, **kw))
-            t, _ = timed(torch, fn, max(20, args.steps // 2), 10, with_consumer=False)
-            barrier[name] = round(t, 5)
-        if agg.check():
-            raise SystemExit("barrier-scheme runs failed")
-        res["barrier_scheme_ms"] = barrier
-    if args.mode == "pipelined" and not args.no_clocks:
-        # before the timed steps, whose launches then stay the consumer
-        # kernel's last ones in a kernel trace
-        res["gfx_clock_mhz"] = gfx_clocks_under_load(torch, call(MODES[args.mode]))
-    info, _, _ = agg.plan("f16", case.n_shards, case.M, case.K, case.N, cr,
-                          agg.options(tile=args.tile))
-    if args.mode == "pipelined":
-        # one pipelined call, untimed, with the device trace on: how long
-        # consumer tiles waited for chunks and when the last landed
-        trace = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
-        agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(workspace=ws, link_gbps=gbps,
-                                                         tile=args.tile, trace=trace))
-        if agg.check():
-            raise SystemExit("traced run failed")
-        tr = trace.cpu().numpy().view(np.uint64).astype(np.float64)
-        nc = info.total_chunks
-        start, rel, cons = tr[0], tr[1:1 + nc], tr[1 + nc:].reshape(-1, 3)
-        waits = cons[:, 1] - cons[:, 0]
-        res["trace"] = {
-            "tile_wait_share": round(float(waits.sum() / (cons[:, 2] - cons[:, 0]).sum()), 4),
-            "mean_tile_wait_us": round(float(waits.mean()) / 100.0, 2),
-            "max_tile_wait_us": round(float(waits.max()) / 100.0, 2),
-            "last_release_us": round(float(rel.max() - start) / 100.0, 2) if nc else 0.0,
-            "consumer_span_us": round(float(cons[:, 2].max() - start) / 100.0, 2)}
-    each = []
-    t_pipe, c_pipe = timed(torch, call(MODES[args.mode]), args.steps, args.warmup,
-                           with_consumer=args.mode != "copy", per_call=each)
-    if each:
-        res["consumer_ms_median"] = float(np.median(each))
-        res["consumer_ms_min"] = float(np.min(each))
+    @property
+    def flops(self):
+        return 2.0 * self.case.M * self.case.K * self.case.N
 
-    rc = agg.check()
-    if rc:
-        raise SystemExit(f"{args.mode} run failed: {agg.status_string(rc)}")
-    res["step_ms"] = t_pipe
-    res["consumer_ms"] = c_pipe
-    if modes:
-        res.update(compute_only_ms=t_comp, compute_only_consumer_ms=c_comp,
-                   copy_only_ms=t_copy, sequential_ms=t_seq)
-        # hidden share of the copy, overlap efficiency and speedup (the page
-        # prints "overlap eff" without a formula; these are the readings)
-        res["hidden_fraction"] = (t_comp + t_copy - t_pipe) / t_copy
-        res["overlap_eff"] = (t_seq - t_pipe) / min(t_copy, t_comp)
-        res["speedup_vs_sequential"] = t_seq / t_pipe
-        copied = (case.n_shards - 1) * case.shard_rows * case.K * 2
-        res["copy_only_GBps"] = 2 * copied / (t_copy * 1e-3) / 1e9
-    res["tile"] = [info.tile_m, info.tile_n]
-    res["tile_id"] = info.tile_id
-    res["chunk_rows"] = info.chunk_rows
-    res["tflops"] = flops / (t_pipe * 1e-3) / 1e12
-    return case, res, flops, (shards, B)
+    def plan(self):
+        info, _, _ = self.agg.plan("f16", self.case.n_shards, self.case.M, self.case.K,
+                                   self.case.N, self.cr, self.agg.options(tile=self.tile))
+        return info
+
+    def entry(self, steps, warmup=10, trace=False, timed_steps=None):
+        """Pipelined steps (with the consumer's own time) and the four modes
+        taken in turn.  timed_steps: (ms per step, consumer ms) measured
+        already, in place of new pipelined steps."""
+        torch, agg = self.torch, self.agg
+        if timed_steps is None:
+            ramp(torch, self.calls["pipelined"], seconds=0.3)
+            t, c = timed(torch, lambda ev: self.prep(MODES["pipelined"], ev), steps, warmup)
+        else:
+            t, c = timed_steps
+        inter = interleaved(torch, self.calls)
+        info = self.plan()
+        out = {"workload": self.case.name, "chunk_rows": info.chunk_rows,
+               "tile": [info.tile_m, info.tile_n], "tile_id": info.tile_id,
+               "link_gbps": self.gbps, "pipelined_ms": round(t, 5),
+               "tflops": round(self.flops / (t * 1e-3) / 1e12, 2),
+               "consumer_ms": round(c, 5),
+               "consumer_tflops": round(self.flops / (c * 1e-3) / 1e12, 2),
+               "consumer_frac_of_peak": round(self.flops / (c * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+               "interleaved": inter}
+        if trace:
+            out["trace"] = device_trace(torch, agg, lambda tr: self.prep(
+                MODES["pipelined"], trace=tr)(), info)
+        if agg.check():
+            raise SystemExit(f"{self.case.name} runs failed")
+        return out
+
+
+class I8Workload:
+    """The int8 + dequant workload, as F16Workload."""
+
+    def __init__(self, torch, agg, case, inputs):
+        self.torch, self.agg, self.case = torch, agg, case
+        shards, B, bias, scale = inputs
+        self.ts = [torch.from_numpy(x).cuda() for x in shards]
+        self.tB = torch.from_numpy(B).cuda()
+        self.tb = torch.from_numpy(bias).cuda()
+        self.tsc = torch.from_numpy(scale).cuda()
+        self.C = torch.empty((case.M, case.N), dtype=torch.float16, device="cuda")
+        self.ws = torch.empty(agg.workspace_bytes(case.n_shards, case.M, case.K, 1),
+                              dtype=torch.uint8, device="cuda")
+        agg.workspace_reset(self.ws)
+        self.calls = {name: self.prep(mode) for name, mode in MODES.items()}
+        self.calls["copy"]()
+        torch.cuda.synchronize()
+
+    def prep(self, mode, ev=None):
+        return self.agg.ag_gemm_i8_dequant(
+            self.ts, self.tB, self.tb, self.tsc, self.C, 0,
+            opts=self.agg.options(workspace=self.ws, mode=mode, consumer_events=ev), prepare=True)
+
+    def entry(self, steps, warmup=10):
+        torch, agg, case = self.torch, self.agg, self.case
+        ops = 2.0 * case.M * case.K * case.N
+        ramp(torch, self.calls["pipelined"], seconds=0.3)
+        t, c = timed(torch, lambda ev: self.prep(MODES["pipelined"], ev), steps, warmup)
+        tc, cc = timed(torch, lambda ev: self.prep(MODES["compute"], ev), steps, warmup)
+        inter = interleaved(torch, self.calls, rounds=3, n=10)
+        if agg.check():
+            raise SystemExit("int8 runs failed")
+        info, _, _ = agg.plan("i8", case.n_shards, case.M, case.K, case.N, 0)
+        return {"workload": case.name, "chunk_rows": info.chunk_rows,
+                "tile": [info.tile_m, info.tile_n], "tile_id": info.tile_id,
+                "pipelined_ms": round(t, 5), "tops": round(ops / (t * 1e-3) / 1e12, 2),
+                "consumer_ms": round(c, 5),
+                "consumer_tops": round(ops / (c * 1e-3) / 1e12, 2),
+                "consumer_frac_of_peak": round(ops / (c * 1e-3) / 1e12 / PEAK_I8_TOPS, 4),
+                "compute_only_consumer_ms": round(cc, 5),
+                "compute_only_consumer_frac_of_peak":
+                    round(ops / (cc * 1e-3) / 1e12 / PEAK_I8_TOPS, 4),
+                "interleaved": inter}
 
 
 # Pallas:MGPU collective matmul page: per-device (1024 D) x 4096 x 4096 fp16
@@ -418,147 +466,154 @@ def run_ring(args, torch, agg, synth):
     n = max(20, args.steps // 2)
     for D in (2, 4, 8):
         M, K, N = 1024 * D, 4096, 4096
-        shards, B = synth.make_f16(M, K, N, D, "normal", 90000 + D)
-        ts = [torch.from_numpy(x).cuda() for x in shards]
-        tB = torch.from_numpy(B).cuda()
-        del shards, B
-        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        ws = torch.empty(agg.workspace_bytes(D, M, K, 2), dtype=torch.uint8, device="cuda")
-        agg.workspace_reset(ws)
+        case = synth.Case(90 + D, "f16", D, M, K, N)
+        w = F16Workload(torch, agg, case, synth.make_f16(M, K, N, D, "normal", 90000 + D))
 
-        def timed_call(**kw):
-            def fn(ev):
-                agg.ag_gemm_f16(ts, tB, C, 0, opts=agg.options(workspace=ws, **kw))
-            return round(timed(torch, fn, n, 10, with_consumer=False)[0] * 1e3, 1)
+        ramp(torch, w.calls["pipelined"], seconds=0.2)
 
-        timed_call(mode=agg.MODE_COPY_ONLY)
+        def us(**kw):
+            mode = kw.pop("mode", MODES["pipelined"])
+            return round(timed(torch, lambda ev: w.prep(mode, **kw), n, 10,
+                               with_consumer=False)[0] * 1e3, 1)
+
         r = {"workload": f"f16 {D}x1024 rows M={M} K={K} N={N}, ring order, one serial link",
-             "ring_us": timed_call(link_model=agg.LINKS_SERIAL),
-             "copy_then_gemm_us": timed_call(link_model=agg.LINKS_SERIAL, mode=agg.MODE_SEQUENTIAL),
-             "compute_only_us": timed_call(mode=agg.MODE_COMPUTE_ONLY),
-             "ring_xgmi_paced_us": timed_call(link_model=agg.LINKS_SERIAL,
-                                              link_gbps=XGMI_LINK_GBPS),
-             "mesh_xgmi_paced_us": timed_call(link_model=agg.LINKS_PARALLEL,
-                                              link_gbps=XGMI_LINK_GBPS)}
+             "ring_us": us(link_model=agg.LINKS_SERIAL),
+             "copy_then_gemm_us": us(link_model=agg.LINKS_SERIAL, mode=MODES["sequential"]),
+             "compute_only_us": us(mode=MODES["compute"]),
+             "ring_xgmi_paced_us": us(link_model=agg.LINKS_SERIAL, link_gbps=XGMI_LINK_GBPS),
+             "mesh_xgmi_paced_us": us(link_model=agg.LINKS_PARALLEL, link_gbps=XGMI_LINK_GBPS)}
         if agg.check():
             raise SystemExit("ring runs failed")
         r["tflops"] = round(2.0 * M * K * N / (r["ring_us"] * 1e-6) / 1e12, 1)
         page = PAGE_RING_US[D]
         r["page_h100_us"] = {"ring": page[0], "model_bound": page[1], "allgather_then_matmul": page[2]}
         out[str(D)] = r
-        del ts, tB, C, ws
+        del w
     return out
 
 
-def run_i8(args, torch, agg, synth):
-    case = synth.CASES[5]
-    shards, B, bias, scale = synth.make_case(case)
-    ts = [torch.from_numpy(s).cuda() for s in shards]
-    tB = torch.from_numpy(B).cuda()
-    tb = torch.from_numpy(bias).cuda()
-    tsc = torch.from_numpy(scale).cuda()
-    del shards, B
-    C = torch.empty((case.M, case.N), dtype=torch.float16, device="cuda")
-    ws = torch.empty(agg.workspace_bytes(2, case.M, case.K, 1), dtype=torch.uint8, device="cuda")
-    agg.workspace_reset(ws)
-    mode = MODES[args.mode]
-
-    def fn(ev, mode=mode):
-        agg.ag_gemm_i8_dequant(ts, tB, tb, tsc, C, 0,
-                               opts=agg.options(workspace=ws, mode=mode, consumer_events=ev))
-    if args.mode != "pipelined":
-        # the remote slot holds the real rows before a compute-only call
-        # reads it (as in the fp16 workload)
-        fn(None, agg.MODE_COPY_ONLY)
-    t, c = timed(torch, fn, max(10, args.steps // 4), 10, with_consumer=args.mode != "copy")
-    rc = agg.check()
-    if rc:
-        raise SystemExit(f"int8 run failed: {agg.status_string(rc)}")
-    ops = 2.0 * case.M * case.K * case.N
-    res = {"workload": case.name, "mode": args.mode, "ms": t, "tops": ops / (t * 1e-3) / 1e12}
-    if c is not None:
-        res.update(consumer_ms=c, consumer_tops=ops / (c * 1e-3) / 1e12,
-                   frac_of_peak=ops / (c * 1e-3) / 1e12 / PEAK_I8_TOPS)
-    return res
-
-
-def run_bf16(args, torch, agg, synth):
-    """The bf16 variant on the same 8 x 1024-row workload, pipelined."""
+def run_variant(args, torch, agg, synth, kind):
+    """The bf16 or fp8 (E4M3) variant on the 8 x 1024-row fp16 workload's
+    shape, pipelined."""
     case = synth.CASES[args.case]
-    shards, B = synth.make_bf16(case.M, case.K, case.N, case.n_shards, "normal",
-                                1000 * case.case_id)
+    if kind == "bf16":
+        shards, B = synth.make_bf16(case.M, case.K, case.N, case.n_shards, "normal",
+                                    1000 * case.case_id)
 
-    def bdev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(
-            torch.bfloat16)
-    ts = [bdev(s) for s in shards]
-    tB = bdev(B)
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(
+                torch.bfloat16)
+        fn, elt, peak = agg.ag_gemm_bf16, 2, PEAK_F16_TFLOPS
+    else:
+        shards, B = synth.make_fp8(case.M, case.K, case.N, case.n_shards, "normal",
+                                   1000 * case.case_id)
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        fn, elt, peak = agg.ag_gemm_fp8, 1, PEAK_FP8_TFLOPS
+    ts = [dev(x) for x in shards]
+    tB = dev(B)
     C = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
-    ws = torch.empty(agg.workspace_bytes(case.n_shards, case.M, case.K, 2), dtype=torch.uint8,
+    ws = torch.empty(agg.workspace_bytes(case.n_shards, case.M, case.K, elt), dtype=torch.uint8,
                      device="cuda")
     agg.workspace_reset(ws)
-
-    def fn(ev):
-        agg.ag_gemm_bf16(ts, tB, C, 0, opts=agg.options(workspace=ws, consumer_events=ev))
-    t, c = timed(torch, fn, max(20, args.steps // 2), 20)
+    def make(ev):
+        return fn(ts, tB, C, 0, opts=agg.options(workspace=ws, consumer_events=ev), prepare=True)
+    ramp(torch, make(None), seconds=0.3)
+    t, c = timed(torch, make, max(20, args.steps // 2), 20)
     if agg.check():
-        raise SystemExit("bf16 run failed")
+        raise SystemExit(f"{kind} run failed")
     flops = 2.0 * case.M * case.K * case.N
-    return {"workload": case.name.replace("f16", "bf16", 1), "ms": t, "consumer_ms": c,
-            "tflops": flops / (t * 1e-3) / 1e12,
-            "consumer_tflops": flops / (c * 1e-3) / 1e12}
+    return {"workload": case.name.replace("f16", kind, 1), "ms": round(t, 5),
+            "consumer_ms": round(c, 5), "tflops": round(flops / (t * 1e-3) / 1e12, 2),
+            "consumer_tflops": round(flops / (c * 1e-3) / 1e12, 2),
+            "consumer_frac_of_peak": round(flops / (c * 1e-3) / 1e12 / peak, 4)}
 
 
-def run_fp8(args, torch, agg, synth):
-    """The fp8 (E4M3) variant on the same 8 x 1024-row workload, pipelined."""
-    case = synth.CASES[args.case]
-    shards, B = synth.make_fp8(case.M, case.K, case.N, case.n_shards, "normal",
-                               1000 * case.case_id)
-    ts = [torch.from_numpy(s).cuda() for s in shards]
-    tB = torch.from_numpy(B).cuda()
-    C = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
-    ws = torch.empty(agg.workspace_bytes(case.n_shards, case.M, case.K, 1), dtype=torch.uint8,
-                     device="cuda")
-    agg.workspace_reset(ws)
-
-    def fn(ev):
-        agg.ag_gemm_fp8(ts, tB, C, 0, opts=agg.options(workspace=ws, consumer_events=ev))
-    t, c = timed(torch, fn, max(20, args.steps // 2), 20)
-    if agg.check():
-        raise SystemExit("fp8 run failed")
-    flops = 2.0 * case.M * case.K * case.N
-    return {"workload": case.name.replace("f16", "fp8", 1), "ms": t, "consumer_ms": c,
-            "tflops": flops / (t * 1e-3) / 1e12,
-            "consumer_tflops": flops / (c * 1e-3) / 1e12,
-            "frac_of_peak": flops / (c * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+def vendor_gemm(torch, w, steps=50):
+    """hipBLASLt (torch.matmul) on the gathered A of the same workload, fp16
+    in and fp16 out (torch has no fp32-output fp16 GEMM): a ceiling
+    reference for the plain local GEMM, with no gather."""
+    A = torch.cat(w.ts, 0)
+    out = torch.empty((A.shape[0], w.tB.shape[1]), dtype=torch.float16, device="cuda")
+    ramp(torch, lambda: torch.matmul(A, w.tB, out=out), seconds=0.3)
+    t, _ = timed(torch, lambda ev: (lambda: torch.matmul(A, w.tB, out=out)), steps, 10,
+                 with_consumer=False)
+    return {"what": "torch.matmul (hipBLASLt), fp16 in, fp16 out, the whole gathered A",
+            "ms": round(t, 5), "tflops": round(w.flops / (t * 1e-3) / 1e12, 2)}
 
 
-def cpu_baseline(case, inputs, budget_s):
-    """The oracle, as it stands, on a bounded sample of the workload's rows."""
-    import oracle
-    shards, B = inputs
-    rows_all = np.arange(case.M, dtype=np.int64)
-    rng = np.random.default_rng(0)
-    # two probes separate the per-call cost (converting B) from the per-row
-    # cost, so the sample can be sized to the time budget
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_rate(oracle, fn, M, K, N, budget_s, seed=0):
+    """The oracle on a bounded sample of rows, sized to about budget_s
+    seconds: (rows, seconds, GFLOP/s)."""
+    rng = np.random.default_rng(seed)
+    rows_all = np.arange(M, dtype=np.int64)
     probe_t = []
-    for k in (16, 128):
-        probe = rng.choice(rows_all, k, replace=False)
+    for k in (8, 32):
+        k = min(k, M)
         t0 = time.perf_counter()
-        oracle.ag_gemm_f16(shards, B, rows=probe, with_abs=False)
-        probe_t.append(time.perf_counter() - t0)
-    per_row = max((probe_t[1] - probe_t[0]) / 112, 1e-7)
-    fixed = max(probe_t[0] - 16 * per_row, 0.0)
-    n = int(min(case.M, max(16, (budget_s - fixed) / per_row)))
+        fn(np.sort(rng.choice(rows_all, k, replace=False)))
+        probe_t.append((k, time.perf_counter() - t0))
+    (k0, t0_), (k1, t1_) = probe_t
+    per_row = max((t1_ - t0_) / max(k1 - k0, 1), 1e-7)
+    n = int(min(M, max(8, budget_s / per_row)))
     rows = np.sort(rng.choice(rows_all, n, replace=False))
     t0 = time.perf_counter()
-    oracle.ag_gemm_f16(shards, B, rows=rows, with_abs=False)
+    fn(rows)
     dt = time.perf_counter() - t0
-    flops = 2.0 * n * case.K * case.N
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": oracle.threads_used(),
-            "kind": "oracle",
-            "sample": f"{n} of {case.M} rows of C ({flops / 1e9:.1f} GFLOP, fp64 "
-                      f"accumulation) in {dt:.1f} s"}
+    return n, dt, 2.0 * n * K * N / dt / 1e9
+
+
+def cpu_baseline(case, inputs, budget_s, synth, i8_inputs=None):
+    """The oracle, as it stands, on a bounded sample of the timed workload's
+    rows on every host thread; beside it the same on C1-C3 (and C5) with
+    every thread and with one."""
+    import oracle
+    shards, B = inputs
+    n, dt, gflops = oracle_rate(oracle, lambda r: oracle.ag_gemm_f16(shards, B, rows=r,
+                                                                      with_abs=False),
+                                case.M, case.K, case.N, budget_s)
+    out = {"value": round(gflops / 1e3, 5), "unit": "TFLOPS", "cores": oracle.threads_used(),
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"{n} of {case.M} rows of C ({2.0 * n * case.K * case.N / 1e9:.1f} GFLOP, "
+                     f"fp64 accumulation) in {dt:.1f} s"}
+    per = {}
+    for threads in (0, 1):
+        prev = oracle.set_threads(1) if threads == 1 else None
+        try:
+            for cid in (1, 2, 3):
+                c = synth.CASES[cid]
+                sh, Bc = synth.make_case(c)
+                rn, rdt, rg = oracle_rate(oracle, lambda r: oracle.ag_gemm_f16(
+                    sh, Bc, rows=r, with_abs=False), c.M, c.K, c.N, 0.5 if threads else 1.0)
+                per.setdefault(f"C{cid}", {})["one_thread" if threads else "all_threads"] = {
+                    "rows": rn, "of_rows": c.M, "seconds": round(rdt, 3),
+                    "gflops": round(rg, 3), "full_config_s": round(rdt * c.M / rn, 3)}
+        finally:
+            if prev is not None:
+                oracle.set_threads(prev)
+    if i8_inputs is not None:
+        c = synth.CASES[5]
+        sh, Bc, bias, scale = i8_inputs
+        rn, rdt, rg = oracle_rate(oracle, lambda r: oracle.ag_gemm_i8_dequant(
+            sh, Bc, bias, scale, rows=r), c.M, c.K, c.N, 2.0)
+        per["C5"] = {"all_threads": {"rows": rn, "of_rows": c.M, "seconds": round(rdt, 3),
+                                     "gops": round(rg, 3), "full_config_s": round(rdt * c.M / rn, 2)}}
+    out["per_config"] = per
+    out["note"] = ("all_threads: every host thread (OpenMP over output rows); one_thread: one; "
+                   "full_config_s scales the sample to every row of the workload")
+    return out
 
 
 def main():
@@ -567,7 +622,7 @@ def main():
         pmc_summary(args.pmc_summary)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.steps)
+        trace_summary(args.trace_summary, args.steps, args.skip)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the streamed "
@@ -583,57 +638,123 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
-    # the ring variant first: its fp16 consumers are the same kernels as the
-    # timed steps', which a kernel trace then finds as their last launches
-    ring = None
-    if not args.no_ring and not args.no_modes and args.mode == "pipelined":
-        ring = run_ring(args, torch, agg, synth)
-    case, res, flops, inputs = run_f16(args, torch, agg, synth)
-    cons_ms = res["consumer_ms"]
-    achieved = flops / (cons_ms * 1e-3) / 1e12 if cons_ms else None
+    case = synth.CASES[args.case]
+    if case.kind != "f16":
+        raise SystemExit("--case must name an fp16 workload")
+    inputs = synth.make_case(case)
+    w = F16Workload(torch, agg, case, inputs, tile=args.tile,
+                    link_gbps=args.link_gbps, chunk_rows=args.chunk_rows or None)
+    mode = MODES[args.mode]
+    if args.mode == "compute":
+        w.calls["copy"]()
+
+    # 1. The timed steps: clocks out of idle, W warm-up steps, K steps.
+    ramp(torch, w.prep(mode), calls=args.ramp_calls)
+    each = []
+    t_step, c_step = timed(torch, lambda ev: w.prep(mode, ev), args.steps, args.warmup,
+                           with_consumer=args.mode != "copy", per_call=each)
+    rc = agg.check()
+    if rc:
+        raise SystemExit(f"{args.mode} run failed: {agg.status_string(rc)}")
+    info = w.plan()
+    tflops = w.flops / (t_step * 1e-3) / 1e12
+    overlap = {"step_ms": round(t_step, 5)}
+    if each:
+        overlap.update(consumer_ms=round(c_step, 5), consumer_ms_median=round(float(np.median(each)), 5),
+                       consumer_ms_min=round(float(np.min(each)), 5),
+                       consumer_launches_timed=len(each))
     line = {
         "metric": METRIC,
-        "value": round(res["tflops"], 2),
+        "value": round(tflops, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["step_ms"], 5),
+        "ms_per_step": round(t_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(res["tflops"] / PAGE_TFLOPS_8192, 3) if case.case_id == 4 else None,
+        "vs_baseline": round(tflops / PAGE_TFLOPS_8192, 3) if case.case_id == 4 else None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": case.name + " streamed AllGather+GEMM, fp16 in, fp32 out",
                    "M": case.M, "K": case.K, "N": case.N, "n_shards": case.n_shards,
-                   "chunk_rows": res["chunk_rows"], "tile": res["tile"],
-                   "tile_id": res["tile_id"],
-                   "link_gbps": case.link_gbps if args.link_gbps is None else args.link_gbps,
+                   "chunk_rows": info.chunk_rows, "tile": [info.tile_m, info.tile_n],
+                   "tile_id": info.tile_id, "link_gbps": w.gbps,
                    "mode": args.mode, "parallelism": "single GPU, shards emulated"},
-        "frac_of_peak": round(res["tflops"] / PEAK_F16_TFLOPS, 4),
-        "roofline": None if achieved is None else {
-            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+        "frac_of_peak": round(tflops / PEAK_F16_TFLOPS, 4),
+        "roofline": None if not each else {
+            "bound": "mfma", "achieved": round(w.flops / (c_step * 1e-3) / 1e12, 2),
+            "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(w.flops / (c_step * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
             "traffic": stored_traffic(case.name) if args.tile == 0 else None,
-            "kernel": "consumer (persistent MFMA GEMM)", "kernel_ms": round(cons_ms, 5)},
-        "overlap": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()
-                    if k not in ("tflops", "tile", "tile_id", "chunk_rows")},
+            "kernel": "consumer (persistent MFMA GEMM)", "kernel_ms": round(c_step, 5)},
+        "overlap": overlap,
         "baseline_note": "vs_baseline divides by the PTO-ISA page's 8-card 8192x4096x4096 "
                          "figure on Ascend 910B1 (191.03 TFLOPS): other hardware, context only",
     }
-    if not args.no_bf16:
-        line["bf16"] = run_bf16(args, torch, agg, synth)
-    if not args.no_fp8:
-        line["fp8"] = run_fp8(args, torch, agg, synth)
-    if not args.no_int8:
-        line["int8"] = run_i8(args, torch, agg, synth)
-    # (run only when the timed mode is pipelined, like the overlap figures:
-    # counter runs serialize kernels, so a pipelined consumer there would
-    # wait out its chunk time-out)
-    if ring is not None:
-        line["ring"] = ring
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, inputs, args.cpu_seconds)
+    full = args.mode == "pipelined" and not args.no_modes
+    if full:
+        # 2. The timed workload's own figures: the four modes in turn, the
+        # device trace, the chunk-size sweep, the comparison scheme, clocks.
+        c4 = w.entry(max(20, args.steps), trace=True, timed_steps=(t_step, c_step))
+        overlap["interleaved"] = c4["interleaved"]
+        overlap["trace"] = c4["trace"]
+        if not args.no_chunk_sweep:
+            sweep = {}
+            for rows in (16, 32, 64, 128, 256):
+                if rows <= case.shard_rows:
+                    t, _ = timed(torch, lambda ev, r=rows: w.prep(MODES["pipelined"], chunk_rows=r),
+                                 max(20, args.steps // 2), 10, with_consumer=False)
+                    sweep[str(rows)] = round(t, 5)
+            barrier = {}
+            for name, kw in (("pvalue1", dict(pvalue=1)), ("pvalue2", dict(pvalue=2)),
+                             ("pvalue1_stages2", dict(pvalue=1, workspace_stages=2))):
+                t, _ = timed(torch, lambda ev, kw=kw: w.prep(
+                    MODES["pipelined"], scheme=agg.SCHEME_BARRIER, **kw),
+                    max(20, args.steps // 2), 10, with_consumer=False)
+                barrier[name] = round(t, 5)
+            if agg.check():
+                raise SystemExit("sweeps failed")
+            overlap["chunk_sweep_ms"] = sweep
+            overlap["barrier_scheme_ms"] = barrier
+        if not args.no_clocks:
+            overlap["gfx_clock_mhz"] = gfx_clocks_under_load(torch, w.calls["pipelined"])
+        # 3. Every workload's entry: C1-C3 (C3 with its paced producer), the
+        # timed one, and the int8 C5.
+        configs = {}
+        for cid in (1, 2, 3):
+            c = synth.CASES[cid]
+            cw = F16Workload(torch, agg, c, synth.make_case(c))
+            configs[f"C{cid}"] = cw.entry(max(50, args.steps), trace=cid == 3)
+            del cw
+        configs[f"C{case.case_id}"] = {k: v for k, v in c4.items() if k != "trace"}
+        i8_inputs = None
+        if not args.no_int8:
+            i8_inputs = synth.make_case(5)
+            iw = I8Workload(torch, agg, synth.CASES[5], i8_inputs)
+            configs["C5"] = iw.entry(max(10, args.steps // 2))
+            del iw
+        line["configs"] = configs
+        if not args.no_bf16:
+            line["bf16"] = run_variant(args, torch, agg, synth, "bf16")
+        if not args.no_fp8:
+            line["fp8"] = run_variant(args, torch, agg, synth, "fp8")
+        if not args.no_ring:
+            line["ring"] = run_ring(args, torch, agg, synth)
+        line["vendor_gemm"] = vendor_gemm(torch, w)
+        # 4. The timed steps again, after everything above has loaded the
+        # board for tens of seconds.
+        ramp(torch, w.calls["pipelined"], seconds=0.3)
+        t2, c2 = timed(torch, lambda ev: w.prep(mode, ev), args.steps, args.warmup)
+        if agg.check():
+            raise SystemExit("sustained run failed")
+        overlap["sustained"] = {"step_ms": round(t2, 5), "consumer_ms": round(c2, 5),
+                                "tflops": round(w.flops / (t2 * 1e-3) / 1e12, 2),
+                                "note": "the timed steps repeated at the end of the run"}
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(case, inputs, args.cpu_seconds, synth, i8_inputs)
+    elif not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, inputs, args.cpu_seconds, synth)
     print(json.dumps(line), flush=True)
 
 

@@ -158,6 +158,36 @@ def _raise(status: int, what: str):
         raise AggError(status, what)
 
 
+class Prepared:
+    """One call with its arguments marshalled once: each call of this object
+    only crosses the C ABI (tight loops pay no Python-side checks).  It keeps
+    the ctypes arguments and the options alive; the caller keeps the tensors
+    alive."""
+
+    __slots__ = ("_fn", "_args", "_what", "_keep")
+
+    def __init__(self, fn, args, what, keep):
+        self._fn = fn
+        self._args = tuple(args)
+        self._what = what
+        self._keep = keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc:
+            raise AggError(rc, self._what)
+
+
+def _invoke(plain, ex, args, opts, what, prepare):
+    """Call (or, with prepare=True, return a Prepared call of) the plain or
+    the _ex entry point with marshalled arguments."""
+    fn = plain if opts is None else ex
+    full = tuple(args) if opts is None else tuple(args) + (ctypes.byref(opts),)
+    if prepare:
+        return Prepared(fn, full, what, (args, opts))
+    _raise(fn(*full), what)
+
+
 def options(**kw) -> Options:
     """An agg_options with the library's defaults, then ``kw`` applied.
 
@@ -178,6 +208,10 @@ def options(**kw) -> Options:
             o.consumer_events[0] = ctypes.c_void_p(v[0].cuda_event)
             o.consumer_events[1] = ctypes.c_void_p(v[1].cuda_event)
         elif k in ("acc_out", "workspace", "trace"):
+            if hasattr(v, "data_ptr"):
+                if not v.is_cuda or not v.is_contiguous():
+                    raise ValueError(f"{k} must be a contiguous CUDA tensor")
+                _on_current_device(v)
             setattr(o, k, v.data_ptr() if hasattr(v, "data_ptr") else int(v))
             if k == "workspace" and hasattr(v, "numel"):
                 o.workspace_bytes = v.numel() * v.element_size()
@@ -194,6 +228,16 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _on_current_device(*tensors):
+    """Every tensor lives on the current device (the library launches there
+    and takes the pointers as that device's)."""
+    import torch
+    cur = torch.cuda.current_device()
+    for t in tensors:
+        if t is not None and t.device.index != cur:
+            raise ValueError(f"tensor on {t.device}, but the current device is cuda:{cur}")
+
+
 def _shard_ptrs(shards, dtype, K):
     import torch
     if not shards:
@@ -206,52 +250,61 @@ def _shard_ptrs(shards, dtype, K):
             raise ValueError(f"shards must be contiguous 2-D {dtype} CUDA tensors")
         if tuple(t.shape) != (S, K):
             raise ValueError("all shards must be S x K")
+    _on_current_device(*shards)
     return (ctypes.c_void_p * len(shards))(*[t.data_ptr() for t in shards]), S
 
 
 def _check_out(C, shape, dtype):
     if C.dtype != dtype or not C.is_cuda or not C.is_contiguous() or tuple(C.shape) != shape:
         raise ValueError(f"output must be a contiguous {dtype} CUDA tensor of shape {shape}")
+    _on_current_device(C)
 
 
-def ag_gemm_f16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None):
-    """C[M, N] (fp32) = concat(shards)[M, K] (fp16) x B[K, N] (fp16)."""
+def _check_vec(v, n, dtype, what):
+    """A contiguous (n,) vector of `dtype` on the current device: a strided
+    view would be read as if it were contiguous."""
+    if v.dtype != dtype or tuple(v.shape) != (n,) or not v.is_cuda or not v.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {dtype} CUDA tensor of shape ({n},)")
+    _on_current_device(v)
+
+
+def ag_gemm_f16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None,
+                prepare: bool = False):
+    """C[M, N] (fp32) = concat(shards)[M, K] (fp16) x B[K, N] (fp16).
+
+    With prepare=True nothing runs: the call is returned as a Prepared
+    object (arguments checked and marshalled once) to be called later."""
     import torch
     if B.dtype != torch.float16 or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
         raise ValueError("B must be a contiguous 2-D fp16 CUDA tensor")
     K, N = B.shape
+    _on_current_device(B)
     table, S = _shard_ptrs(shards, torch.float16, K)
     M = S * len(shards)
     _check_out(C, (M, N), torch.float32)
     st = _stream_handle(stream)
-    if opts is None:
-        rc = lib.ag_gemm_f16(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
-                             int(chunk_rows), st)
-    else:
-        rc = lib.ag_gemm_f16_ex(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
-                                int(chunk_rows), st, ctypes.byref(opts))
-    _raise(rc, "ag_gemm_f16")
-    return C
+    r = _invoke(lib.ag_gemm_f16, lib.ag_gemm_f16_ex,
+                (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st),
+                opts, "ag_gemm_f16", prepare)
+    return r if prepare else C
 
 
-def ag_gemm_bf16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None):
+def ag_gemm_bf16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None,
+                 prepare: bool = False):
     """C[M, N] (fp32) = concat(shards)[M, K] (bf16) x B[K, N] (bf16)."""
     import torch
     if B.dtype != torch.bfloat16 or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
         raise ValueError("B must be a contiguous 2-D bf16 CUDA tensor")
     K, N = B.shape
+    _on_current_device(B)
     table, S = _shard_ptrs(shards, torch.bfloat16, K)
     M = S * len(shards)
     _check_out(C, (M, N), torch.float32)
     st = _stream_handle(stream)
-    if opts is None:
-        rc = lib.ag_gemm_bf16(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
-                              int(chunk_rows), st)
-    else:
-        rc = lib.ag_gemm_bf16_ex(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
-                                 int(chunk_rows), st, ctypes.byref(opts))
-    _raise(rc, "ag_gemm_bf16")
-    return C
+    r = _invoke(lib.ag_gemm_bf16, lib.ag_gemm_bf16_ex,
+                (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st),
+                opts, "ag_gemm_bf16", prepare)
+    return r if prepare else C
 
 
 def _fp8_dtypes():
@@ -259,7 +312,8 @@ def _fp8_dtypes():
     return (torch.uint8, torch.float8_e4m3fn)
 
 
-def ag_gemm_fp8(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None):
+def ag_gemm_fp8(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None,
+                prepare: bool = False):
     """C[M, N] (fp32) = concat(shards)[M, K] (fp8 E4M3) x B[K, N] (fp8 E4M3).
 
     Shards and B are torch.float8_e4m3fn tensors, or uint8 tensors holding
@@ -269,45 +323,36 @@ def ag_gemm_fp8(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | 
     if dt not in _fp8_dtypes() or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
         raise ValueError("B must be a contiguous 2-D float8_e4m3fn (or uint8) CUDA tensor")
     K, N = B.shape
+    _on_current_device(B)
     table, S = _shard_ptrs(shards, dt, K)
     M = S * len(shards)
     _check_out(C, (M, N), torch.float32)
     st = _stream_handle(stream)
-    if opts is None:
-        rc = lib.ag_gemm_fp8(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
-                             int(chunk_rows), st)
-    else:
-        rc = lib.ag_gemm_fp8_ex(table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N,
-                                int(chunk_rows), st, ctypes.byref(opts))
-    _raise(rc, "ag_gemm_fp8")
-    return C
+    r = _invoke(lib.ag_gemm_fp8, lib.ag_gemm_fp8_ex,
+                (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st),
+                opts, "ag_gemm_fp8", prepare)
+    return r if prepare else C
 
 
 def ag_gemm_i8_dequant(shards, B, bias, scale, C, chunk_rows: int = 0, stream=None,
-                       opts: Options | None = None):
+                       opts: Options | None = None, prepare: bool = False):
     """C[M, N] (fp16) = fp16(fp32(concat(shards) x B + bias) * scale)."""
     import torch
     if B.dtype != torch.int8 or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
         raise ValueError("B must be a contiguous 2-D int8 CUDA tensor")
     K, N = B.shape
+    _on_current_device(B)
     table, S = _shard_ptrs(shards, torch.int8, K)
     M = S * len(shards)
-    if bias.dtype != torch.int32 or tuple(bias.shape) != (N,) or not bias.is_cuda:
-        raise ValueError("bias must be an int32 CUDA tensor of shape (N,)")
-    if scale.dtype != torch.float32 or tuple(scale.shape) != (N,) or not scale.is_cuda:
-        raise ValueError("scale must be a float32 CUDA tensor of shape (N,)")
+    _check_vec(bias, N, torch.int32, "bias")
+    _check_vec(scale, N, torch.float32, "scale")
     _check_out(C, (M, N), torch.float16)
     st = _stream_handle(stream)
-    if opts is None:
-        rc = lib.ag_gemm_i8_dequant(table, len(shards), B.data_ptr(), bias.data_ptr(),
-                                    scale.data_ptr(), C.data_ptr(), M, K, N,
-                                    int(chunk_rows), st)
-    else:
-        rc = lib.ag_gemm_i8_dequant_ex(table, len(shards), B.data_ptr(), bias.data_ptr(),
-                                       scale.data_ptr(), C.data_ptr(), M, K, N,
-                                       int(chunk_rows), st, ctypes.byref(opts))
-    _raise(rc, "ag_gemm_i8_dequant")
-    return C
+    r = _invoke(lib.ag_gemm_i8_dequant, lib.ag_gemm_i8_dequant_ex,
+                (table, len(shards), B.data_ptr(), bias.data_ptr(), scale.data_ptr(),
+                 C.data_ptr(), M, K, N, int(chunk_rows), st),
+                opts, "ag_gemm_i8_dequant", prepare)
+    return r if prepare else C
 
 
 def pick_chunk_rows(shard_rows: int) -> int:

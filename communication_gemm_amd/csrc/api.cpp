@@ -28,8 +28,9 @@ struct Track {
 };
 
 struct Device {
-    bool ready = false;
-    int num_cus = 0;
+    bool ready = false;        // side stream and events made
+    int id = 0;
+    int num_cus = 0;           // 0 until the attributes were read
     double clock_hz = 0;       // rate of the device's constant clock
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr;  // orders a ring-mode producer after the consumer
@@ -45,29 +46,145 @@ std::map<void*, Track> g_user_ws;   // caller-owned workspaces, by address
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int device_state(Device** out)
+// Bound of a pipelined producer's wait for its consumer to start: the work
+// queued ahead of a call on the caller's stream may take long, and a call
+// must not fail for it (the chunk waits keep the call's own limit).
+constexpr double kStartWaitSeconds = 120.0;
+
+// The device's entry with its CU count and clock rate (attribute queries
+// only: nothing is created or enqueued, so argument errors can still be
+// reported before any side effect).
+int device_entry(Device** out)
 {
     int id = 0;
     if (hipGetDevice(&id) != hipSuccess) return AGG_E_HIP;
     Device& d = g_dev[id];
-    if (!d.ready) {
+    if (!d.num_cus) {
         int cus = 0, khz = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess)
             return AGG_E_HIP;
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, id) != hipSuccess)
             return AGG_E_HIP;
-        if (hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) != hipSuccess)
-            return AGG_E_HIP;
-        if (hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess)
-            return AGG_E_HIP;
-        d.num_cus = cus;
+        d.num_cus = cus > 0 ? cus : 256;
         d.clock_hz = (khz > 0 ? khz : 100000) * 1000.0;
-        memset(&d.track, 0, sizeof d.track);
-        d.track.device = id;
-        d.ready = true;
+        d.id = id;
     }
     *out = &d;
     return AGG_OK;
+}
+
+// The side stream and the events of a device, made on first use.
+int device_ready(Device& d)
+{
+    if (d.ready) return AGG_OK;
+    if (hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) != hipSuccess)
+        return AGG_E_HIP;
+    if (hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess)
+        return AGG_E_HIP;
+    memset(&d.track, 0, sizeof d.track);
+    d.track.device = d.id;
+    d.ready = true;
+    return AGG_OK;
+}
+
+int device_state(Device** out)
+{
+    int rc = device_entry(out);
+    if (rc) return rc;
+    return device_ready(**out);
+}
+
+// The side stream must not run a producer before a header reset queued on
+// `st` has run: the producer polls words of the header (start word, error
+// word, counters) that hold stale values until then.  One event, once per
+// reset (a one-time preparation, so its cross-stream cost does not recur).
+int order_side_after(Device& d, hipStream_t st)
+{
+    if (hipEventRecord(d.fork, st) != hipSuccess) return AGG_E_HIP;
+    if (hipStreamWaitEvent(d.side, d.fork, 0) != hipSuccess) return AGG_E_HIP;
+    return AGG_OK;
+}
+
+// ---- plan cache --------------------------------------------------------
+//
+// A call's plan depends only on its sizes, the options that shape the
+// schedule and the device's CU count; calls in a loop repeat the same
+// ones, so the last few plans are kept (looked up under the library lock).
+struct PlanKey {
+    int kind, n, chunk_rows, num_cus;
+    int64_t M, K, N;
+    uint32_t struct_size;
+    int local_shard, mode, link_model, producer_wgs, consumer_wgs, tile;
+    int workspace_stages, scheme, pvalue, k_splits, debug_drop_chunk;
+    double link_gbps, timeout_ms;
+    int64_t piece;
+    int has_order;
+    int order[kMaxShards];
+};
+
+struct PlanSlot {
+    bool used;
+    PlanKey key;
+    int rc;
+    Plan plan;
+};
+
+constexpr int kPlanSlots = 8;
+PlanSlot g_plans[kPlanSlots];
+int g_plan_next = 0;
+
+void plan_key(PlanKey* k, Kind kind, int n, int64_t M, int64_t K, int64_t N, int chunk_rows,
+              const agg_options* o, int num_cus)
+{
+    memset(k, 0, sizeof *k);   // padding bytes take part in the comparison
+    k->kind = (int)kind;
+    k->n = n;
+    k->chunk_rows = chunk_rows;
+    k->num_cus = num_cus;
+    k->M = M;
+    k->K = K;
+    k->N = N;
+    k->struct_size = o->struct_size;
+    k->local_shard = o->local_shard;
+    k->mode = o->mode;
+    k->link_model = o->link_model;
+    k->producer_wgs = o->producer_wgs;
+    k->consumer_wgs = o->consumer_wgs;
+    k->tile = o->tile;
+    k->workspace_stages = o->workspace_stages;
+    k->scheme = o->scheme;
+    k->pvalue = o->pvalue;
+    k->k_splits = o->k_splits;
+    k->debug_drop_chunk = o->debug_drop_chunk;
+    k->link_gbps = o->link_gbps;
+    k->timeout_ms = o->timeout_ms;
+    k->piece = o->producer_piece_bytes;
+    k->has_order = o->send_order != nullptr;
+    if (o->send_order && n > 1 && n <= kMaxShards)
+        for (int i = 0; i + 1 < n; ++i) k->order[i] = o->send_order[i];
+}
+
+// The plan of a call (made, or found among the last few); a positive
+// status for invalid arguments.
+int cached_plan(Kind kind, int n, int64_t M, int64_t K, int64_t N, int chunk_rows,
+                const agg_options* o, int num_cus, const Plan** out)
+{
+    PlanKey k;
+    plan_key(&k, kind, n, M, K, N, chunk_rows, o, num_cus);
+    for (int i = 0; i < kPlanSlots; ++i) {
+        PlanSlot& sl = g_plans[i];
+        if (sl.used && memcmp(&sl.key, &k, sizeof k) == 0) {
+            *out = &sl.plan;
+            return sl.rc;
+        }
+    }
+    PlanSlot& sl = g_plans[g_plan_next];
+    g_plan_next = (g_plan_next + 1) % kPlanSlots;
+    sl.used = true;
+    sl.key = k;
+    sl.rc = make_plan(kind, n, M, K, N, chunk_rows, o, num_cus, &sl.plan);
+    *out = &sl.plan;
+    return sl.rc;
 }
 
 int occupancy(Device& d, int kind, int tile)
@@ -97,6 +214,10 @@ int internal_workspace(Device& d, size_t need, hipStream_t st, char** ws, Track*
         d.ws_bytes = bytes;
         if (launch_header_reset(reinterpret_cast<uint32_t*>(d.ws), kHeaderBytes, st) != hipSuccess)
             return AGG_E_HIP;
+        // fresh memory holds anything: no producer may look at the header
+        // before the reset has run
+        int rc = order_side_after(d, st);
+        if (rc) return rc;
         uint32_t keep = d.track.epoch;
         memset(&d.track, 0, sizeof d.track);
         d.track.epoch = keep;
@@ -151,17 +272,21 @@ int run(const Call& c)
     }
     if (opt->trace && !aligned(opt->trace, 8)) return AGG_E_UNSUPPORTED;
 
-    // every argument check runs before the first HIP call
-    Plan p;
-    int rc = make_plan(c.kind, c.n, c.M, c.K, c.N, c.chunk_rows, opt, 0, &p);
-    if (rc) return rc;
-    if (empty) return AGG_OK;   // nothing to compute or move
-
+    // Every argument check runs before anything is created or enqueued:
+    // the plan needs only the device's attributes (and argument errors are
+    // reported even where no device can be queried: the plan then assumes
+    // 256 CUs).
     std::lock_guard<std::mutex> lock(g_mu);
     Device* d = nullptr;
-    rc = device_state(&d);
+    const int drc = device_entry(&d);
+    const Plan* pp = nullptr;
+    int rc = cached_plan(c.kind, c.n, c.M, c.K, c.N, c.chunk_rows, opt,
+                         drc == AGG_OK ? d->num_cus : 0, &pp);
     if (rc) return rc;
-    rc = make_plan(c.kind, c.n, c.M, c.K, c.N, c.chunk_rows, opt, d->num_cus, &p);
+    const Plan& p = *pp;
+    if (empty) return AGG_OK;   // nothing to compute or move
+    if (drc) return drc;
+    rc = device_ready(*d);
     if (rc) return rc;
 
     const int kind = static_cast<int>(c.kind);
@@ -232,6 +357,10 @@ int run(const Call& c)
     pa.drop = p.drop_chunk;
     pa.ticks_per_byte = p.link_gbps > 0 ? d->clock_hz / (p.link_gbps * 1e9) : 0.0;
     pa.limit = limit;
+    // the producer's wait for the consumer's start covers the work queued
+    // ahead of the call on the caller's stream, not a chunk: its own bound
+    pa.start_limit = limit > (uint64_t)(kStartWaitSeconds * d->clock_hz)
+                         ? limit : (uint64_t)(kStartWaitSeconds * d->clock_hz);
 
     int occ = occupancy(*d, kind, p.shape.id);
     if (occ < 1) return AGG_E_HIP;
@@ -398,14 +527,20 @@ int ag_gemm_workspace_reset(void* workspace, size_t bytes, void* stream)
     if (!workspace || bytes < (size_t)kHeaderBytes) return AGG_E_INVALID;
     if (!aligned(workspace, 256)) return AGG_E_UNSUPPORTED;
     std::lock_guard<std::mutex> lock(g_mu);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return AGG_E_HIP;
-    if (launch_header_reset(static_cast<uint32_t*>(workspace), kHeaderBytes,
-                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    Device* d = nullptr;
+    int rc = device_state(&d);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (launch_header_reset(static_cast<uint32_t*>(workspace), kHeaderBytes, st) != hipSuccess)
         return AGG_E_HIP;
+    // The memory may hold anything (a workspace's earlier life, a caller's
+    // fill): a pipelined producer, which starts on the side stream without
+    // waiting for `stream`, must not read the header before the reset.
+    rc = order_side_after(*d, st);
+    if (rc) return rc;
     Track t;
     memset(&t, 0, sizeof t);
-    t.device = dev;
+    t.device = d->id;
     g_user_ws[workspace] = t;
     return AGG_OK;
 }

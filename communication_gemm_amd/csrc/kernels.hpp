@@ -30,6 +30,9 @@ struct ProducerArgs {
     uint64_t* trace;               // optional timestamps (see agg_options.trace)
     const uint32_t* start;         // pipelined mode: wait until it holds the epoch
                                    // before reading a shard (nullptr: no wait)
+    uint64_t start_limit;          // bound of that wait in clock ticks: the work
+                                   // queued ahead of the call on the caller's
+                                   // stream may take far longer than a chunk
     const uint64_t* stages;        // workspace ring: tiles finished per source and
                                    // stage, [shard][kMaxStages] (nullptr: no wait)
 };

@@ -160,9 +160,12 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     // are device-scope loads, which are coherent at that scope and take no
     // such line (so no cache invalidation, which cost the consumer its
     // cached panels, is needed here).
+    // The bound of this wait is its own, far above a chunk's: it covers
+    // whatever the caller queued ahead of the call.
     if (a.start) {
         if (threadIdx.x == 0)
-            stop_sh = !reached(poll_until(a.start, a.epoch, a.err, a.epoch, a.limit), a.epoch);
+            stop_sh = !reached(poll_until(a.start, a.epoch, a.err, a.epoch, a.start_limit),
+                               a.epoch);
         __syncthreads();
         if (stop_sh) return;
     }

@@ -38,11 +38,12 @@
  * The producer reads no shard before the consumer has started (the
  * consumer's start, in `stream` order, proves that the work queued ahead of
  * the call is done; the producer waits for it on the device, for at most
- * the call's time limit).  `stream` does not wait for the producer: the
- * consumer ends only after every chunk is released, which comes after all
- * of the producer's reads of the shards and writes of the workspace.  After
- * a failed call the producer may still be running when `stream` passes the
- * call; ag_gemm_check() waits for it.
+ * 120 s or the call's time limit if that is longer, so work queued ahead
+ * of a call does not count against the chunk waits' limit).  `stream` does
+ * not wait for the producer: the consumer ends only after every chunk is
+ * released, which comes after all of the producer's reads of the shards
+ * and writes of the workspace.  After a failed call the producer may still
+ * be running when `stream` passes the call; ag_gemm_check() waits for it.
  */
 #ifndef AGGEMM_H
 #define AGGEMM_H
@@ -283,8 +284,13 @@ size_t ag_gemm_workspace_bytes(int n_shards, int64_t M, int64_t K,
                                int elt_bytes);
 
 /* Make a caller-owned workspace ready (zeroes its counter header on
- * `stream`); needed once after allocating it.  Call ag_gemm_check() after
- * the last call that used it before freeing it. */
+ * `stream`); needed once after allocating it, and again before a memory
+ * area that held another workspace (or anything else) is used as one.
+ * The library's side stream is ordered after the reset (one event), so no
+ * producer of a later call reads the header before it is zeroed.  Call
+ * ag_gemm_check() after the last call that used it before freeing it.
+ * A library convention (query the size, prepare, then execute), not an
+ * operation of the pages. */
 int ag_gemm_workspace_reset(void *workspace, size_t bytes, void *stream);
 
 /*

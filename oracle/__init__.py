@@ -66,6 +66,8 @@ def _load():
             lib.oracle_half_to_double_n.argtypes = [P, P, I64]
             lib.oracle_float_to_half_n.argtypes = [P, P, I64]
             lib.oracle_dequant_n.argtypes = [P, P, P, I64]
+            lib.oracle_set_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_threads.restype = ctypes.c_int
             lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
             lib.oracle_half_to_double.restype = ctypes.c_double
             lib.oracle_float_to_half.argtypes = [ctypes.c_float]
@@ -222,6 +224,12 @@ def dequant(v: np.ndarray, s: np.ndarray) -> np.ndarray:
     out = np.empty(v.shape, np.uint16)
     lib.oracle_dequant_n(_ptr(v), _ptr(s), _ptr(out), v.size)
     return out
+
+
+def set_threads(n: int) -> int:
+    """Use n threads in the oracle's loops from now on (n <= 0: unchanged);
+    returns the previous count.  Results do not depend on it."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 def threads_used() -> int:

@@ -40,6 +40,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -427,4 +428,15 @@ void oracle_dequant_n(const int32_t *v, const float *s, uint16_t *out,
 {
     for (int64_t i = 0; i < n; i++)
         out[i] = dequant_one(v[i], s[i]);
+}
+
+/* Threads the parallel loops above use from now on (how the oracle's CPU
+ * time is measured on one core or on all of them); returns the previous
+ * count.  No effect on any result: every output element is summed by one
+ * thread in a fixed order. */
+int oracle_set_threads(int n)
+{
+    int old = omp_get_max_threads();
+    if (n > 0) omp_set_num_threads(n);
+    return old;
 }

@@ -62,7 +62,7 @@ def test_pmc_summary_means_per_kernel_and_counter(tmp_path, capsys):
     assert float(got["kB"].split()[1]) == 7.0 and "dispatches=   1" in got["kB"]
 
 
-def test_trace_summary_last_n_in_dispatch_order(tmp_path, capsys):
+def test_trace_summary_window_in_dispatch_order(tmp_path, capsys):
     d = tmp_path / "tr"
     d.mkdir()
     with open(d / "x_kernel_trace.csv", "w") as f:
@@ -70,18 +70,20 @@ def test_trace_summary_last_n_in_dispatch_order(tmp_path, capsys):
         # kernel k: durations 1, 2, 3, 4, 5 us, written out of dispatch order
         for i, us in [(3, 3), (1, 1), (5, 5), (2, 2), (4, 4)]:
             f.write(f"{i},k,{1000 * i},{1000 * i + 1000 * us}\n")
-    bench.trace_summary(str(d), 2)
+    bench.trace_summary(str(d), 2, 3)
     line = capsys.readouterr().out.strip()
     assert line.startswith("5 dispatches")
-    assert "mean       3.0 us" in line          # all five
-    assert "last 2: mean       4.5 us" in line  # dispatches 4 and 5
+    assert "mean       3.0 us" in line            # all five
+    assert "[3, 5): mean       4.5 us" in line    # dispatches 4 and 5
     assert "min      4.0  max      5.0" in line
+    bench.trace_summary(str(d), 2, 1)
+    assert "[1, 3): mean       2.5 us" in capsys.readouterr().out
 
 
-@pytest.mark.parametrize("steps,expect", [(100, 20), (5, 5), (40, 20), (1, 1)])
-def test_timed_brackets_one_call_in_every_stride(steps, expect):
-    """timed() brackets one call of every max(1, steps // 20) with the
-    consumer's event pair; a stand-in for torch counts the pairs."""
+@pytest.mark.parametrize("steps,expect", [(100, 20), (5, 1), (20, 4), (1, 1), (7, 2)])
+def test_timed_brackets_one_call_in_five(steps, expect):
+    """timed() brackets the first call of every five with the consumer's
+    event pair (at least one); a stand-in for torch counts the pairs."""
     class Ev:
         def __init__(self, enable_timing=False):
             self.t = 0.0
@@ -102,10 +104,17 @@ def test_timed_brackets_one_call_in_every_stride(steps, expect):
     class Torch:
         cuda = Cuda
 
-    seen = []
+    made = []
+    ran = []
+
+    def make(ev):
+        made.append(ev)
+        return lambda: ran.append(ev)
+
     per = []
-    t, c = bench.timed(Torch, lambda ev: seen.append(ev), steps, 3, per_call=per)
-    assert len(seen) == 3 + steps
-    assert sum(ev is not None for ev in seen[3:]) == expect
-    assert all(ev is None for ev in seen[:3])
+    t, c = bench.timed(Torch, make, steps, 3, per_call=per)
+    assert len(ran) == 3 + steps
+    assert all(ev is None for ev in ran[:3])
+    assert sum(ev is not None for ev in ran[3:]) == expect
+    assert [i for i, ev in enumerate(ran[3:]) if ev is not None] == list(range(0, steps, 5))
     assert len(per) == expect and c == 1.0

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import check_f16, check_i8, dev, sample_rows
+from gpu_util import check_f16, check_i8, dev, freivalds_i8, stratified_rows
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -68,9 +68,11 @@ def test_ring_int8_sampled_rows(agg, orc):
     agg.ag_gemm_i8_dequant(ts, dev(B, torch), dev(bias, torch), dev(scale, torch), D, 0,
                            opts=agg.options(workspace_stages=2, workspace=ws, acc_out=acc))
     assert agg.check() == 0
-    rows = sample_rows(c.M, c.n_shards, info.chunk_rows, extra=6)
+    rows = stratified_rows(c.M, c.n_shards, info.chunk_rows, extra=6)
     ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale, rows=rows)
-    check_i8(acc.cpu().numpy()[rows], D.cpu().numpy()[rows], ao, Do, "int8 ring")
+    acc = acc.cpu().numpy()
+    check_i8(acc[rows], D.cpu().numpy()[rows], ao, Do, "int8 ring")
+    assert freivalds_i8(acc, shards, B, bias) == c.M
 
 
 def test_ring_workspace_size_is_checked(agg):
