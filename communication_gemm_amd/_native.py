@@ -14,7 +14,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libaggemm.so")
 
-AGG_OK, AGG_E_INVALID, AGG_E_UNSUPPORTED, AGG_E_NOMEM, AGG_E_HIP, AGG_E_TIMEOUT = range(6)
+(AGG_OK, AGG_E_INVALID, AGG_E_UNSUPPORTED, AGG_E_NOMEM, AGG_E_HIP, AGG_E_TIMEOUT,
+ AGG_E_TOO_LARGE) = range(7)
+NOALLOC_MAX_BYTES = 64 << 20   # AGG_NOALLOC_MAX_BYTES
 MODE_PIPELINED, MODE_COMPUTE_ONLY, MODE_SEQUENTIAL, MODE_COPY_ONLY = range(4)
 SCHEME_COUNTERS, SCHEME_BARRIER = range(2)
 LINKS_PARALLEL, LINKS_SERIAL = range(2)
@@ -90,6 +92,10 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.POINTER(Options)]),
+    "ag_gemm_f16_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.POINTER(Options)]),
     "ag_gemm_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]),
@@ -287,6 +293,29 @@ def ag_gemm_f16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | 
                 (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st),
                 opts, "ag_gemm_f16", prepare)
     return r if prepare else C
+
+
+def ag_gemm_f16_noalloc(shards, B, C, chunk_rows: int = 0, stream=None,
+                        opts: Options | None = None, prepare: bool = False):
+    """ag_gemm_f16 through the allocation-free entry point: the library's
+    fixed per-GPU scratch array is the workspace (opts.workspace must be
+    unset); AggError with AGG_E_TOO_LARGE if the call needs more than
+    NOALLOC_MAX_BYTES of it."""
+    import torch
+    if B.dtype != torch.float16 or not B.is_cuda or not B.is_contiguous() or B.dim() != 2:
+        raise ValueError("B must be a contiguous 2-D fp16 CUDA tensor")
+    K, N = B.shape
+    _on_current_device(B)
+    table, S = _shard_ptrs(shards, torch.float16, K)
+    M = S * len(shards)
+    _check_out(C, (M, N), torch.float32)
+    st = _stream_handle(stream)
+    args = (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st,
+            ctypes.byref(opts) if opts is not None else None)
+    if prepare:
+        return Prepared(lib.ag_gemm_f16_noalloc, args, "ag_gemm_f16_noalloc", (table, opts))
+    _raise(lib.ag_gemm_f16_noalloc(*args), "ag_gemm_f16_noalloc")
+    return C
 
 
 def ag_gemm_bf16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | None = None,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libaggemm.so")
 
-SOURCES = ["api.cpp", "plan.cpp", "producer.hip", "consumer.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "producer.hip", "consumer.hip", "scratch.hip"]
 
 # Packed fp32 instructions are switched off for every HIP translation unit.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

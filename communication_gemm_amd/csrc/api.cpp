@@ -34,6 +34,7 @@ struct Device {
     double clock_hz = 0;       // rate of the device's constant clock
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr;  // orders a ring-mode producer after the consumer
+    char* scratch = nullptr;   // the allocation-free entry point's array here
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
     Track track{};
@@ -73,27 +74,6 @@ int device_entry(Device** out)
     return AGG_OK;
 }
 
-// The side stream and the events of a device, made on first use.
-int device_ready(Device& d)
-{
-    if (d.ready) return AGG_OK;
-    if (hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) != hipSuccess)
-        return AGG_E_HIP;
-    if (hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess)
-        return AGG_E_HIP;
-    memset(&d.track, 0, sizeof d.track);
-    d.track.device = d.id;
-    d.ready = true;
-    return AGG_OK;
-}
-
-int device_state(Device** out)
-{
-    int rc = device_entry(out);
-    if (rc) return rc;
-    return device_ready(**out);
-}
-
 // The side stream must not run a producer before a header reset queued on
 // `st` has run: the producer polls words of the header (start word, error
 // word, counters) that hold stale values until then.  One event, once per
@@ -103,6 +83,47 @@ int order_side_after(Device& d, hipStream_t st)
     if (hipEventRecord(d.fork, st) != hipSuccess) return AGG_E_HIP;
     if (hipStreamWaitEvent(d.side, d.fork, 0) != hipSuccess) return AGG_E_HIP;
     return AGG_OK;
+}
+
+// Per-device set-up, at the first call of any entry point on the device
+// (with it current): the side stream and event, and the allocation-free
+// entry point's fixed array -- its address here (taking it loads the code
+// that holds the array, which the runtime places on the device then, not
+// inside a later allocation-free call) and its counter header zeroed on
+// `st`, registered like a caller-owned workspace so that ag_gemm_check()
+// looks at it and re-arms it after a failure.
+int device_ready(Device& d, hipStream_t st)
+{
+    if (d.ready) return AGG_OK;
+    if (!d.side && hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) != hipSuccess)
+        return AGG_E_HIP;
+    if (!d.fork && hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess)
+        return AGG_E_HIP;
+    void* p = nullptr;
+    if (scratch_address(&p) != hipSuccess) {
+        (void)hipGetLastError();
+        return AGG_E_HIP;
+    }
+    if (launch_header_reset(static_cast<uint32_t*>(p), kHeaderBytes, st) != hipSuccess)
+        return AGG_E_HIP;
+    int rc = order_side_after(d, st);
+    if (rc) return rc;
+    Track t;
+    memset(&t, 0, sizeof t);
+    t.device = d.id;
+    g_user_ws[p] = t;
+    d.scratch = static_cast<char*>(p);
+    memset(&d.track, 0, sizeof d.track);
+    d.track.device = d.id;
+    d.ready = true;
+    return AGG_OK;
+}
+
+int device_state(Device** out, hipStream_t st)
+{
+    int rc = device_entry(out);
+    if (rc) return rc;
+    return device_ready(**out, st);
 }
 
 // ---- plan cache --------------------------------------------------------
@@ -240,6 +261,7 @@ struct Call {
     int chunk_rows;
     hipStream_t st;
     const agg_options* opt;
+    bool scratch;   // the allocation-free entry point: the fixed array as workspace
 };
 
 int run(const Call& c)
@@ -271,6 +293,7 @@ int run(const Call& c)
         }
     }
     if (opt->trace && !aligned(opt->trace, 8)) return AGG_E_UNSUPPORTED;
+    if (c.scratch && opt->workspace) return AGG_E_INVALID;
 
     // Every argument check runs before anything is created or enqueued:
     // the plan needs only the device's attributes (and argument errors are
@@ -284,9 +307,10 @@ int run(const Call& c)
                          drc == AGG_OK ? d->num_cus : 0, &pp);
     if (rc) return rc;
     const Plan& p = *pp;
+    if (c.scratch && p.ws_bytes > kScratchBytes) return AGG_E_TOO_LARGE;
     if (empty) return AGG_OK;   // nothing to compute or move
     if (drc) return drc;
-    rc = device_ready(*d);
+    rc = device_ready(*d, c.st);
     if (rc) return rc;
 
     const int kind = static_cast<int>(c.kind);
@@ -301,6 +325,10 @@ int run(const Call& c)
         if (it == g_user_ws.end() || opt->workspace_bytes < p.ws_bytes) return AGG_E_INVALID;
         ws = static_cast<char*>(opt->workspace);
         tr = &it->second;
+    } else if (c.scratch) {
+        // set up with the device (device_ready): no allocation, no reset here
+        ws = d->scratch;
+        tr = &g_user_ws[d->scratch];
     } else {
         rc = internal_workspace(*d, p.ws_bytes, c.st, &ws, &tr);
         if (rc) return rc;
@@ -470,7 +498,16 @@ int ag_gemm_f16_ex(const void* const* shards, int n_shards, const void* B, float
                    const agg_options* opt)
 {
     Call c{kF16, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
-           static_cast<hipStream_t>(stream), opt};
+           static_cast<hipStream_t>(stream), opt, false};
+    return run(c);
+}
+
+int ag_gemm_f16_noalloc(const void* const* shards, int n_shards, const void* B, float* C,
+                        int64_t M, int64_t K, int64_t N, int chunk_rows, void* stream,
+                        const agg_options* opt)
+{
+    Call c{kF16, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
+           static_cast<hipStream_t>(stream), opt, true};
     return run(c);
 }
 
@@ -485,7 +522,7 @@ int ag_gemm_bf16_ex(const void* const* shards, int n_shards, const void* B, floa
                     const agg_options* opt)
 {
     Call c{kBF16, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
-           static_cast<hipStream_t>(stream), opt};
+           static_cast<hipStream_t>(stream), opt, false};
     return run(c);
 }
 
@@ -500,7 +537,7 @@ int ag_gemm_fp8_ex(const void* const* shards, int n_shards, const void* B, float
                    const agg_options* opt)
 {
     Call c{kFP8, shards, n_shards, B, nullptr, nullptr, C, M, K, N, chunk_rows,
-           static_cast<hipStream_t>(stream), opt};
+           static_cast<hipStream_t>(stream), opt, false};
     return run(c);
 }
 
@@ -518,7 +555,7 @@ int ag_gemm_i8_dequant_ex(const int8_t* const* shards, int n_shards, const int8_
                           const agg_options* opt)
 {
     Call c{kI8, reinterpret_cast<const void* const*>(shards), n_shards, B, bias, scale,
-           C, M, K, N, chunk_rows, static_cast<hipStream_t>(stream), opt};
+           C, M, K, N, chunk_rows, static_cast<hipStream_t>(stream), opt, false};
     return run(c);
 }
 
@@ -528,9 +565,9 @@ int ag_gemm_workspace_reset(void* workspace, size_t bytes, void* stream)
     if (!aligned(workspace, 256)) return AGG_E_UNSUPPORTED;
     std::lock_guard<std::mutex> lock(g_mu);
     Device* d = nullptr;
-    int rc = device_state(&d);
-    if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = device_state(&d, st);
+    if (rc) return rc;
     if (launch_header_reset(static_cast<uint32_t*>(workspace), kHeaderBytes, st) != hipSuccess)
         return AGG_E_HIP;
     // The memory may hold anything (a workspace's earlier life, a caller's

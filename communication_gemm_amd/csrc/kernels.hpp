@@ -76,6 +76,12 @@ hipError_t launch_consumer_fp8(const ConsumerArgs& a, int tile_id, int wgs,
                                hipStream_t st);
 hipError_t launch_header_reset(uint32_t* header, size_t bytes, hipStream_t st);
 
+// The allocation-free entry point's workspace: a file-scope device array of
+// kScratchBytes per GPU.  scratch_address() gives its address on the
+// current device (256-byte aligned).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_address(void** out);
+
 // Workgroups of a consumer tile shape that fit on one CU at once (kind:
 // 0 fp16, 1 int8, 2 bf16, 3 fp8).
 int consumer_occupancy(int kind, int tile_id);

@@ -354,6 +354,7 @@ const char* ag_gemm_status_string(int status)
     case AGG_E_NOMEM: return "out of device memory";
     case AGG_E_HIP: return "HIP runtime error";
     case AGG_E_TIMEOUT: return "counter wait timed out";
+    case AGG_E_TOO_LARGE: return "workspace needed exceeds the allocation-free entry point's scratch";
     default: return "unknown status";
     }
 }

@@ -63,8 +63,11 @@ enum agg_status {
                                size past the limits below                   */
     AGG_E_NOMEM = 3,        /* workspace allocation failed                   */
     AGG_E_HIP = 4,          /* a HIP call failed while enqueueing            */
-    AGG_E_TIMEOUT = 5       /* a counter wait exceeded its limit (reported
+    AGG_E_TIMEOUT = 5,      /* a counter wait exceeded its limit (reported
                                by ag_gemm_check)                             */
+    AGG_E_TOO_LARGE = 6     /* ag_gemm_f16_noalloc: the call needs more
+                               workspace than its fixed scratch holds
+                               (AGG_NOALLOC_MAX_BYTES)                       */
 };
 
 /* What one call runs (PTO-ISA README, "benchmark and output"). */
@@ -217,6 +220,41 @@ int ag_gemm_f16(const void *const *shards, int n_shards, const void *B,
 int ag_gemm_f16_ex(const void *const *shards, int n_shards, const void *B,
                    float *C, int64_t M, int64_t K, int64_t N, int chunk_rows,
                    void *stream, const agg_options *opt);
+
+/*
+ * ag_gemm_f16_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments, kernels and results (bit for bit), but
+ * the workspace is a fixed device array of AGG_NOALLOC_MAX_BYTES that the
+ * library holds on every GPU it runs on, from the first use of its code on
+ * that GPU until the process ends.  The call makes no hipMalloc or hipFree
+ * and calls no allocating routine.
+ *   opt         as for ag_gemm_f16_ex (may be NULL); opt->workspace must be
+ *               NULL (AGG_E_INVALID otherwise).
+ *   Size limit  the workspace the call needs (a counter header plus the
+ *               remote shards' slots, agg_plan_info.workspace_bytes) must
+ *               fit in AGG_NOALLOC_MAX_BYTES, else AGG_E_TOO_LARGE and
+ *               nothing is enqueued.  With full slots that is
+ *               (n_shards - 1) * S * K * 2 bytes plus about 0.8 MiB (8
+ *               shards of 1024 x 4096 fit); a workspace ring
+ *               (opt->workspace_stages) brings larger shapes under it.
+ *   Set-up      the library's per-device set-up (run by the first call of
+ *               any entry point on a device, with that device current)
+ *               takes the array's address there, which loads the code that
+ *               holds it, and zeroes its counter header on that call's
+ *               stream (a kernel, no memset); allocation-free calls then go
+ *               straight to the kernels.
+ *   Sharing     every call on one GPU uses the same array, which keeps what
+ *               the last call left in it: calls that overlap in time on one
+ *               GPU (two streams, two host threads) race and give wrong
+ *               results.  Serialise them, as for the internal workspace.
+ *   Errors      as ag_gemm_f16_ex; a time-out is reported by
+ *               ag_gemm_check(), which also re-arms the array's header.
+ */
+#define AGG_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int ag_gemm_f16_noalloc(const void *const *shards, int n_shards, const void *B,
+                        float *C, int64_t M, int64_t K, int64_t N,
+                        int chunk_rows, void *stream, const agg_options *opt);
 
 /*
  * bf16 x bf16 -> fp32 streamed AllGather + GEMM: the fp16 operation above
