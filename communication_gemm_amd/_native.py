@@ -56,6 +56,7 @@ class Options(ctypes.Structure):
         ("trace", ctypes.c_void_p),
         ("producer_piece_bytes", ctypes.c_int64),
         ("k_splits", ctypes.c_int),
+        ("k_block", ctypes.c_int64),
     ]
 
 
@@ -79,6 +80,8 @@ class PlanInfo(ctypes.Structure):
         ("workspace_stages", ctypes.c_int),
         ("workspace_bytes", ctypes.c_int64),
         ("k_splits", ctypes.c_int),
+        ("k_blocks", ctypes.c_int),
+        ("k_block", ctypes.c_int64),
     ]
 
 

@@ -138,7 +138,7 @@ struct PlanKey {
     int local_shard, mode, link_model, producer_wgs, consumer_wgs, tile;
     int workspace_stages, scheme, pvalue, k_splits, debug_drop_chunk;
     double link_gbps, timeout_ms;
-    int64_t piece;
+    int64_t piece, k_block;
     int has_order;
     int order[kMaxShards];
 };
@@ -180,6 +180,7 @@ void plan_key(PlanKey* k, Kind kind, int n, int64_t M, int64_t K, int64_t N, int
     k->link_gbps = o->link_gbps;
     k->timeout_ms = o->timeout_ms;
     k->piece = o->producer_piece_bytes;
+    k->k_block = o->k_block;
     k->has_order = o->send_order != nullptr;
     if (o->send_order && n > 1 && n <= kMaxShards)
         for (int i = 0; i + 1 < n; ++i) k->order[i] = o->send_order[i];

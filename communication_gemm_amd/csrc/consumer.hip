@@ -468,9 +468,16 @@ struct Engine {
     // The whole K loop of one tile over the NS stages starting at `ring`.
     // The previous tile left no load in flight (its last slice waited for
     // all of them) and no LDS read pending (its last barrier came after
-    // them), so the ring can be refilled at once.
+    // them), so the ring can be refilled at once.  gate(k) is called, by
+    // every wave alike, before the loads of each slice after the first
+    // NS - 1 (k: the slice's first element).  (The loop has no early exit:
+    // one would make the register allocator give up the accumulators'
+    // registers; a gate that fails lets the tile run on, and the caller
+    // drops it.)
+    template <class Gate>
     __device__ __attribute__((always_inline)) static void run(
-        char* ring, int nk, const Src& src, const Lane& L, typename T::Acc (&acc)[kTM][kTN])
+        char* ring, int nk, const Src& src, const Lane& L, typename T::Acc (&acc)[kTM][kTN],
+        Gate& gate)
     {
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
@@ -485,6 +492,7 @@ struct Engine {
             // slices still loading once slice kt + 1 has landed
             const int last = l < nk ? l : nk - 1;
             const int behind = last - (kt + 1) > 0 ? last - (kt + 1) : 0;
+            if (l < nk) gate(src.kb + (int64_t)l * kBK);
             slice(ring + (kt % NS) * kStage, ring + ((kt + 1) % NS) * kStage,
                   ring + (l % NS) * kStage, l < nk, src.kb + (int64_t)l * kBK, behind, kt + 1 < nk,
                   src, L, f0, f1, acc);
@@ -626,6 +634,40 @@ __device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int
     return ok;
 }
 
+// Wave 0 inside a tile's K loop: wait until the source's counter reaches
+// `need` (relative to the call's base), then acquire.  No flag walk: the
+// counter passes chunk j only after a producer wave saw j's flag set, and
+// that flag was stored after j's data stores were performed in memory, so
+// the counter alone vouches for the data (the walk at a tile's start pairs
+// with each copier in the same way).  Kept small: it is inlined into the
+// software-pipelined loop, beside the live accumulators.
+__device__ __forceinline__ int wait_counter(const ConsumerArgs& a, int shard, int need,
+                                            uint32_t* seen, int tid)
+{
+    if (seen[shard] >= (uint32_t)need) return 1;
+    const uint32_t target = a.base[shard] + (uint32_t)need;
+    uint32_t v = target;
+    if (tid == 0)
+        v = poll_until(a.counters + shard * (kCounterStride / 4), target, a.err, a.epoch,
+                       a.limit);
+    v = __builtin_amdgcn_readfirstlane(v);
+    if (!reached(v, target)) return 0;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (tid == 0) seen[shard] = v - a.base[shard];
+    return 1;
+}
+
+// With `have` chunks of a source known released, the K-blocks whose chunks
+// of m-tile m's rows (`rows` row chunks) -- and everything before them in
+// the source's order -- are all in: [0, covered).  32-bit: at most 1024
+// chunks per source.
+__device__ __forceinline__ int covered_kblocks(const Schedule& s, uint32_t rows, uint32_t have)
+{
+    if (have < rows) return 0;
+    const uint32_t c = (have - rows) / (uint32_t)s.rcs + 1;
+    return c < (uint32_t)s.nkb ? (int)c : s.nkb;
+}
+
 // Split-K: one part of a tile's K range is done.  Its accumulators go to
 // the tile's partial sums (register-major: each store of a wave writes 256
 // contiguous bytes), written through at device scope; once they are
@@ -727,9 +769,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
 
     for (int64_t p = wg_position(s, blockIdx.x, gridDim.x); p < tiles; p += gridDim.x) {
         const TileRef t = tile_at(s, p);
+        // K range: all of K, or part kp of a split-K tile (parts hold a
+        // multiple of 256 k, a whole number of slices)
+        const int64_t kb = (int64_t)t.kp * s.kc;
+        const int64_t ke = kb + s.kc < s.K ? kb + s.kc : s.K;
+        const int nk = ke > kb ? (int)cdiv(ke - kb, E::kBK) : 0;
+        // Loads of K below `open_k` need no wait: all of K for a local tile,
+        // in a mode without waits, or once every K-block is in; `open_kb` is
+        // the first K-block not known to be in.  (32-bit: K <= 2^21.)
+        int32_t open_k = INT32_MAX, open_kb = s.nkb;
+        const uint32_t rows_need = (uint32_t)t.need;   // the tile's row chunks
+        const bool gated = t.need > 0 && !a.no_wait;
         if (a.trace && tid == 0) a.trace[3 * p] = ticks();
-        if (t.need > 0 && !a.no_wait) {
-            // wave 0 waits; the other waves hold at the barrier
+        if (gated) {
+            // Before the first slices (the NS - 1 loaded before the loop),
+            // wave 0 waits for the K-blocks they read -- with chunks of all
+            // of K, for the tile's rows; the other waves hold at the barrier.
             if (tid < 64) {
                 int ok = 1;
                 if (s.pv > 0) {
@@ -737,24 +792,55 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
                     for (int q = 1; q < s.n_shards && ok; ++q)
                         ok = wait_source(a, s.order[q], t.need, seen_sh, tid);
                 } else {
-                    ok = wait_source(a, t.shard, t.need, seen_sh, tid);
+                    const int64_t pro = kb + (int64_t)(NS - 1) * E::kBK;
+                    const int kb0 = kblock_of(s, (pro < ke ? pro : ke) - 1);
+                    ok = wait_source(a, t.shard, need_at(s, t.m, kb0), seen_sh, tid);
                 }
                 if (tid == 0) ok_sh = ok;
             }
             __syncthreads();
             if (!ok_sh) break;   // the call has failed; every lane leaves
+            if (s.pv == 0) {
+                open_kb = covered_kblocks(s, rows_need, seen_sh[t.shard]);
+                open_k = open_kb >= s.nkb ? INT32_MAX : (int32_t)(open_kb * s.kbk);
+            }
         }
         if (a.trace && tid == 0) a.trace[3 * p + 1] = ticks();
+
+        // Before a slice's loads: when the slice reaches past open_k, wave 0
+        // waits for its K-block and every wave learns the new open_k.  The
+        // test is uniform (open_k is the same in every wave), so the extra
+        // barrier is taken by all waves or by none.  The barrier is a bare
+        // one: slices already loading stay in flight.
+        // A slice is at most one K-block long (K-blocks are whole KiB of
+        // elements, slices at most 256 bytes), so the block it enters past
+        // open_k is open_kb itself.
+        // A failed wait opens all of K (no further waits) and marks the
+        // tile, which the workgroup then drops.
+        bool failed = false;
+        auto gate = [&](int64_t k) {
+            const int32_t end = (int32_t)(k + E::kBK < s.K ? k + E::kBK : s.K);
+            if (end <= open_k) return;
+            if (tid < 64) {
+                const int ok = wait_counter(a, t.shard, open_kb * s.rcs + (int)rows_need,
+                                            seen_sh, tid);
+                if (tid == 0) ok_sh = ok;
+                wait_vm_lgkm0<63>();   // the LDS stores are done (loads may fly)
+            }
+            bare_barrier();
+            if (!ok_sh) {
+                failed = true;
+                open_k = INT32_MAX;
+                return;
+            }
+            open_kb = covered_kblocks(s, rows_need, seen_sh[t.shard]);
+            open_k = open_kb >= s.nkb ? INT32_MAX : (int32_t)(open_kb * s.kbk);
+        };
 
         const int64_t row0 = (int64_t)t.m * BM;
         const int64_t rows = s.S - row0;
         // remote rows sit in the workspace (a full slot or a ring stage)
         const int64_t arow = t.shard == s.local ? row0 : slot_row(s, row0);
-        // K range: all of K, or part kp of a split-K tile (parts hold a
-        // multiple of 256 k, a whole number of slices)
-        const int64_t kb = (int64_t)t.kp * s.kc;
-        const int64_t ke = kb + s.kc < s.K ? kb + s.kc : s.K;
-        const int nk = ke > kb ? (int)cdiv(ke - kb, E::kBK) : 0;
         const typename E::Src src{a.a[t.shard] + arow * s.K * T::kElt,
                                   rows < BM ? rows : BM, a.B, s.K, s.N, (int64_t)t.n * BN, kb};
 
@@ -764,7 +850,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
 #pragma unroll
             for (int j = 0; j < E::kTN; ++j) acc[i][j] = T::zero();
 
-        if (nk > 0) E::run(lds, nk, src, L, acc);
+        if (nk > 0) E::run(lds, nk, src, L, acc, gate);
+        if (failed) break;   // the call has failed; every lane leaves
         // every wave's loads of the tile have completed (the last slice
         // waited for them before its barrier): the stage may be reused
         if (a.stages && t.shard != s.local && tid == 0)

@@ -246,8 +246,22 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         }
         s.ring = opt->workspace_stages;
     }
-    s.cps = S > 0 ? (int)cdiv(S, s.cr) : 0;
-    if (n_shards > 1 && s.cps > kFlagCap) return AGG_E_UNSUPPORTED;
+    s.rcs = S > 0 ? (int)cdiv(S, s.cr) : 0;
+    // K-blocks (2-D chunks): whole KiB of every row segment, so that the
+    // producer's 1 KiB vectors never straddle two rows
+    if (opt->k_block < 0) return AGG_E_INVALID;
+    s.nkb = 1;
+    s.kbk = K;
+    if (opt->k_block > 0 && opt->k_block < K) {
+        const int64_t kib = 1024 / elt_bytes(kind);
+        if (opt->k_block % kib || K % kib) return AGG_E_UNSUPPORTED;
+        if (s.ring > 0 || opt->scheme != AGG_SCHEME_COUNTERS || s.ks > 1)
+            return AGG_E_UNSUPPORTED;
+        s.kbk = opt->k_block;
+        s.nkb = (int)(K / s.kbk);           // the last K-block takes the rest
+    }
+    if ((int64_t)s.rcs * s.nkb > kFlagCap && n_shards > 1) return AGG_E_UNSUPPORTED;
+    s.cps = s.rcs * s.nkb;
     s.pv = opt->scheme == AGG_SCHEME_BARRIER ? (opt->pvalue > 0 ? opt->pvalue : 1) : 0;
     if (s.pv > s.mt) s.pv = s.mt > 0 ? s.mt : 1;
     // a tile of iteration i waits for every panel of the iteration, so a
@@ -266,8 +280,9 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     int cw = opt->consumer_wgs ? opt->consumer_wgs : num_cus;
     if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
     if (cw < 1) cw = 1;
-    // pieces per chunk
-    const int64_t chunk_bytes = (int64_t)s.cr * K * elt_bytes(kind);
+    // pieces per chunk (the largest chunk: the last K-block's)
+    const int64_t chunk_bytes =
+        (int64_t)s.cr * (kblock_end(s, s.nkb - 1) - kblock_begin(s, s.nkb - 1)) * elt_bytes(kind);
     // Automatic piece, in whole sweeps, between one sweep and kPieceMax.
     // Pipelined: about kPiecesPerChunk pieces a chunk, so that chunks land
     // close to their send order (the consumer takes them as they land)
@@ -386,6 +401,8 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
         info->workspace_stages = s.ring;
         info->workspace_bytes = (int64_t)p.ws_bytes;
         info->k_splits = s.ks;
+        info->k_blocks = s.nkb;
+        info->k_block = s.kbk;
     }
     if (tile_order) {
         int64_t T = agg::total_tiles(s);

@@ -208,6 +208,17 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     int32_t n = 0, off = 0;
     const char* src = nullptr;
     char* dst = nullptr;
+    // A chunk of one K-block (2-D chunks) is `rows` row segments of `seg`
+    // bytes, row_bytes apart in the shard and in the slot alike; a piece is
+    // bytes [begin, begin + n) of the chunk taken segment after segment.
+    // seg == 0: the chunk spans all of K, so it is contiguous and src/dst
+    // point at the piece itself.  Otherwise src/dst point at the chunk's
+    // first element, the descriptors span the chunk (`ext` bytes), and
+    // (pr, pc) is the row and byte within its segment of the piece's next
+    // 1 KiB vector.  Segments are whole KiB, so a vector never straddles
+    // two rows and every offset is uniform across the wave.
+    int32_t seg = 0, ext = 0, pr = 0, pc = 0;
+    const int32_t rb32 = (int32_t)row_bytes;   // a row is below 2^31 bytes
     bool timed_out = false;   // a stage wait timed out (reported at the end)
     // Workspace ring: the current item may be copied once the stage counter
     // `wait_word` reaches `wait_for` (null: no wait); polls so far, and the
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     auto setup = [&]() -> bool {
         if (chunk >= nchunks) return false;
         const ChunkRef r = chunk_at(s, chunk);
-        const int64_t row0 = (int64_t)r.j * s.cr;
+        const int64_t row0 = (int64_t)r.jr * s.cr;
         // Workspace ring: the chunk's panel goes over the panel that used
         // the stage before; wait until the consumer has finished every
         // tile of that one (its reads of the stage are complete then).
@@ -238,14 +249,27 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
         }
         total = (uint32_t)(r.shard * kFlagCap + r.j);
         weight = piece_weight((int)q, a.ppc);
-        const int64_t bytes = (chunk_row_end(s, r.j) - row0) * row_bytes;
+        const int64_t rows = chunk_row_end(s, r.jr) - row0;
+        const int64_t k0 = kblock_begin(s, r.kb);
+        const int64_t sb = (kblock_end(s, r.kb) - k0) * a.elt;   // bytes per row segment
+        const int64_t bytes = rows * sb;
         const int64_t begin = q * a.piece;
         const int64_t end = begin + a.piece < bytes ? begin + a.piece : bytes;
         // an empty piece of a short last chunk copies nothing but counts
         n = end > begin ? (int32_t)(end - begin) : 0;  // a chunk is below 2 GiB
         off = 0;
-        src = a.src[r.shard] + row0 * row_bytes + begin;
-        dst = a.dst[r.shard] + slot_row(s, row0) * row_bytes + begin;
+        if (sb == row_bytes) {
+            seg = 0;
+            src = a.src[r.shard] + row0 * row_bytes + begin;
+            dst = a.dst[r.shard] + slot_row(s, row0) * row_bytes + begin;
+        } else {
+            seg = (int32_t)sb;
+            ext = (int32_t)((rows - 1) * row_bytes + sb);
+            src = a.src[r.shard] + row0 * row_bytes + k0 * a.elt;
+            dst = a.dst[r.shard] + slot_row(s, row0) * row_bytes + k0 * a.elt;
+            pr = (int32_t)(begin / sb);
+            pc = (int32_t)(begin - (int64_t)pr * sb);
+        }
         return true;
     };
 
@@ -258,15 +282,37 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
         // (a multiple of 16 bytes), so lanes past it load zeros and store
         // nothing.  Built from first-lane copies, which are uniform to the
         // compiler (loop-carried, it would take them as per-lane values).
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(src), 0, uniform(n), kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rd =
-            __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(dst), 0, uniform(n), kRsrcWord3);
+        const int32_t sg = uniform(seg);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(src), 0, sg ? uniform(ext) : uniform(n), kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(dst), 0, sg ? uniform(ext) : uniform(n), kRsrcWord3);
+        // Scalar offset of vector u of the sweep.  2-D chunk: the vector
+        // lies in row segment r at byte c, and (r, c) steps on by one
+        // vector.  A vector past the piece's end (pieces are whole KiB, so
+        // it is whole too) copies vector 0 of the sweep again: the same
+        // bytes to the same place, with no branch.  The offsets are made
+        // again for the stores rather than kept across the wait.
+        const int32_t r0 = uniform(pr), c0 = uniform(pc);
+        auto vec_off = [&](int u, int32_t& r, int32_t& c) -> int32_t {
+            const int32_t o = uniform(off) + u * kLaneStep;
+            if (!sg) return o;
+            const int32_t at = o < uniform(n) ? r * rb32 + c : r0 * rb32 + c0;
+            c += kLaneStep;
+            if (c >= sg) {
+                c -= sg;
+                ++r;
+            }
+            return at;
+        };
         if (copy) {
+            int32_t r = r0, c = c0;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < kUnroll; ++u) {
+                const int32_t so = vec_off(u, r, c);
                 v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rs, lane_off, uniform(off) + u * kLaneStep, kDevice));
+                                                     rs, lane_off, so, kDevice));
+            }
         }
         // The one wait point of a sweep: this wave's loads have landed, and
         // its earlier stores and add are performed.  Store the sweep (its
@@ -274,12 +320,16 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
         // that was in flight, then count the piece whose stores were last.
         __builtin_amdgcn_s_waitcnt(0);
         if (copy) {
+            int32_t r = r0, c = c0;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < kUnroll; ++u) {
+                const int32_t so = vec_off(u, r, c);
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[u]), rd,
-                                                       lane_off, uniform(off) + u * kLaneStep,
-                                                       kDevice);
+                                                       lane_off, so, kDevice);
+            }
             off += kWaveSweepBytes;
+            pr = r;
+            pc = c;
         }
         if (cnt >= 0) {
             // lane 0's add returned the running total before it

@@ -79,7 +79,11 @@ struct Schedule {
     int local;             // shard read in place
     int link_model;        // 0 = parallel links, 1 = one serial link
     int cr;                // rows per chunk
-    int cps;               // chunks per source
+    int cps;               // chunks per source: rcs row chunks x nkb K-blocks
+    int rcs;               // row chunks per source, ceil(S / cr)
+    int nkb;               // K-blocks per row chunk (1: a chunk spans all of K)
+    int64_t kbk;           // elements of K per K-block (the last one also takes
+                           // the remainder of K); K when nkb == 1
     int tm, tn;            // output tile
     int mt;                // m-tiles per shard
     int nt;                // n-tiles
@@ -102,13 +106,37 @@ constexpr int kXcds = 8;   // XCDs; workgroup b of a grid runs on XCD b % 8
 
 AGG_HD int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Chunks of a source that must be released before m-tile `m` can start:
-// the chunk holding the tile's last row, and all before it.
+// Row chunks of a source that m-tile `m` needs: the one holding the
+// tile's last row, and all before it.
 AGG_HD int need_chunks(const Schedule& s, int m)
 {
     int64_t last = (int64_t)(m + 1) * s.tm;
     if (last > s.S) last = s.S;
     return (int)cdiv(last, s.cr);
+}
+
+// Chunks are K-block major inside a source: chunk j = kb * rcs + row chunk
+// (a chunk of rows x all of K when nkb == 1).  Counter value that m-tile m
+// needs before it reads K-block kb: every chunk of the K-blocks before kb,
+// and the tile's row chunks of kb -- a prefix of the source's chunk order,
+// so one monotonic counter per source still says it.
+AGG_HD int need_at(const Schedule& s, int m, int kb)
+{
+    return kb * s.rcs + need_chunks(s, m);
+}
+
+// K-block of element k (the last K-block takes the remainder of K).
+AGG_HD int kblock_of(const Schedule& s, int64_t k)
+{
+    const int64_t b = k / s.kbk;
+    return b < s.nkb ? (int)b : s.nkb - 1;
+}
+
+// First element of K-block kb, and the first element after it.
+AGG_HD int64_t kblock_begin(const Schedule& s, int kb) { return (int64_t)kb * s.kbk; }
+AGG_HD int64_t kblock_end(const Schedule& s, int kb)
+{
+    return kb + 1 >= s.nkb ? s.K : (int64_t)(kb + 1) * s.kbk;
 }
 
 AGG_HD int64_t total_tiles(const Schedule& s)
@@ -199,40 +227,53 @@ AGG_HD TileRef tile_at(const Schedule& s, int64_t p)
 struct ChunkRef {
     int shard;   // source shard
     int src;     // its position in the send order (0-based over remotes)
-    int j;       // chunk index within the shard
+    int j;       // chunk index within the shard: kb * rcs + jr
+    int jr;      // row chunk: rows [jr * cr, min((jr + 1) * cr, S))
+    int kb;      // K-block
 };
 
 // Producer position c -> chunk, in the order the consumer needs them.
-// Parallel links: group g holds the chunks first needed by m-tile g (chunk
-// j of a source belongs to group j * cr / tm), every source in send order,
-// chunks ascending inside a source.  Group g starts at source chunk
+// Parallel links: K-block after K-block (one K-block when chunks span all
+// of K); inside a K-block, group g holds the row chunks first needed by
+// m-tile g (row chunk j belongs to group j * cr / tm), every source in send
+// order, row chunks ascending inside a source.  Group g starts at row chunk
 // f = ceil(g tm / cr); as f * remotes <= c exactly when f <= c / remotes,
-// the group of position c is the group of source chunk c / remotes.
+// the group of position c is the group of row chunk c / remotes.
+// One serial link: source after source, each source's chunks in its own
+// (K-block major) order.
 // 32-bit arithmetic: positions stay below kMaxShards * kFlagCap, and
 // j * cr below S (at most 2^30).
 AGG_HD ChunkRef chunk_at(const Schedule& s, int64_t c64)
 {
     ChunkRef r;
     const uint32_t remotes = (uint32_t)(s.n_shards - 1);
-    const uint32_t cps = (uint32_t)s.cps, cr = (uint32_t)s.cr, tm = (uint32_t)s.tm;
+    const uint32_t cps = (uint32_t)s.cps, rcs = (uint32_t)s.rcs;
+    const uint32_t cr = (uint32_t)s.cr, tm = (uint32_t)s.tm;
     if (c64 < 0 || remotes == 0 || c64 >= (int64_t)remotes * cps) {
-        r.src = -1; r.j = -1; r.shard = -1;   // out of range
+        r.src = -1; r.j = -1; r.shard = -1; r.jr = -1; r.kb = -1;   // out of range
         return r;
     }
     const uint32_t c = (uint32_t)c64;
     if (s.link_model == 0) {
-        const uint32_t g = (c / remotes) * cr / tm;
-        const uint32_t f = (g * tm + cr - 1) / cr;           // first chunk of group g
-        uint32_t e = ((g + 1) * tm + cr - 1) / cr;           // first chunk after it
-        if (e > cps) e = cps;
-        const uint32_t gs = e - f;                           // chunks per source in g
-        const uint32_t rel = c - f * remotes;
+        const uint32_t per_kb = remotes * rcs;
+        const uint32_t kb = c / per_kb;
+        const uint32_t q = c - kb * per_kb;
+        const uint32_t g = (q / remotes) * cr / tm;
+        const uint32_t f = (g * tm + cr - 1) / cr;           // first row chunk of group g
+        uint32_t e = ((g + 1) * tm + cr - 1) / cr;           // first row chunk after it
+        if (e > rcs) e = rcs;
+        const uint32_t gs = e - f;                           // row chunks per source in g
+        const uint32_t rel = q - f * remotes;
         r.src = (int)(rel / gs);
-        r.j = (int)(f + rel % gs);
+        r.jr = (int)(f + rel % gs);
+        r.kb = (int)kb;
     } else {
         r.src = (int)(c / cps);
-        r.j = (int)(c % cps);
+        const uint32_t j = c % cps;
+        r.kb = (int)(j / rcs);
+        r.jr = (int)(j % rcs);
     }
+    r.j = r.kb * s.rcs + r.jr;
     r.shard = s.order[1 + r.src];
     return r;
 }
@@ -312,14 +353,17 @@ AGG_HD int64_t chunk_row_end(const Schedule& s, int j)
     return e < s.S ? e : s.S;
 }
 
-// Bytes that must have crossed the emulated link before chunk (src, j) may
-// be released: its own source's rows up to the chunk's end (parallel
-// links), or everything sent before it on the one link (serial).
+// Bytes that must have crossed the emulated link before chunk r may be
+// released: its own source's bytes up to the chunk's end in the source's
+// order -- every row of the K-blocks before it, then its K-block's rows up
+// to the chunk's last (parallel links) -- or everything sent before it on
+// the one link too (serial).
 AGG_HD int64_t paced_bytes(const Schedule& s, const ChunkRef& r, int elt)
 {
-    int64_t rows = chunk_row_end(s, r.j);
-    if (s.link_model != 0) rows += (int64_t)r.src * s.S;
-    return rows * s.K * elt;
+    int64_t b = kblock_begin(s, r.kb) * s.S +
+                chunk_row_end(s, r.jr) * (kblock_end(s, r.kb) - kblock_begin(s, r.kb));
+    if (s.link_model != 0) b += (int64_t)r.src * s.S * s.K;
+    return b * elt;
 }
 
 }  // namespace agg

@@ -193,6 +193,23 @@ typedef struct agg_options {
                                (agg_plan_info.workspace_bytes).  The sum
                                order is fixed, so results do not depend on
                                which part finishes last.                   */
+    int64_t k_block;        /* elements of K per chunk; 0 (default) or >= K:
+                               a chunk spans all of K.  Otherwise a chunk is
+                               chunk_rows rows x one K-block of this many
+                               elements (the last K-block also takes the
+                               remainder of K): the chunk flag matrix of the
+                               PTO-ISA README read as row groups x K-blocks.
+                               A source's chunks are sent and counted
+                               K-block after K-block, and a tile waits at
+                               each K-block it enters, not for all of its
+                               rows x K at once.  The same results, bit for
+                               bit.  Needs k_block and K to be whole KiB of
+                               elements (multiples of 512 for fp16/bf16, of
+                               1024 for int8/fp8), at most 1024 chunks per
+                               source (rows chunks x K-blocks), and the
+                               counters scheme without a workspace ring or
+                               split-K (AGG_E_UNSUPPORTED otherwise);
+                               negative: AGG_E_INVALID.                    */
 } agg_options;
 
 /* Fill *opt with the defaults above. */
@@ -351,7 +368,7 @@ void ag_gemm_release(void);
 typedef struct agg_plan_info {
     int64_t shard_rows;     /* S */
     int chunk_rows;         /* rows per chunk */
-    int chunks_per_source;  /* ceil(S / chunk_rows) */
+    int chunks_per_source;  /* ceil(S / chunk_rows) x k_blocks */
     int tile_m, tile_n;     /* consumer output tile */
     int m_tiles_per_shard;  /* ceil(S / tile_m) */
     int n_tiles;            /* ceil(N / tile_n) */
@@ -366,6 +383,8 @@ typedef struct agg_plan_info {
     int64_t workspace_bytes; /* workspace this call needs (a caller-owned
                                 workspace must be at least this large)     */
     int k_splits;           /* parts of K per output tile (1: no split-K)   */
+    int k_blocks;           /* K-blocks per row chunk (1: chunks span K)    */
+    int64_t k_block;        /* elements of K per K-block (K when 1 block)   */
 } agg_plan_info;
 
 /*
@@ -373,10 +392,11 @@ typedef struct agg_plan_info {
  *   kind: 0 = fp16 path, 1 = int8 path, 2 = bf16 path, 3 = fp8 path; num_cus: CUs of
  *   the device to plan for (0 = 256).  tile_order (nullable, capacity total_tiles * 4 int32):
  *   per consumer position: shard, m-tile, n-tile, counter value waited for
- *   (0 for the local shard); with split-K the positions run part after
+ *   before the tile's first K-block (0 for the local shard); with split-K the positions run part after
  *   part, each part's positions in the same order, so each (shard, m-tile,
  *   n-tile) appears once per part.  chunk_order (nullable, capacity
- *   total_chunks * 2 int32): per producer position: shard, chunk index.
+ *   total_chunks * 2 int32): per producer position: shard, chunk index
+ *   (K-block * ceil(S / chunk_rows) + row chunk).
  */
 int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
                  int chunk_rows, const agg_options *opt, int num_cus,

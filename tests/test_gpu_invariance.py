@@ -63,6 +63,12 @@ def ref(agg, data, orc):
     # every chunk; one sweep on a single producer workgroup
     dict(producer_piece_bytes=8192), dict(producer_piece_bytes=8192, chunk_rows=100),
     dict(producer_piece_bytes=1 << 20), dict(producer_piece_bytes=8192, producer_wgs=1),
+    # chunks of rows x one K-block (K = 1024: two blocks of 512)
+    dict(k_block=512), dict(k_block=512, chunk_rows=1), dict(k_block=512, chunk_rows=100),
+    dict(k_block=512, local_shard=3, send_order=[1, 0, 2]), dict(k_block=512, link_model=1),
+    dict(k_block=512, link_gbps=30.0), dict(k_block=512, link_gbps=20.0, link_model=1),
+    dict(k_block=512, producer_wgs=1), dict(k_block=512, mode=2),
+    dict(k_block=512, producer_piece_bytes=8192, chunk_rows=7),
 ])
 def test_bitwise_invariant(agg, data, ref, kw):
     kw = dict(kw)
@@ -193,3 +199,39 @@ def test_barrier_scheme_gives_the_same_bits(agg, kw):
     agg.ag_gemm_f16(ts, B, C, 0, opts=agg.options(**kw))
     assert agg.check() == 0
     assert torch.equal(C, ref)
+
+
+def test_k_blocks_nan_poisoned_workspace(agg, data, ref):
+    """K-blocks on a paced link over a workspace whose slots hold NaN until
+    each chunk is released: a tile that read a K-block early would carry
+    a NaN into C."""
+    ts, B = data[0], data[1]
+    M, K = ts[0].shape[0] * len(ts), ts[0].shape[1]
+    ws = torch.empty(agg.workspace_bytes(len(ts), M, K, 2) // 2, dtype=torch.float16,
+                     device="cuda")
+    for it, cr in enumerate((8, 64, 1)):
+        ws.fill_(float("nan"))
+        agg.workspace_reset(ws)
+        C = torch.full_like(ref, float("nan"))
+        agg.ag_gemm_f16(ts, B, C, cr, opts=agg.options(workspace=ws, link_gbps=60.0,
+                                                       k_block=512))
+        assert agg.check() == 0
+        assert torch.equal(C, ref), f"iteration {it}"
+
+
+def test_k_blocks_withheld_chunk_times_out_inside_a_tile(agg, data, ref):
+    """A chunk of K-block 1 is never released: tiles pass their first wait
+    (K-block 0 is in) and time out inside their K loop; the call reports
+    the time-out and the next call is exact again."""
+    ts, B = data[0], data[1]
+    info, _, chunks = agg.plan("f16", len(ts), ts[0].shape[0] * len(ts), ts[0].shape[1],
+                               B.shape[1], 8, agg.options(k_block=512), orders=True)
+    R = info.chunks_per_source // info.k_blocks
+    drop = 3 * R + 5                     # K-block 1 (positions 3R.. on 3 sources)
+    assert chunks[drop, 1] // R == 1
+    C = torch.zeros_like(ref)
+    agg.ag_gemm_f16(ts, B, C, 8, opts=agg.options(k_block=512, debug_drop_chunk=drop,
+                                                  timeout_ms=50.0))
+    assert agg.check() == agg.AGG_E_TIMEOUT
+    assert torch.equal(call(agg, data, 8, k_block=512), ref)
+    assert torch.equal(call(agg, data), ref)

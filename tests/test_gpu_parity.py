@@ -338,3 +338,57 @@ def test_fp8_large_full(agg, orc):
     C = run_fp8(agg, shards, B)
     Co, So = orc.ag_gemm_fp8(shards, B)
     print("fp8 8x1024x4096x4096: max err/S", check_f16(C, Co, So, "fp8 large"))
+
+
+# ---------------------------------------------------------------- K-blocks
+# Chunks of rows x one K-block: the same sums in the same order, so the
+# output is bitwise that of whole-K chunks, and within the bar of the oracle.
+
+@pytest.mark.parametrize("kind,tile,n,S,K,N,cr,kb", [
+    ("f16", 8, 3, 300, 2048, 264, 7, 512),     # ragged rows and columns, 4 K-blocks
+    ("f16", 13, 3, 100, 2560, 168, 7, 1024),   # the last K-block takes the remainder
+    ("f16", 11, 4, 256, 1536, 512, 16, 512),
+    ("f16", 9, 2, 300, 2048, 256, 0, 512),     # four-stage ring: three slices ahead
+    ("f16", 12, 3, 64, 1024, 64, 1, 512),      # eight-stage ring, one-row chunks
+    ("f16", 3, 2, 128, 4096, 64, 32, 4096),    # one K-block: whole-K chunks
+    ("bf16", 8, 3, 300, 2048, 264, 7, 512),
+    ("fp8", 6, 3, 100, 3072, 168, 7, 1024),
+    ("fp8", 13, 2, 130, 2048, 256, 5, 1024),
+    ("i8", 8, 3, 77, 3072, 152, 9, 1024),
+    ("i8", 13, 2, 130, 2048, 256, 5, 1024),
+])
+def test_k_blocks_full(agg, orc, kind, tile, n, S, K, N, cr, kb):
+    M = n * S
+    seed = 38000 + S + K
+    if kind == "i8":
+        shards, B, bias, scale = synth.make_i8(M, K, N, n, seed)
+        acc, D = run_i8(agg, shards, B, bias, scale, cr, dict(tile=tile, k_block=kb))
+        ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale)
+        check_i8(acc, D, ao, Do, f"int8 k_block {kb} tile {tile}")
+        acc1, D1 = run_i8(agg, shards, B, bias, scale, cr, dict(tile=tile))
+        assert np.array_equal(D.view(np.uint16), D1.view(np.uint16))
+        return
+    if kind == "f16":
+        shards, B = synth.make_f16(M, K, N, n, "normal", seed)
+        run, oracle_fn = run_f16, orc.ag_gemm_f16
+    elif kind == "bf16":
+        shards, B = synth.make_bf16(M, K, N, n, "normal", seed)
+        run, oracle_fn = run_bf16, orc.ag_gemm_bf16
+    else:
+        shards, B = synth.make_fp8(M, K, N, n, "normal", seed)
+        run, oracle_fn = run_fp8, orc.ag_gemm_fp8
+    C = run(agg, shards, B, cr, agg.options(tile=tile, k_block=kb))
+    Co, So = oracle_fn(shards, B)
+    check_f16(C, Co, So, f"{kind} k_block {kb} tile {tile}")
+    C1 = run(agg, shards, B, cr, agg.options(tile=tile))
+    assert np.array_equal(C.view(np.uint32), C1.view(np.uint32)), "differs from whole-K chunks"
+
+
+@pytest.mark.parametrize("cid,kb", [(3, 512), (4, 256 * 2)])
+def test_k_blocks_full_size(agg, orc, cid, kb):
+    """C3 (paced) and C4 with K-blocks of 512: every element of C."""
+    c = synth.CASES[cid]
+    shards, B = synth.make_case(c)
+    C = run_f16(agg, shards, B, c.chunk_rows, agg.options(link_gbps=c.link_gbps, k_block=kb))
+    Co, So = orc.ag_gemm_f16(shards, B)
+    print(c.name, "k_block", kb, "max err/S", check_f16(C, Co, So, c.name))

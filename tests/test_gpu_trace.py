@@ -57,3 +57,48 @@ def test_trace_orders_releases_before_dependent_tiles(agg):
     # this; the consumer starts before the producer
     pace_ticks = S * K * 2 / (gbps * 1e9) * 1e8
     assert rel.max() - start >= 0.9 * pace_ticks
+
+
+def test_trace_k_blocks_gate_every_block(agg):
+    """Chunks of rows x one K-block (k_block): a remote tile starts after
+    its rows of the first K-block are released and cannot end before its
+    rows of the last K-block are; on a paced link the tile waits inside
+    its K loop.  The output is bitwise that of whole-K chunks."""
+    n, S, K, N, cr, gbps, kbk = 4, 512, 2048, 512, 32, 20.0, 512
+    M = n * S
+    shards, B = synth.make_f16(M, K, N, n, "normal", 60010)
+    ts = [dev(s, torch) for s in shards]
+    tB = dev(B, torch)
+    opts = dict(link_gbps=gbps, k_block=kbk)
+    info, tiles, chunks = agg.plan("f16", n, M, K, N, cr, agg.options(**opts), orders=True)
+    R, nkb = S // cr, K // kbk
+    assert info.k_blocks == nkb and info.chunks_per_source == R * nkb
+    trace = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
+    C = torch.empty((M, N), device="cuda")
+    agg.ag_gemm_f16(ts, tB, C, cr, opts=agg.options(trace=trace, **opts))
+    assert agg.check() == 0
+    ref = torch.empty_like(C)
+    agg.ag_gemm_f16(ts, tB, ref, cr)
+    assert agg.check() == 0
+    assert torch.equal(C, ref)
+
+    tr = trace.cpu().numpy().view(np.uint64).astype(np.float64)
+    nc = info.total_chunks
+    start, rel, cons = tr[0], tr[1:1 + nc], tr[1 + nc:].reshape(-1, 3)
+    assert (rel > 0).all() and (cons > 0).all()
+    pos = {(int(s), int(j)): i for i, (s, j) in enumerate(chunks)}
+    # a source's releases come K-block after K-block
+    for sh in range(1, n):
+        order = [int(j) for s_, j in chunks if s_ == sh]
+        assert order == sorted(order, key=lambda j: (j // R, j % R))
+    late = 0
+    for p, (shard, m, nn, need) in enumerate(tiles):
+        if need > 0:
+            assert need <= R
+            first = rel[pos[(int(shard), int(need) - 1)]]
+            last = rel[pos[(int(shard), (nkb - 1) * R + int(need) - 1)]]
+            assert cons[p, 1] >= first, (p, shard, m)
+            assert cons[p, 2] >= last, (p, shard, m)
+            # the tile began computing before its last K-block was there
+            late += cons[p, 1] < last
+    assert late > 0

@@ -381,3 +381,60 @@ def test_barrier_scheme_ring_must_hold_an_iteration():
         with pytest.raises(agg.AggError) as e:
             agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(**bad))
         assert e.value.status == agg.AGG_E_INVALID
+
+
+# ---- K-blocks (2-D chunks: row chunk x K-block) ------------------------
+
+def test_k_block_plan():
+    info, tiles, chunks = agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(k_block=512),
+                                   orders=True)
+    assert info.k_blocks == 8 and info.k_block == 512
+    assert info.chunks_per_source == 64 * 8
+    assert info.total_chunks == 7 * 512
+    # K-block major: the first 7 * 64 positions are K-block 0 of every source
+    R = 64
+    assert (chunks[:7 * R, 1] < R).all() and (chunks[7 * R:14 * R, 1] // R == 1).all()
+    # inside a K-block, m-tile group by group across sources, as without
+    # K-blocks: the first 16 row chunks of each of the 7 sources, then the next
+    one, _, c1 = agg.plan("f16", 8, 8192, 4096, 4096, 0, None, orders=True)
+    assert (chunks[:7 * R] == c1).all()
+    # the tile order (and each tile's first wait) is unchanged
+    _, t1, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0, None, orders=True)
+    assert (tiles == t1).all()
+
+
+def test_k_block_last_block_takes_the_remainder():
+    info, _, _ = agg.plan("f16", 2, 256, 2560, 128, 32, agg.options(k_block=1024))
+    assert info.k_blocks == 2 and info.k_block == 1024
+    info, _, _ = agg.plan("fp8", 2, 256, 3072, 128, 32, agg.options(k_block=1024))
+    assert info.k_blocks == 3
+    # a K-block of all of K (or more) is a chunk of all of K
+    for kb in (4096, 8192, 0):
+        info, _, _ = agg.plan("f16", 2, 256, 4096, 128, 32, agg.options(k_block=kb))
+        assert info.k_blocks == 1 and info.k_block == 4096
+
+
+@pytest.mark.parametrize("kind,K,kw,status", [
+    ("f16", 4096, dict(k_block=-512), agg.AGG_E_INVALID),
+    ("f16", 4096, dict(k_block=256), agg.AGG_E_UNSUPPORTED),       # not whole KiB
+    ("f16", 4096, dict(k_block=768), agg.AGG_E_UNSUPPORTED),
+    ("f16", 4104, dict(k_block=512), agg.AGG_E_UNSUPPORTED),       # K not whole KiB
+    ("i8", 27392, dict(k_block=2048), agg.AGG_E_UNSUPPORTED),      # C5's K
+    ("i8", 4096, dict(k_block=512), agg.AGG_E_UNSUPPORTED),        # int8: KiB = 1024
+    ("f16", 4096, dict(k_block=512, workspace_stages=2), agg.AGG_E_UNSUPPORTED),
+    ("f16", 4096, dict(k_block=512, scheme=1), agg.AGG_E_UNSUPPORTED),
+])
+def test_k_block_rejected(kind, K, kw, status):
+    with pytest.raises(agg.AggError) as e:
+        agg.plan(kind, 2, 2048, K, 256, 0, agg.options(**kw))
+    assert e.value.status == status
+
+
+def test_k_block_chunk_cap_and_split_k():
+    # 1024 row chunks x 2 K-blocks: past the 1024 chunks a source may have
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 2, 2048, 1024, 256, 1, agg.options(k_block=512))
+    assert e.value.status == agg.AGG_E_UNSUPPORTED
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 2, 128, 4096, 7168, 0, agg.options(k_block=512, k_splits=2, tile=13))
+    assert e.value.status == agg.AGG_E_UNSUPPORTED

@@ -80,17 +80,23 @@ CHUNK_ORDER = r"""
 #include <cstdio>
 #include "schedule.hpp"
 using namespace agg;
-// The send order by its definition: m-tile group after m-tile group, the
-// chunks each group needs first, source after source (parallel links), or
-// source after source (one serial link).
+// The send order by its definition.  Parallel links: K-block after K-block;
+// inside one, m-tile group after m-tile group, the row chunks each group
+// needs first, source after source.  One serial link: source after source,
+// each source's chunks in its own order (K-block major).  Chunk index
+// within a source: K-block * row chunks + row chunk.
 static bool by_definition(const Schedule& s, long c, int* src, int* j) {
     int remotes = s.n_shards - 1;
     if (s.link_model != 0) { *src = (int)(c / s.cps); *j = (int)(c % s.cps); return c < (long)remotes * s.cps; }
+    long per_kb = (long)remotes * s.rcs;
+    if (c >= per_kb * s.nkb) return false;
+    int kb = (int)(c / per_kb);
+    c %= per_kb;
     int prev = 0;
     for (int g = 0; g < s.mt; ++g) {
         int cur = need_chunks(s, g);
         long span = (long)(cur - prev) * remotes;
-        if (c < span) { *src = (int)(c / (cur - prev)); *j = prev + (int)(c % (cur - prev)); return true; }
+        if (c < span) { *src = (int)(c / (cur - prev)); *j = kb * s.rcs + prev + (int)(c % (cur - prev)); return true; }
         c -= span; prev = cur;
     }
     return false;
@@ -99,11 +105,13 @@ int main() {
     long checked = 0;
     const int Ss[] = {1, 7, 63, 64, 100, 128, 1000, 1024, 4096, 8192, 65536};
     const int tms[] = {32, 64, 128, 256};
+    const int nkbs[] = {1, 3, 8};
     for (int S : Ss) for (int tm : tms) for (int n = 2; n <= 9; n += 3) for (int lm = 0; lm < 2; ++lm)
+    for (int nkb : nkbs)
     for (int cr = 1; cr <= S; cr = cr < 8 ? cr + 1 : cr * 2 + (cr % 3)) {
         Schedule s{};
         s.n_shards = n; s.link_model = lm; s.cr = cr; s.S = S; s.tm = tm;
-        s.cps = (int)cdiv(S, cr); s.mt = (int)cdiv(S, tm);
+        s.rcs = (int)cdiv(S, cr); s.nkb = nkb; s.cps = s.rcs * nkb; s.mt = (int)cdiv(S, tm);
         if (s.cps > kFlagCap) continue;
         for (int i = 0; i < n; ++i) s.order[i] = (i * 5 + 1) % n;
         long total = (long)(n - 1) * s.cps;
@@ -112,8 +120,9 @@ int main() {
             bool in = c >= 0 && by_definition(s, c, &src, &j);
             ChunkRef r = chunk_at(s, c);
             if (!in) { if (r.src != -1) { printf("range S=%d cr=%d tm=%d c=%ld\n", S, cr, tm, c); return 1; } continue; }
-            if (r.src != src || r.j != j || r.shard != s.order[1 + src]) {
-                printf("S=%d cr=%d tm=%d n=%d lm=%d c=%ld: %d/%d vs %d/%d\n", S, cr, tm, n, lm, c, r.src, r.j, src, j);
+            if (r.src != src || r.j != j || r.shard != s.order[1 + src] ||
+                r.j != r.kb * s.rcs + r.jr || r.jr < 0 || r.jr >= s.rcs || r.kb < 0 || r.kb >= nkb) {
+                printf("S=%d cr=%d tm=%d n=%d lm=%d nkb=%d c=%ld: %d/%d vs %d/%d\n", S, cr, tm, n, lm, nkb, c, r.src, r.j, src, j);
                 return 1;
             }
             ++checked;
@@ -128,8 +137,9 @@ int main() {
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ needed")
 def test_chunk_order_closed_form_matches_definition(tmp_path):
     """chunk_at's constant-time form (used for every producer piece) gives
-    the send order defined group by group: for many shard, chunk and tile
-    heights, both link models, every position and one past each end."""
+    the send order defined K-block by K-block and group by group: for many
+    shard, chunk and tile heights, 1, 3 and 8 K-blocks, both link models,
+    every position and one past each end."""
     src = tmp_path / "chunks.cpp"
     src.write_text(CHUNK_ORDER)
     exe = tmp_path / "chunks"
@@ -138,3 +148,61 @@ def test_chunk_order_closed_form_matches_definition(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout
     assert int(out.stdout) > 100000
+
+
+PACED = r"""
+#include <cstdio>
+#include <initializer_list>
+#include "schedule.hpp"
+using namespace agg;
+// paced_bytes(chunk) is the bytes of the source's chunks up to and
+// including it in the source's own order (parallel links), plus every
+// earlier source whole (serial link): summed chunk by chunk here.
+int main() {
+    long checked = 0;
+    const int Ss[] = {1, 33, 100, 1024};
+    const long Ks[] = {1024, 2560, 4096};
+    for (int S : Ss) for (long K : Ks) for (int lm = 0; lm < 2; ++lm)
+    for (long kbk : {256L, 512L, 1024L, 4096L}) for (int cr : {1, 7, 16, 100}) {
+        if (cr > S) continue;
+        Schedule s{};
+        s.n_shards = 4; s.link_model = lm; s.cr = cr; s.S = S; s.K = K; s.tm = 64;
+        s.rcs = (int)cdiv(S, cr); s.kbk = kbk < K ? kbk : K; s.nkb = (int)(K / s.kbk);
+        s.cps = s.rcs * s.nkb; s.mt = (int)cdiv(S, s.tm);
+        if (s.cps > kFlagCap) continue;
+        for (int i = 0; i < 4; ++i) s.order[i] = i;
+        for (int src = 0; src < 3; ++src) {
+            long sum = lm ? (long)src * S * K * 2 : 0;
+            for (int j = 0; j < s.cps; ++j) {
+                ChunkRef r; r.src = src; r.shard = src + 1; r.j = j; r.kb = j / s.rcs; r.jr = j % s.rcs;
+                const long rows = chunk_row_end(s, r.jr) - (long)r.jr * cr;
+                sum += rows * (kblock_end(s, r.kb) - kblock_begin(s, r.kb)) * 2;
+                if (paced_bytes(s, r, 2) != sum) {
+                    printf("S=%d K=%ld kbk=%ld cr=%d lm=%d src=%d j=%d: %ld vs %ld\n", S, K, kbk, cr,
+                           lm, src, j, (long)paced_bytes(s, r, 2), sum);
+                    return 1;
+                }
+                ++checked;
+            }
+            if (sum != (lm ? (long)(src + 1) : 1L) * S * K * 2) { printf("total\n"); return 1; }
+        }
+    }
+    printf("%ld\n", checked);
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ needed")
+def test_paced_bytes_follow_each_sources_order(tmp_path):
+    """The emulated link's byte count for a chunk is what the source has
+    sent up to and including it: K-blocks before it whole, then its
+    K-block's rows up to its last; the serial link adds earlier sources."""
+    src = tmp_path / "paced.cpp"
+    src.write_text(PACED)
+    exe = tmp_path / "paced"
+    subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout
+    assert int(out.stdout) > 10000
