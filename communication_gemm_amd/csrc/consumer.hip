@@ -605,55 +605,91 @@ __device__ __forceinline__ void store_tile(
 }
 
 // Wave 0 of a workgroup: wait until chunks [0, need) of source `shard` are
-// released, and acquire them.  What the workgroup has already seen of the
-// source is kept in seen[shard], so a satisfied wait touches no memory.
-// Returns 0 after a time-out or a failure elsewhere in the call.
+// known released, `have` of them known already.  Either of the PTO-ISA
+// README's two structures says so: the source's summary counter covering
+// `need`, or the chunk flags of [have, need) all holding the call's epoch.
+// The counter moves only once the chunk before the first unflagged one is
+// flagged (and then in a compare-and-swap after a flag walk), so it lags the
+// flags; the flags alone cost one wave-wide load per 64 chunks.  Each poll
+// issues the counter load and the flag loads together: one memory round
+// trip.  A flag is stored only after its chunk's data (every piece of it,
+// whoever copied it) was performed in memory, and the counter passes a
+// chunk only after some wave saw its flag, so either vouches for the data.
+// Returns the chunks now known released (>= need), or 0 after a time-out or
+// a failure elsewhere in the call.
+__device__ __forceinline__ uint32_t poll_ready(const ConsumerArgs& a, int shard, uint32_t have,
+                                               uint32_t need, int tid)
+{
+    const uint32_t base = a.base[shard];
+    const uint32_t* ctr = a.counters + shard * (kCounterStride / 4);
+    const uint32_t* fl = a.flags + shard * kFlagCap;
+    uint64_t t0 = 0;
+    uint32_t spins = 0;
+    for (;;) {
+        const uint32_t c = load_agent(ctr);          // one request for the wave
+        const uint32_t j = have + (uint32_t)tid;
+        const bool set = j >= need || load_agent(fl + j) == a.epoch;
+        const uint32_t cur = __builtin_amdgcn_readfirstlane(c) - base;
+        if (cur >= need && cur <= (uint32_t)kFlagCap) return cur;
+        const uint64_t unset = __builtin_amdgcn_ballot_w64(!set);
+        if (!unset) {
+            if (have + 64 >= need) return need;
+            have += 64;                              // the next 64 at once
+            continue;
+        }
+        have += (uint32_t)__builtin_ctzll(unset);    // the flagged run so far
+        if (spins == 0) t0 = ticks();
+        __builtin_amdgcn_s_sleep(2);
+        if ((++spins & 31u) == 0) {
+            if (reached(__builtin_amdgcn_readfirstlane(load_agent(a.err)), a.epoch)) return 0;
+            if (ticks() - t0 > a.limit) {
+                if (tid == 0) raise_error(a.err, a.epoch);
+                return 0;
+            }
+        }
+    }
+}
+
+// Wave 0 of a workgroup, before a tile: wait until chunks [0, need) of
+// source `shard` are released (poll_ready), then acquire: an agent-scope
+// fence, which invalidates this CU's L1 and this XCD's L2 and so drops any
+// line an earlier call left at these workspace addresses.  What the
+// workgroup has already seen of the source is kept in seen[shard], so a
+// satisfied wait touches no memory.  Returns 0 after a time-out or a
+// failure elsewhere in the call.
 __device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int need,
                                            uint32_t* seen, int tid)
 {
     const uint32_t have = seen[shard];
     if (have >= (uint32_t)need) return 1;
-    const uint32_t base = a.base[shard];
-    const uint32_t target = base + (uint32_t)need;
-    uint32_t v = target;
-    if (tid == 0)
-        v = poll_until(a.counters + shard * (kCounterStride / 4), target, a.err, a.epoch,
-                       a.limit);
-    v = __builtin_amdgcn_readfirstlane(v);
-    if (!reached(v, target)) return 0;
-    // the chunks the counter vouches for carry their copier's flag;
-    // reading them, then acquiring, pairs with each copier's release
-    const uint32_t upto = v - base;
-    const uint32_t* fl = a.flags + shard * kFlagCap;
-    bool mine = true;
-    for (uint32_t c = have + tid; c < upto; c += 64)
-        mine = mine && poll_flag(fl + c, a.epoch, a.err, a.limit);
-    const int ok = __builtin_amdgcn_ballot_w64(!mine) == 0;
+    const uint32_t got = poll_ready(a, shard, have, (uint32_t)need, tid);
+    if (!got) return 0;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (tid == 0 && ok) seen[shard] = upto;
-    return ok;
+    if (tid == 0) seen[shard] = got;
+    return 1;
 }
 
-// Wave 0 inside a tile's K loop: wait until the source's counter reaches
-// `need` (relative to the call's base), then acquire.  No flag walk: the
-// counter passes chunk j only after a producer wave saw j's flag set, and
-// that flag was stored after j's data stores were performed in memory, so
-// the counter alone vouches for the data (the walk at a tile's start pairs
-// with each copier in the same way).  Kept small: it is inlined into the
-// software-pipelined loop, beside the live accumulators.
+// Wave 0 inside a tile's K loop: the same wait, with no acquire fence,
+// which on gfx950 invalidates the CU's L1 and the whole L2 of the XCD (the
+// panels every other workgroup there is sharing).  None is needed here:
+//   * a load of a chunk is issued only after its release was seen, and the
+//     release comes after the chunk's data stores (write-through) were
+//     performed in memory;
+//   * so a load can only be served stale data by a cache line that held
+//     the address before the data was written.  In this call nobody reads
+//     a chunk before its release (every read is gated) and chunk edges are
+//     cache-line edges (rows and K-blocks are whole KiB), so such a line
+//     can only be left over from an earlier call -- and the acquire at this
+//     tile's first wait, after which this wave issues every load of the
+//     tile, dropped every such line from this CU's L1 and this XCD's L2.
 __device__ __forceinline__ int wait_counter(const ConsumerArgs& a, int shard, int need,
                                             uint32_t* seen, int tid)
 {
-    if (seen[shard] >= (uint32_t)need) return 1;
-    const uint32_t target = a.base[shard] + (uint32_t)need;
-    uint32_t v = target;
-    if (tid == 0)
-        v = poll_until(a.counters + shard * (kCounterStride / 4), target, a.err, a.epoch,
-                       a.limit);
-    v = __builtin_amdgcn_readfirstlane(v);
-    if (!reached(v, target)) return 0;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (tid == 0) seen[shard] = v - a.base[shard];
+    const uint32_t have = seen[shard];
+    if (have >= (uint32_t)need) return 1;
+    const uint32_t got = poll_ready(a, shard, have, (uint32_t)need, tid);
+    if (!got) return 0;
+    if (tid == 0) seen[shard] = got;
     return 1;
 }
 

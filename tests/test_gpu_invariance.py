@@ -235,3 +235,33 @@ def test_k_blocks_withheld_chunk_times_out_inside_a_tile(agg, data, ref):
     assert agg.check() == agg.AGG_E_TIMEOUT
     assert torch.equal(call(agg, data, 8, k_block=512), ref)
     assert torch.equal(call(agg, data), ref)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(link_gbps=40.0), dict(k_block=512),
+                                dict(k_block=512, link_gbps=40.0),
+                                dict(k_block=512, chunk_rows=1), dict(mode=2)])
+def test_alternating_contents_on_one_workspace(agg, orc, data, ref, kw):
+    """Two different sets of shards, in turn, through one caller-owned
+    workspace: each call must give its own data's result.  The rows of
+    consecutive calls sit at the same workspace addresses, so a cache line
+    left over from the previous call would show here (with the same data in
+    every call it could not)."""
+    ts, B = data[0], data[1]
+    shards2, _ = synth.make_f16(4 * 512, 1024, 768, 4, "normal", 50500)
+    ts2 = [dev(s, torch) for s in shards2]
+    C2 = torch.full_like(ref, float("nan"))
+    agg.ag_gemm_f16(ts2, B, C2, 0)
+    assert agg.check() == 0
+    Co, So = orc.ag_gemm_f16(shards2, data[3])
+    check_f16(C2.cpu().numpy(), Co, So, "second data set")
+    M, K = ts[0].shape[0] * len(ts), ts[0].shape[1]
+    ws = torch.empty(agg.workspace_bytes(len(ts), M, K, 2), dtype=torch.uint8, device="cuda")
+    agg.workspace_reset(ws)
+    kw = dict(kw)
+    cr = kw.pop("chunk_rows", 0)
+    for it in range(10):
+        src, want = (ts, ref) if it % 2 == 0 else (ts2, C2)
+        C = torch.full_like(ref, float("nan"))
+        agg.ag_gemm_f16(src, B, C, cr, opts=agg.options(workspace=ws, **kw))
+        assert agg.check() == 0
+        assert torch.equal(C, want), f"call {it} {kw}"
