@@ -9,6 +9,9 @@ namespace agg {
 
 namespace {
 
+// K-blocks of the automatic 2-D chunks.
+constexpr int kAutoKBlocks = 4;
+
 // Output tiles the consumer kernels are instantiated for, largest first.
 // Ids 1, 6, 7, 8 and 9 are the same 256 x 256 tile with different K
 // pipelines and wave grids (see the Cfg table of the consumer); 8 (eight
@@ -246,20 +249,31 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         }
         s.ring = opt->workspace_stages;
     }
-    s.rcs = S > 0 ? (int)cdiv(S, s.cr) : 0;
     // K-blocks (2-D chunks): whole KiB of every row segment, so that the
     // producer's 1 KiB vectors never straddle two rows
     if (opt->k_block < 0) return AGG_E_INVALID;
     s.nkb = 1;
     s.kbk = K;
+    const int64_t kib = 1024 / elt_bytes(kind);
+    const bool two_d_ok = s.ring == 0 && opt->scheme == AGG_SCHEME_COUNTERS && s.ks == 1;
     if (opt->k_block > 0 && opt->k_block < K) {
-        const int64_t kib = 1024 / elt_bytes(kind);
         if (opt->k_block % kib || K % kib) return AGG_E_UNSUPPORTED;
-        if (s.ring > 0 || opt->scheme != AGG_SCHEME_COUNTERS || s.ks > 1)
-            return AGG_E_UNSUPPORTED;
+        if (!two_d_ok) return AGG_E_UNSUPPORTED;
         s.kbk = opt->k_block;
         s.nkb = (int)(K / s.kbk);           // the last K-block takes the rest
+    } else if (opt->k_block == 0 && chunk_rows == 0 && two_d_ok && K % (kAutoKBlocks * kib) == 0 &&
+               n_shards > 1 && S > 0) {
+        // Automatic chunks where K-blocks are allowed: S/16 rows x a quarter
+        // of K, still 64 chunks per source (the PTO-ISA README's 64-128).
+        // Measured against whole-K chunks of S/64 rows (interleaved, one
+        // box): 147 against 176 us on 4 x 1024 rows at K = N = 4096 paced at
+        // 153 GB/s per link, level (277 / 279 us, 40 / 39 us) on 8 x 1024
+        // rows at K = N = 4096 and on 2 x 1024 rows at K = 2048, N = 1024.
+        s.kbk = K / kAutoKBlocks;
+        s.nkb = kAutoKBlocks;
+        s.cr = (int)(S / 16 > 0 ? S / 16 : 1);
     }
+    s.rcs = S > 0 ? (int)cdiv(S, s.cr) : 0;
     if ((int64_t)s.rcs * s.nkb > kFlagCap && n_shards > 1) return AGG_E_UNSUPPORTED;
     s.cps = s.rcs * s.nkb;
     s.pv = opt->scheme == AGG_SCHEME_BARRIER ? (opt->pvalue > 0 ? opt->pvalue : 1) : 0;

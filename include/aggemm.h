@@ -193,8 +193,11 @@ typedef struct agg_options {
                                (agg_plan_info.workspace_bytes).  The sum
                                order is fixed, so results do not depend on
                                which part finishes last.                   */
-    int64_t k_block;        /* elements of K per chunk; 0 (default) or >= K:
-                               a chunk spans all of K.  Otherwise a chunk is
+    int64_t k_block;        /* elements of K per chunk; 0 (default): the
+                               automatic choice that goes with chunk_rows 0
+                               (see ag_gemm_f16), or all of K for an
+                               explicit chunk_rows; >= K: a chunk spans all
+                               of K.  Otherwise a chunk is
                                chunk_rows rows x one K-block of this many
                                elements (the last K-block also takes the
                                remainder of K): the chunk flag matrix of the
@@ -222,7 +225,12 @@ void ag_gemm_options_init(agg_options *opt);
  *   B          DEVICE fp16 [K, N] row-major, 16-byte aligned.
  *   C          DEVICE fp32 [M, N] row-major, fully overwritten; must not
  *              alias any input.
- *   chunk_rows rows per chunk; 0 = ag_gemm_pick_chunk_rows(S).
+ *   chunk_rows rows per chunk; 0 = automatic: with agg_options.k_block
+ *              also 0 and K-blocks allowed (K a multiple of 4 KiB of
+ *              elements, the counters scheme, no workspace ring or
+ *              split-K), S/16 rows x one quarter of K (64 chunks per
+ *              source); otherwise ag_gemm_pick_chunk_rows(S) rows x all of
+ *              K.  agg_plan_info reports the choice.
  * Requires K % 8 == 0 and N % 8 == 0 (AGG_E_UNSUPPORTED otherwise).
  * Size limits (both paths, AGG_E_UNSUPPORTED past them): n_shards <= 64,
  * S <= 2^30, K <= 2^21, N <= 2^20, at most 1024 chunks per shard, and one
@@ -325,8 +333,10 @@ int ag_gemm_i8_dequant_ex(const int8_t *const *shards, int n_shards,
                           const agg_options *opt);
 
 /*
- * Rows per chunk so that each source has 64 to 127 chunks: max(1, S / 64)
- * (PTO-ISA README, "dynamic chunk size": 64-128 chunks per source).
+ * Rows per chunk so that each source has 64 to 127 chunks of all of K:
+ * max(1, S / 64) (PTO-ISA README, "dynamic chunk size": 64-128 chunks per
+ * source).  The automatic choice for whole-K chunks; where K-blocks are
+ * allowed the automatic chunks are S/16 rows x K/4 (see ag_gemm_f16).
  * Returns 0 for S < 1.
  */
 int ag_gemm_pick_chunk_rows(int64_t shard_rows);

@@ -396,10 +396,11 @@ def test_k_block_plan():
     assert (chunks[:7 * R, 1] < R).all() and (chunks[7 * R:14 * R, 1] // R == 1).all()
     # inside a K-block, m-tile group by group across sources, as without
     # K-blocks: the first 16 row chunks of each of the 7 sources, then the next
-    one, _, c1 = agg.plan("f16", 8, 8192, 4096, 4096, 0, None, orders=True)
+    one, _, c1 = agg.plan("f16", 8, 8192, 4096, 4096, 16, None, orders=True)
+    assert one.k_blocks == 1 and one.chunk_rows == 16
     assert (chunks[:7 * R] == c1).all()
     # the tile order (and each tile's first wait) is unchanged
-    _, t1, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0, None, orders=True)
+    _, t1, _ = agg.plan("f16", 8, 8192, 4096, 4096, 16, None, orders=True)
     assert (tiles == t1).all()
 
 
@@ -438,3 +439,26 @@ def test_k_block_chunk_cap_and_split_k():
     with pytest.raises(agg.AggError) as e:
         agg.plan("f16", 2, 128, 4096, 7168, 0, agg.options(k_block=512, k_splits=2, tile=13))
     assert e.value.status == agg.AGG_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kind,n,M,K,N,opts,cr,nkb", [
+    ("f16", 8, 8192, 4096, 4096, {}, 64, 4),          # S/16 rows x K/4
+    ("f16", 4, 4096, 4096, 4096, {}, 64, 4),
+    ("f16", 2, 2048, 2048, 1024, {}, 64, 4),
+    ("bf16", 8, 8192, 4096, 4096, {}, 64, 4),
+    ("fp8", 8, 8192, 4096, 4096, {}, 64, 4),          # int8/fp8: K/4 whole KiB
+    ("i8", 2, 16384, 27392, 4096, {}, 128, 1),        # K not a multiple of 4 KiB
+    ("f16", 2, 256, 256, 128, {}, 2, 1),              # K too small: S/64 rows
+    ("f16", 8, 8192, 4096, 4096, {"workspace_stages": 2}, 16, 1),
+    ("f16", 8, 8192, 4096, 4096, {"scheme": 1}, 16, 1),
+    ("f16", 8, 8192, 4096, 4096, {"k_block": 4096}, 16, 1),   # explicitly whole K
+])
+def test_automatic_chunks(kind, n, M, K, N, opts, cr, nkb):
+    info, _, _ = agg.plan(kind, n, M, K, N, 0, agg.options(**opts))
+    assert (info.chunk_rows, info.k_blocks) == (cr, nkb)
+    if nkb > 1:
+        assert info.chunks_per_source == 64 and info.k_block == K // 4
+    # an explicit chunk size keeps whole-K chunks
+    info, _, _ = agg.plan(kind, n, M, K, N, 8, agg.options(**{k: v for k, v in opts.items()
+                                                               if k != "k_block"}))
+    assert info.k_blocks == 1
