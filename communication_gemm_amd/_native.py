@@ -56,6 +56,8 @@ class Options(ctypes.Structure):
         ("trace", ctypes.c_void_p),
         ("producer_piece_bytes", ctypes.c_int64),
         ("k_splits", ctypes.c_int),
+        ("debug_delay_us", ctypes.c_double),
+        ("debug_delay_seed", ctypes.c_uint32),
         ("k_block", ctypes.c_int64),
     ]
 

@@ -137,7 +137,7 @@ struct PlanKey {
     uint32_t struct_size;
     int local_shard, mode, link_model, producer_wgs, consumer_wgs, tile;
     int workspace_stages, scheme, pvalue, k_splits, debug_drop_chunk;
-    double link_gbps, timeout_ms;
+    double link_gbps, timeout_ms, delay_us;
     int64_t piece, k_block;
     int has_order;
     int order[kMaxShards];
@@ -179,6 +179,7 @@ void plan_key(PlanKey* k, Kind kind, int n, int64_t M, int64_t K, int64_t N, int
     k->debug_drop_chunk = o->debug_drop_chunk;
     k->link_gbps = o->link_gbps;
     k->timeout_ms = o->timeout_ms;
+    k->delay_us = o->debug_delay_us;
     k->piece = o->producer_piece_bytes;
     k->k_block = o->k_block;
     k->has_order = o->send_order != nullptr;
@@ -384,6 +385,8 @@ int run(const Call& c)
     pa.epoch = epoch;
     pa.elt = p.elt;
     pa.drop = p.drop_chunk;
+    pa.delay_seed = opt->debug_delay_seed;
+    pa.delay_max = (uint32_t)(opt->debug_delay_us * 1e-6 * d->clock_hz);
     pa.ticks_per_byte = p.link_gbps > 0 ? d->clock_hz / (p.link_gbps * 1e9) : 0.0;
     pa.limit = limit;
     // the producer's wait for the consumer's start covers the work queued

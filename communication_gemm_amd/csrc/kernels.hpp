@@ -25,6 +25,8 @@ struct ProducerArgs {
     uint32_t epoch;
     int elt;                       // bytes per element
     int64_t drop;                  // producer position whose release is withheld
+    uint32_t delay_seed;           // test hook: each piece starts after a pseudo-random
+    uint32_t delay_max;            // delay in [0, delay_max] ticks (0: none)
     double ticks_per_byte;         // pacing; 0 = unpaced
     uint64_t limit;                // wait limit in clock ticks
     uint64_t* trace;               // optional timestamps (see agg_options.trace)

@@ -144,6 +144,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         return AGG_E_INVALID;
     if (opt->k_splits < 0) return AGG_E_INVALID;
     if (!(opt->timeout_ms >= 0.0)) return AGG_E_INVALID;
+    if (!(opt->debug_delay_us >= 0.0) || isinf(opt->debug_delay_us)) return AGG_E_INVALID;
     if (num_cus <= 0) num_cus = 256;
     // Row and element offsets are formed in 64-bit; per-tile loop counters
     // in 32-bit.

@@ -93,6 +93,20 @@ __device__ void advance(uint32_t* ctr, const uint32_t* flags, uint32_t base, int
     }
 }
 
+// Test hook: a pseudo-random delay for item `item` (a hash of the seed
+// and the item: 32-bit multiply-xorshift mixing), so that pieces, and with
+// them chunks, complete in an order unrelated to the send order.
+__device__ __forceinline__ uint32_t item_delay(uint32_t seed, uint32_t item, uint32_t max)
+{
+    uint32_t h = seed * 0x9E3779B9u ^ item;
+    h ^= h >> 16;
+    h *= 0x7FEB352Du;
+    h ^= h >> 15;
+    h *= 0x846CA68Bu;
+    h ^= h >> 16;
+    return h % (max + 1u);
+}
+
 __device__ __forceinline__ int32_t uniform(int32_t x)
 {
     return __builtin_amdgcn_readfirstlane(x);
@@ -249,6 +263,13 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
         }
         total = (uint32_t)(r.shard * kFlagCap + r.j);
         weight = piece_weight((int)q, a.ppc);
+        if (a.delay_max) {
+            const uint32_t d = __builtin_amdgcn_readfirstlane(
+                item_delay(a.delay_seed, (uint32_t)uniform(chunk) * ppc + (uint32_t)uniform((int32_t)q),
+                           a.delay_max));
+            const uint64_t t = ticks();
+            while (ticks() - t < d) __builtin_amdgcn_s_sleep(1);
+        }
         const int64_t rows = chunk_row_end(s, r.jr) - row0;
         const int64_t k0 = kblock_begin(s, r.kb);
         const int64_t sb = (kblock_end(s, r.kb) - k0) * a.elt;   // bytes per row segment

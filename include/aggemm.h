@@ -193,6 +193,14 @@ typedef struct agg_options {
                                (agg_plan_info.workspace_bytes).  The sum
                                order is fixed, so results do not depend on
                                which part finishes last.                   */
+    double debug_delay_us;  /* test hook: each producer piece starts after a
+                               pseudo-random delay in [0, debug_delay_us]
+                               (a hash of debug_delay_seed and the piece),
+                               so pieces and chunks complete in an order
+                               unrelated to the send order; 0 = off; must be
+                               below the time limit (AGG_E_INVALID if
+                               negative or not finite)                     */
+    uint32_t debug_delay_seed;
     int64_t k_block;        /* elements of K per chunk; 0 (default): the
                                automatic choice that goes with chunk_rows 0
                                (see ag_gemm_f16), or all of K for an

@@ -265,3 +265,40 @@ def test_alternating_contents_on_one_workspace(agg, orc, data, ref, kw):
         agg.ag_gemm_f16(src, B, C, cr, opts=agg.options(workspace=ws, **kw))
         assert agg.check() == 0
         assert torch.equal(C, want), f"call {it} {kw}"
+
+
+@pytest.mark.parametrize("kw", [
+    dict(debug_delay_us=30.0, debug_delay_seed=1),
+    dict(debug_delay_us=30.0, debug_delay_seed=2, chunk_rows=1),
+    dict(debug_delay_us=20.0, debug_delay_seed=3, producer_piece_bytes=8192, chunk_rows=64),
+    dict(debug_delay_us=30.0, debug_delay_seed=4, k_block=512, chunk_rows=8),
+    dict(debug_delay_us=30.0, debug_delay_seed=5, k_block=512, link_gbps=40.0),
+    dict(debug_delay_us=30.0, debug_delay_seed=6, link_model=1, chunk_rows=16),
+    dict(debug_delay_us=10.0, debug_delay_seed=7, workspace_stages=2, chunk_rows=8),
+])
+def test_random_completion_order(agg, data, ref, kw):
+    """Seeded random delays before every producer piece: pieces and chunks
+    complete in an order unrelated to the send order (the flag walk and the
+    counter must still release exactly the chunks whose pieces are all in).
+    The output stays bitwise the same."""
+    kw = dict(kw)
+    cr = kw.pop("chunk_rows", 0)
+    for rep in range(2):
+        C = call(agg, data, cr, **dict(kw, debug_delay_seed=kw["debug_delay_seed"] + 100 * rep))
+        assert torch.equal(C, ref), (kw, rep)
+
+
+def test_random_completion_order_nan_poisoned(agg, data, ref):
+    ts, B = data[0], data[1]
+    M, K = ts[0].shape[0] * len(ts), ts[0].shape[1]
+    ws = torch.empty(agg.workspace_bytes(len(ts), M, K, 2) // 2, dtype=torch.float16,
+                     device="cuda")
+    for it in range(4):
+        ws.fill_(float("nan"))
+        agg.workspace_reset(ws)
+        C = torch.full_like(ref, float("nan"))
+        agg.ag_gemm_f16(ts, B, C, [1, 8, 0, 8][it], opts=agg.options(
+            workspace=ws, debug_delay_us=25.0, debug_delay_seed=40 + it,
+            k_block=[0, 512, 0, 512][it]))
+        assert agg.check() == 0
+        assert torch.equal(C, ref), f"iteration {it}"
