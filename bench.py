@@ -96,6 +96,8 @@ def parse():
                     help="skip the ring-variant runs (D = 2, 4, 8)")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip the pipelined chunk-size sweep")
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip the producer variants (DMA engines, reserved CUs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--ramp-calls", type=int, default=1000,
                     help="untimed calls before the warm-up that bring the clocks out of idle")
@@ -530,6 +532,60 @@ def run_variant(args, torch, agg, synth, kind):
             "consumer_frac_of_peak": round(flops / (c * 1e-3) / 1e12 / peak, 4)}
 
 
+PRODUCERS = {"kernel": dict(), "sdma": dict(producer=1), "kernel_32cus": dict(producer_cus=32),
+             "kernel_64cus": dict(producer_cus=64)}
+
+
+def producer_variants(torch, agg, synth, i8_inputs=None):
+    """What moves the chunks: the producer kernel on every CU (default), the
+    DMA engines, or the producer kernel on 32 or 64 CUs of its own.
+    Pipelined and copy-only medians, the variants taken in turn.  The DMA
+    engines cannot be paced, so C3 runs unpaced here (its link rate
+    belongs to the emulated link, not to the engine that copies)."""
+    out = {}
+    for cid in (3, 4, 5):
+        c = synth.CASES[cid]
+        if c.kind == "i8":
+            if i8_inputs is None:
+                continue
+            w = I8Workload(torch, agg, c, i8_inputs)
+
+            def prep(mode, kw, w=w):
+                return agg.ag_gemm_i8_dequant(
+                    w.ts, w.tB, w.tb, w.tsc, w.C, 0,
+                    opts=agg.options(workspace=w.ws, mode=mode, **kw), prepare=True)
+        else:
+            w = F16Workload(torch, agg, c, synth.make_case(c), link_gbps=0.0)
+
+            def prep(mode, kw, w=w):
+                return w.prep(mode, **kw)
+        calls = {name: {m: prep(MODES[m], kw) for m in ("pipelined", "copy", "compute")}
+                 for name, kw in PRODUCERS.items()}
+        ramp(torch, calls["kernel"]["pipelined"], seconds=0.3)
+        res = {name: {"pipelined": [], "copy": []} for name in PRODUCERS}
+        n = 10 if c.kind == "i8" else 20
+        comp = []
+        for _ in range(3):
+            comp.append(timed(torch, lambda ev: calls["kernel"]["compute"], n, 2,
+                              with_consumer=False)[0])
+            for name in PRODUCERS:
+                for m in ("pipelined", "copy"):
+                    t, _ = timed(torch, lambda ev, f=calls[name][m]: f, n, 2, with_consumer=False)
+                    res[name][m].append(t)
+        if agg.check():
+            raise SystemExit("producer variants failed")
+        t_comp = float(np.median(comp))
+        entry = {"workload": c.name + (" (unpaced)" if cid == 3 else ""),
+                 "compute_ms": round(t_comp, 5)}
+        for name in PRODUCERS:
+            tp, tc = float(np.median(res[name]["pipelined"])), float(np.median(res[name]["copy"]))
+            entry[name] = {"pipelined_ms": round(tp, 5), "copy_ms": round(tc, 5),
+                           "hidden_fraction": round((t_comp + tc - tp) / tc, 4)}
+        out[f"C{cid}"] = entry
+        del w, calls
+    return out
+
+
 def vendor_gemm(torch, w, steps=50):
     """hipBLASLt (torch.matmul) on the gathered A of the same workload, fp16
     in and fp16 out (torch has no fp32-output fp16 GEMM): a ceiling
@@ -741,6 +797,8 @@ def main():
             line["fp8"] = run_variant(args, torch, agg, synth, "fp8")
         if not args.no_ring:
             line["ring"] = run_ring(args, torch, agg, synth)
+        if not args.no_producers:
+            line["producers"] = producer_variants(torch, agg, synth, i8_inputs)
         line["vendor_gemm"] = vendor_gemm(torch, w)
         # 4. The timed steps again, after everything above has loaded the
         # board for tens of seconds.

@@ -20,6 +20,7 @@ NOALLOC_MAX_BYTES = 64 << 20   # AGG_NOALLOC_MAX_BYTES
 MODE_PIPELINED, MODE_COMPUTE_ONLY, MODE_SEQUENTIAL, MODE_COPY_ONLY = range(4)
 SCHEME_COUNTERS, SCHEME_BARRIER = range(2)
 LINKS_PARALLEL, LINKS_SERIAL = range(2)
+PRODUCER_KERNEL, PRODUCER_SDMA = range(2)
 MAX_SHARDS = 64
 
 
@@ -58,6 +59,8 @@ class Options(ctypes.Structure):
         ("k_splits", ctypes.c_int),
         ("debug_delay_us", ctypes.c_double),
         ("debug_delay_seed", ctypes.c_uint32),
+        ("producer", ctypes.c_int),
+        ("producer_cus", ctypes.c_int),
         ("k_block", ctypes.c_int64),
     ]
 

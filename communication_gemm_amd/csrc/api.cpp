@@ -34,6 +34,9 @@ struct Device {
     double clock_hz = 0;       // rate of the device's constant clock
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr;  // orders a ring-mode producer after the consumer
+    hipEvent_t join = nullptr;  // joins a CU-masked consumer back to the caller
+    hipStream_t pmask[3] = {};  // CU-masked producer / consumer streams, by
+    hipStream_t cmask[3] = {};  //   producer CUs / 32 (made on first use)
     char* scratch = nullptr;   // the allocation-free entry point's array here
     char* ws = nullptr;        // internal workspace
     size_t ws_bytes = 0;
@@ -99,6 +102,8 @@ int device_ready(Device& d, hipStream_t st)
         return AGG_E_HIP;
     if (!d.fork && hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess)
         return AGG_E_HIP;
+    if (!d.join && hipEventCreateWithFlags(&d.join, hipEventDisableTiming) != hipSuccess)
+        return AGG_E_HIP;
     void* p = nullptr;
     if (scratch_address(&p) != hipSuccess) {
         (void)hipGetLastError();
@@ -136,7 +141,7 @@ struct PlanKey {
     int64_t M, K, N;
     uint32_t struct_size;
     int local_shard, mode, link_model, producer_wgs, consumer_wgs, tile;
-    int workspace_stages, scheme, pvalue, k_splits, debug_drop_chunk;
+    int workspace_stages, scheme, pvalue, k_splits, debug_drop_chunk, producer, producer_cus;
     double link_gbps, timeout_ms, delay_us;
     int64_t piece, k_block;
     int has_order;
@@ -177,6 +182,8 @@ void plan_key(PlanKey* k, Kind kind, int n, int64_t M, int64_t K, int64_t N, int
     k->pvalue = o->pvalue;
     k->k_splits = o->k_splits;
     k->debug_drop_chunk = o->debug_drop_chunk;
+    k->producer = o->producer;
+    k->producer_cus = o->producer_cus;
     k->link_gbps = o->link_gbps;
     k->timeout_ms = o->timeout_ms;
     k->delay_us = o->debug_delay_us;
@@ -251,6 +258,63 @@ int internal_workspace(Device& d, size_t need, hipStream_t st, char** ws, Track*
     return AGG_OK;
 }
 
+// The CU-masked stream pair for a producer of `cus` CUs (32 or 64): the
+// producer's CUs spread evenly over the XCDs, the consumer's the rest.
+int masked_streams(Device& d, int cus, hipStream_t* prod, hipStream_t* cons)
+{
+    const int i = cus / 32;
+    if (!d.pmask[i]) {
+        uint32_t m[8];
+        producer_cu_mask(cus, m);
+        uint32_t c[8];
+        for (int w = 0; w < 8; ++w) c[w] = ~m[w];
+        hipStream_t ps = nullptr, cs = nullptr;
+        if (hipExtStreamCreateWithCUMask(&ps, 8, m) != hipSuccess) return AGG_E_HIP;
+        if (hipExtStreamCreateWithCUMask(&cs, 8, c) != hipSuccess) {
+            (void)hipStreamDestroy(ps);
+            return AGG_E_HIP;
+        }
+        d.pmask[i] = ps;
+        d.cmask[i] = cs;
+    }
+    *prod = d.pmask[i];
+    *cons = d.cmask[i];
+    return AGG_OK;
+}
+
+// The DMA producer (AGG_PRODUCER_SDMA): row group after row group in send
+// order (group g: the row chunks m-tile g needs first), one copy per remote
+// source on the DMA engines, then a stream write of the source's counter
+// past the group's chunks -- the release, which the stream performs only
+// after the copy has completed.  Chunks span all of K here.
+hipError_t enqueue_sdma(const Schedule& s, const ProducerArgs& pa, int elt, hipStream_t st)
+{
+    const size_t row_bytes = (size_t)s.K * (size_t)elt;
+    const int remotes = s.n_shards - 1;
+    auto group = [&](int src, int g) -> hipError_t {
+        const int shard = s.order[1 + src];
+        const int f = g == 0 ? 0 : need_chunks(s, g - 1);
+        const int e = need_chunks(s, g);
+        if (e <= f) return hipSuccess;   // chunks taller than a tile: empty group
+        const int64_t r0 = (int64_t)f * s.cr, r1 = chunk_row_end(s, e - 1);
+        hipError_t err = hipMemcpyAsync(pa.dst[shard] + r0 * row_bytes, pa.src[shard] + r0 * row_bytes,
+                                        (size_t)(r1 - r0) * row_bytes,
+                                        hipMemcpyDeviceToDeviceNoCU, st);
+        if (err != hipSuccess) return err;
+        return hipStreamWriteValue32(st, pa.counters + shard * (kCounterStride / 4),
+                                     pa.base[shard] + (uint32_t)e, 0);
+    };
+    hipError_t err = hipSuccess;
+    if (s.link_model == 0) {
+        for (int g = 0; g < s.mt && err == hipSuccess; ++g)
+            for (int src = 0; src < remotes && err == hipSuccess; ++src) err = group(src, g);
+    } else {
+        for (int src = 0; src < remotes && err == hipSuccess; ++src)
+            for (int g = 0; g < s.mt && err == hipSuccess; ++g) err = group(src, g);
+    }
+    return err;
+}
+
 struct Call {
     Kind kind;
     const void* const* shards;
@@ -295,6 +359,8 @@ int run(const Call& c)
         }
     }
     if (opt->trace && !aligned(opt->trace, 8)) return AGG_E_UNSUPPORTED;
+    // DMA copies leave no release stamps
+    if (opt->trace && opt->producer == AGG_PRODUCER_SDMA) return AGG_E_UNSUPPORTED;
     if (c.scratch && opt->workspace) return AGG_E_INVALID;
 
     // Every argument check runs before anything is created or enqueued:
@@ -399,7 +465,8 @@ int run(const Call& c)
     int cwgs = p.consumer_wgs;
     // a persistent grid larger than what can be resident at once gains
     // nothing, and its waiting workgroups would sit in front of the producer
-    if (cwgs > d->num_cus * occ) cwgs = d->num_cus * occ;
+    const int ccus = d->num_cus - p.producer_cus;
+    if (cwgs > ccus * occ) cwgs = ccus * occ;
     // No slots are held back for the producer: every consumer kernel leaves
     // room for producer waves on each CU even at full occupancy.
     // Workgroups of one XCD take neighbouring tiles (the grid is now final).
@@ -418,6 +485,7 @@ int run(const Call& c)
         return e;
     };
 
+    const bool sdma = p.producer == AGG_PRODUCER_SDMA;
     hipError_t e = hipSuccess;
     if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer) {
         // The consumer goes first so that its persistent workgroups are all
@@ -438,6 +506,34 @@ int run(const Call& c)
         ca.start = header + kStartOffset / 4;
         pa.start = header + kStartOffset / 4;
         if (s.ring > 0) {
+            ca.stages = reinterpret_cast<uint64_t*>(ws + kStageOffset);
+            pa.stages = ca.stages;
+        }
+        if (sdma) {
+            // DMA copies cannot wait on a word: an event on the caller's
+            // stream, recorded before the consumer, holds them back until
+            // the work ahead of the call is done.  The join is as above:
+            // the counter writes follow the copies on the library's stream.
+            e = hipEventRecord(d->fork, c.st);
+            if (e == hipSuccess) e = consumer(c.st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
+            if (e == hipSuccess) e = enqueue_sdma(s, pa, p.elt, d->side);
+        } else if (p.producer_cus) {
+            // Disjoint CU sets: the consumer on the complement-masked
+            // stream, forked from and joined to `stream` by events (the
+            // start word still gates the producer).  With disjoint CUs the
+            // producer cannot keep a consumer workgroup off its CU, so a
+            // workspace ring needs no further ordering.
+            hipStream_t ps = nullptr, cs = nullptr;
+            rc = masked_streams(*d, p.producer_cus, &ps, &cs);
+            if (rc) return rc;
+            e = hipEventRecord(d->fork, c.st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(cs, d->fork, 0);
+            if (e == hipSuccess) e = consumer(cs);
+            if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, ps);
+            if (e == hipSuccess) e = hipEventRecord(d->join, cs);
+            if (e == hipSuccess) e = hipStreamWaitEvent(c.st, d->join, 0);
+        } else if (s.ring > 0) {
             // With a workspace ring the producer also waits for consumer
             // tiles, so consumer workgroups must not be kept off the CUs by
             // producer workgroups dispatched ahead of them.  An event on
@@ -445,17 +541,17 @@ int run(const Call& c)
             // producer back until the work ahead of the call is done, by
             // which time the consumer's grid has been dispatched.  (Should
             // a wait still starve, it ends at the time limit as an error.)
-            ca.stages = reinterpret_cast<uint64_t*>(ws + kStageOffset);
-            pa.stages = ca.stages;
             e = hipEventRecord(d->fork, c.st);
             if (e == hipSuccess) e = consumer(c.st);
             if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
+            if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
         } else {
             e = consumer(c.st);
+            if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
         }
-        if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
     } else {
-        if (run_producer) e = launch_producer(pa, p.producer_wgs, c.st);
+        if (run_producer)
+            e = sdma ? enqueue_sdma(s, pa, p.elt, c.st) : launch_producer(pa, p.producer_wgs, c.st);
         if (e == hipSuccess && run_consumer) e = consumer(c.st);
     }
     if (e != hipSuccess) return AGG_E_HIP;
@@ -601,6 +697,8 @@ int ag_gemm_check(void* stream)
     if (it != g_dev.end() && it->second.ready) {
         Device& d = it->second;
         if (hipStreamSynchronize(d.side) != hipSuccess) return AGG_E_HIP;
+        for (int i = 0; i < 3; ++i)
+            if (d.pmask[i] && hipStreamSynchronize(d.pmask[i]) != hipSuccess) return AGG_E_HIP;
         if (d.ws && d.track.used) {
             int r = check_track(d.track, reinterpret_cast<uint32_t*>(d.ws), st);
             if (r) rc = r;
@@ -628,6 +726,11 @@ void ag_gemm_release(void)
         (void)hipDeviceSynchronize();
         if (d.ws) (void)hipFree(d.ws);
         if (d.fork) (void)hipEventDestroy(d.fork);
+        if (d.join) (void)hipEventDestroy(d.join);
+        for (int i = 0; i < 3; ++i) {
+            if (d.pmask[i]) (void)hipStreamDestroy(d.pmask[i]);
+            if (d.cmask[i]) (void)hipStreamDestroy(d.cmask[i]);
+        }
         if (d.side) (void)hipStreamDestroy(d.side);
     }
     g_dev.clear();

@@ -94,6 +94,12 @@ const TileShape* tile_shapes(Kind kind, int* count)
     return kI8Shapes;
 }
 
+void producer_cu_mask(int cus, uint32_t words[8])
+{
+    for (int i = 0; i < 8; ++i) words[i] = 0;
+    for (int bit = 0; bit < cus && bit < 256; ++bit) words[bit / 32] |= 1u << (bit % 32);
+}
+
 int pick_chunk_rows(int64_t S)
 {
     if (S < 1) return 0;
@@ -145,7 +151,19 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (opt->k_splits < 0) return AGG_E_INVALID;
     if (!(opt->timeout_ms >= 0.0)) return AGG_E_INVALID;
     if (!(opt->debug_delay_us >= 0.0) || isinf(opt->debug_delay_us)) return AGG_E_INVALID;
+    if (opt->producer != AGG_PRODUCER_KERNEL && opt->producer != AGG_PRODUCER_SDMA)
+        return AGG_E_INVALID;
+    if (opt->producer_cus < 0) return AGG_E_INVALID;
+    const bool sdma = opt->producer == AGG_PRODUCER_SDMA;
+    if (opt->producer_cus && ((opt->producer_cus != 32 && opt->producer_cus != 64) || sdma))
+        return AGG_E_UNSUPPORTED;
+    // the DMA engines copy whole ranges and cannot be paced or delayed
+    if (sdma && (opt->link_gbps > 0.0 || opt->workspace_stages > 0 ||
+                 opt->debug_drop_chunk >= 0 || opt->debug_delay_us > 0.0 ||
+                 (opt->k_block > 0 && opt->k_block < K)))
+        return AGG_E_UNSUPPORTED;
     if (num_cus <= 0) num_cus = 256;
+    if (opt->producer_cus >= num_cus) return AGG_E_UNSUPPORTED;
     // Row and element offsets are formed in 64-bit; per-tile loop counters
     // in 32-bit.
     // The consumer addresses a tile's A rows, a slice's B rows and a
@@ -256,7 +274,8 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     s.nkb = 1;
     s.kbk = K;
     const int64_t kib = 1024 / elt_bytes(kind);
-    const bool two_d_ok = s.ring == 0 && opt->scheme == AGG_SCHEME_COUNTERS && s.ks == 1;
+    const bool two_d_ok = s.ring == 0 && opt->scheme == AGG_SCHEME_COUNTERS && s.ks == 1 &&
+                          !sdma;
     if (opt->k_block > 0 && opt->k_block < K) {
         if (opt->k_block % kib || K % kib) return AGG_E_UNSUPPORTED;
         if (!two_d_ok) return AGG_E_UNSUPPORTED;
@@ -292,7 +311,9 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
 
     int64_t tiles = total_tiles(s);
     int64_t chunks = total_chunks(s);
-    int cw = opt->consumer_wgs ? opt->consumer_wgs : num_cus;
+    // with CUs reserved for the producer, the consumer grid covers the rest
+    const int consumer_cus = opt->mode == AGG_MODE_PIPELINED ? num_cus - opt->producer_cus : num_cus;
+    int cw = opt->consumer_wgs ? opt->consumer_wgs : consumer_cus;
     if (cw > tiles) cw = (int)(tiles > 0 ? tiles : 1);
     if (cw < 1) cw = 1;
     // pieces per chunk (the largest chunk: the last K-block's)
@@ -325,7 +346,9 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (ppc64 > kMaxPiecesPerChunk) return AGG_E_UNSUPPORTED;
     const int ppc = (int)ppc64;
     const int64_t items = chunks * ppc;
-    int pw = opt->producer_wgs ? opt->producer_wgs : num_cus;
+    const int producer_cus =
+        opt->mode == AGG_MODE_PIPELINED && opt->producer_cus ? opt->producer_cus : num_cus;
+    int pw = opt->producer_wgs ? opt->producer_wgs : producer_cus;
     if (pw > items) pw = (int)(items > 0 ? items : 1);
     if (pw < 1) pw = 1;
     p.consumer_wgs = cw;
@@ -344,6 +367,8 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         p.ws_bytes += (size_t)((int64_t)n_shards * s.mt * s.nt * s.ks * s.tm * s.tn * 4);
     }
     p.drop_chunk = opt->debug_drop_chunk;
+    p.producer = opt->producer;
+    p.producer_cus = opt->mode == AGG_MODE_PIPELINED ? opt->producer_cus : 0;
     *out = p;
     return AGG_OK;
 }

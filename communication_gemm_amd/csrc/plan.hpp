@@ -45,7 +45,19 @@ struct Plan {
     size_t ws_bytes;    // workspace bytes this call needs
     size_t part_off;    // split-K partial sums: offset in the workspace
     int drop_chunk;
+    int producer;       // AGG_PRODUCER_KERNEL or AGG_PRODUCER_SDMA
+    int producer_cus;   // CUs the pipelined producer is masked to (0: all)
 };
+
+// CU mask bits of a `cus`-CU producer set (32 or 64): bits 0 .. cus - 1.
+// The driver deals a queue's mask bits round-robin over the XCDs (bit b on
+// XCD b % 8, measured), so that is cus / 8 CUs on every XCD.  Smaller sets
+// are not offered: with 8 to 24 CUs reserved, 5 to 19 of the remaining CUs
+// could not take a 128 KiB-LDS workgroup at once on the masked queue
+// (measured), which a workspace ring, whose producer waits for consumer
+// tiles, cannot tolerate; with 32 or 64 all of them could.  words: 8 x 32
+// bits.
+void producer_cu_mask(int cus, uint32_t words[8]);
 
 // Validate arguments and build the plan.  num_cus: CUs of the target device.
 int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,

@@ -94,6 +94,21 @@ enum agg_scheme {
                                 of per-source counters)                  */
 };
 
+/* What moves the remote chunks (PTO-ISA README, "AI Core resources": the
+ * communication runs on engines of its own beside the compute). */
+enum agg_producer {
+    AGG_PRODUCER_KERNEL = 0, /* the producer kernel: compute-unit loads and
+                                stores, per-piece release (default)        */
+    AGG_PRODUCER_SDMA = 1    /* the DMA engines: one copy per row group of
+                                one m-tile and source, in send order, on the
+                                library's stream, each followed by a stream
+                                write of the source's counter (the release,
+                                ordered after the copy by the stream).  No
+                                compute unit moves data.  Chunks span all of
+                                K; no pacing, workspace ring, trace of
+                                releases or test hooks (AGG_E_UNSUPPORTED)  */
+};
+
 /* How the emulated links are paced when link_gbps > 0. */
 enum agg_link_model {
     AGG_LINKS_PARALLEL = 0,  /* one link per source, all in parallel (full
@@ -201,6 +216,19 @@ typedef struct agg_options {
                                below the time limit (AGG_E_INVALID if
                                negative or not finite)                     */
     uint32_t debug_delay_seed;
+    int producer;           /* enum agg_producer (default KERNEL)            */
+    int producer_cus;       /* 0 (default): producer and consumer share every
+                               CU.  32 or 64: in pipelined calls the
+                               producer kernel runs on a stream masked to
+                               that many CUs (the same number on each of
+                               the 8 XCDs) and the consumer on a stream
+                               masked to the others, with a grid sized to
+                               them; the two are forked from and joined to
+                               `stream` by events.  Other values, or with
+                               SDMA: AGG_E_UNSUPPORTED (smaller masks leave
+                               the remaining CUs unable to hold a full
+                               consumer grid at once).  Ignored outside the
+                               pipelined mode.                             */
     int64_t k_block;        /* elements of K per chunk; 0 (default): the
                                automatic choice that goes with chunk_rows 0
                                (see ag_gemm_f16), or all of K for an

@@ -302,3 +302,59 @@ def test_random_completion_order_nan_poisoned(agg, data, ref):
             k_block=[0, 512, 0, 512][it]))
         assert agg.check() == 0
         assert torch.equal(C, ref), f"iteration {it}"
+
+
+# ---- producer options --------------------------------------------------
+
+@pytest.mark.parametrize("kw", [
+    dict(producer=1), dict(producer=1, chunk_rows=1), dict(producer=1, chunk_rows=100),
+    dict(producer=1, local_shard=2, send_order=[3, 0, 1]), dict(producer=1, link_model=1),
+    dict(producer=1, mode=2), dict(producer=1, scheme=1), dict(producer=1, scheme=1, pvalue=2),
+    dict(producer_cus=32), dict(producer_cus=64),
+    dict(producer_cus=32, k_block=512), dict(producer_cus=64, link_gbps=40.0),
+    dict(producer_cus=32, workspace_stages=2, chunk_rows=8),
+    dict(producer_cus=64, workspace_stages=2, chunk_rows=8),
+    dict(producer_cus=32, mode=2),
+])
+def test_producer_options_give_the_same_bits(agg, data, ref, kw):
+    """The DMA producer and a CU-masked producer change only what moves the
+    rows and where the kernels run: the output is bitwise the same."""
+    kw = dict(kw)
+    cr = kw.pop("chunk_rows", 0)
+    for rep in range(2):
+        C = call(agg, data, cr, **kw)
+        assert torch.equal(C, ref), (kw, rep)
+
+
+def test_sdma_copy_then_compute(agg, data, ref):
+    ts, B = data[0], data[1]
+    C = torch.full_like(ref, float("nan"))
+    agg.ag_gemm_f16(ts, B, C, opts=agg.options(mode=3, producer=1))
+    agg.ag_gemm_f16(ts, B, C, opts=agg.options(mode=1))
+    assert agg.check() == 0
+    assert torch.equal(C, ref)
+
+
+@pytest.mark.parametrize("kw", [dict(producer=1), dict(producer_cus=32),
+                                dict(producer_cus=64, k_block=512)])
+def test_producer_options_alternating_and_poisoned(agg, orc, data, ref, kw):
+    """Two data sets in turn through one workspace, NaN-filled before every
+    other call: each call gives its own data's result."""
+    ts, B = data[0], data[1]
+    shards2, _ = synth.make_f16(4 * 512, 1024, 768, 4, "normal", 50600)
+    ts2 = [dev(s, torch) for s in shards2]
+    C2 = torch.full_like(ref, float("nan"))
+    agg.ag_gemm_f16(ts2, B, C2, 0)
+    assert agg.check() == 0
+    M, K = ts[0].shape[0] * len(ts), ts[0].shape[1]
+    ws = torch.empty(agg.workspace_bytes(len(ts), M, K, 2) // 2, dtype=torch.float16,
+                     device="cuda")
+    for it in range(8):
+        if it % 2 == 0:
+            ws.fill_(float("nan"))
+            agg.workspace_reset(ws)
+        src, want = (ts, ref) if it % 2 == 0 else (ts2, C2)
+        C = torch.full_like(ref, float("nan"))
+        agg.ag_gemm_f16(src, B, C, 0, opts=agg.options(workspace=ws, **kw))
+        assert agg.check() == 0
+        assert torch.equal(C, want), f"call {it} {kw}"

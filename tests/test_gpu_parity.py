@@ -392,3 +392,25 @@ def test_k_blocks_full_size(agg, orc, cid, kb):
     C = run_f16(agg, shards, B, c.chunk_rows, agg.options(link_gbps=c.link_gbps, k_block=kb))
     Co, So = orc.ag_gemm_f16(shards, B)
     print(c.name, "k_block", kb, "max err/S", check_f16(C, Co, So, c.name))
+
+
+# ---------------------------------------------------------------- producers
+
+@pytest.mark.parametrize("kw", [dict(producer=1), dict(producer_cus=32),
+                                dict(producer_cus=64, k_block=1024)])
+def test_producer_options_full_size(agg, orc, kw):
+    """C4 moved by the DMA engines, or by a producer on 32 or 64 CUs of its
+    own: every element of C."""
+    c = synth.CASES[4]
+    shards, B = synth.make_case(c)
+    C = run_f16(agg, shards, B, 0, agg.options(**kw))
+    Co, So = orc.ag_gemm_f16(shards, B)
+    print(kw, "max err/S", check_f16(C, Co, So, f"{c.name} {kw}"))
+
+
+@pytest.mark.parametrize("kw", [dict(producer=1), dict(producer_cus=32)])
+def test_producer_options_i8(agg, orc, kw):
+    shards, B, bias, scale = synth.make_i8(3 * 77, 16 * 37, 8 * 19, 3, 41500)
+    acc, D = run_i8(agg, shards, B, bias, scale, 9, kw)
+    ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale)
+    check_i8(acc, D, ao, Do, f"int8 {kw}")

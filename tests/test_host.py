@@ -462,3 +462,39 @@ def test_automatic_chunks(kind, n, M, K, N, opts, cr, nkb):
     info, _, _ = agg.plan(kind, n, M, K, N, 8, agg.options(**{k: v for k, v in opts.items()
                                                                if k != "k_block"}))
     assert info.k_blocks == 1
+
+
+# ---- producer options: DMA engines, CU-masked producer ---------------
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(producer=2), agg.AGG_E_INVALID),
+    (dict(producer_cus=-8), agg.AGG_E_INVALID),
+    (dict(producer_cus=12), agg.AGG_E_UNSUPPORTED),
+    (dict(producer_cus=16), agg.AGG_E_UNSUPPORTED),
+    (dict(producer_cus=40), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=1, producer_cus=32), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=1, link_gbps=100.0), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=1, workspace_stages=2), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=1, k_block=1024), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=1, debug_drop_chunk=3), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=1, debug_delay_us=5.0), agg.AGG_E_UNSUPPORTED),
+])
+def test_producer_options_rejected(kw, status):
+    with pytest.raises(agg.AggError) as e:
+        agg.plan("f16", 4, 4096, 4096, 4096, 0, agg.options(**kw))
+    assert e.value.status == status
+
+
+def test_producer_options_plans():
+    # the DMA producer moves whole-K chunks (automatic S/64 rows)
+    info, _, _ = agg.plan("f16", 4, 4096, 4096, 4096, 0, agg.options(producer=1))
+    assert info.k_blocks == 1 and info.chunk_rows == 16
+    # a CU-masked producer: the consumer grid covers the other CUs, the
+    # producer grid its own; outside the pipelined mode nothing is masked
+    info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(producer_cus=32))
+    assert info.consumer_wgs == 224 and info.producer_wgs == 32
+    info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(producer_cus=64))
+    assert info.consumer_wgs == 192 and info.producer_wgs == 64
+    info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0,
+                          agg.options(producer_cus=32, mode=agg.MODE_SEQUENTIAL))
+    assert info.consumer_wgs == 256 and info.producer_wgs == 256

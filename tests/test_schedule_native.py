@@ -206,3 +206,38 @@ def test_paced_bytes_follow_each_sources_order(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout
     assert int(out.stdout) > 10000
+
+
+CU_MASK = r"""
+#include <cstdio>
+#include "plan.hpp"
+using namespace agg;
+// The producer's CU mask has `cus` bits, cus/8 on every XCD: the driver
+// deals a queue's mask bits round-robin over the XCDs (bit b on XCD b % 8).
+int main() {
+    for (int cus = 32; cus <= 64; cus += 32) {
+        uint32_t m[8];
+        producer_cu_mask(cus, m);
+        int n = 0, rr[8] = {0};
+        for (int b = 0; b < 256; ++b)
+            if (m[b / 32] >> (b % 32) & 1) { ++n; ++rr[b % 8]; }
+        if (n != cus) { printf("count %d %d\n", cus, n); return 1; }
+        for (int x = 0; x < 8; ++x)
+            if (rr[x] != cus / 8) { printf("xcd %d %d\n", cus, x); return 1; }
+    }
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ needed")
+def test_producer_cu_mask_spreads_over_xcds(tmp_path):
+    src = tmp_path / "mask.cpp"
+    src.write_text(CU_MASK)
+    exe = tmp_path / "mask"
+    inc = os.path.join(ROOT, "include")
+    subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", f"-I{inc}", str(src),
+                    os.path.join(CSRC, "plan.cpp"), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
