@@ -108,6 +108,9 @@ def parse():
                          "because counter collection serializes the two kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--vendor-only", action="store_true",
+                    help="only time hipBLASLt (torch.matmul) on the workload's gathered shape "
+                         "(a reference for counter runs)")
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="summarise rocprofv3 counter CSVs under DIR and exit")
     ap.add_argument("--trace-summary", metavar="DIR",
@@ -698,6 +701,11 @@ def main():
     if case.kind != "f16":
         raise SystemExit("--case must name an fp16 workload")
     inputs = synth.make_case(case)
+    if args.vendor_only:
+        w = F16Workload(torch, agg, case, inputs)
+        print(json.dumps({"vendor_gemm": vendor_gemm(torch, w, args.steps),
+                          "workload": case.name}), flush=True)
+        return
     w = F16Workload(torch, agg, case, inputs, tile=args.tile,
                     link_gbps=args.link_gbps, chunk_rows=args.chunk_rows or None)
     mode = MODES[args.mode]

@@ -471,6 +471,7 @@ int run(const Call& c)
     // room for producer waves on each CU even at full occupancy.
     // Workgroups of one XCD take neighbouring tiles (the grid is now final).
     ca.s.xf = pick_xcd_split(ca.s, cwgs);
+    ca.s.gm = pick_group(ca.s, cwgs);
 
     hipEvent_t* cev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opt->consumer_events));
     auto consumer = [&](hipStream_t st) -> hipError_t {

@@ -224,6 +224,32 @@ __device__ __forceinline__ void wait_vm_lgkm0()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
 }
 
+// A value every lane of the workgroup holds alike (read back from LDS after
+// a barrier), marked as such: the compiler cannot tell that an LDS read is
+// uniform, and a branch or address that depends on one would otherwise be
+// taken as divergent -- every buffer descriptor derived from it would sit in
+// vector registers and each load would be wrapped in a loop over its
+// distinct values.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uniform(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// A buffer descriptor over `bytes` bytes from p (at most 2^31 - 1), built
+// from scalar registers.  Its fields are the same in every lane, but they
+// are often computed with vector instructions (64-bit products and
+// divisions have no scalar form), and a descriptor left in vector
+// registers makes the compiler wrap every load and store through it in a
+// loop over the lanes' distinct values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void* p, int64_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t base = (uint64_t)uniform((uint32_t)a) | ((uint64_t)uniform((uint32_t)(a >> 32)) << 32);
+    const int n = uniform((int)(bytes < 0x7fffffff ? bytes : 0x7fffffff));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
 // Workgroup barrier without the release/acquire fences of __syncthreads:
 // those would wait for every load still in flight, including the slices
 // being prefetched.  Callers wait for exactly what the barrier publishes
@@ -328,12 +354,8 @@ struct Engine {
         const int64_t elt = T::kElt;
         const int64_t a_left = (src.rows_valid * src.K - k0) * elt;
         const int64_t b_left = ((src.K - k0) * src.N - src.n0) * elt;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(src.arows + k0 * elt), 0, (int)(a_left < 0x7fffffff ? a_left : 0x7fffffff),
-            kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(src.B + (k0 * src.N + src.n0) * elt), 0,
-            (int)(b_left < 0x7fffffff ? b_left : 0x7fffffff), kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t ra = scalar_rsrc(src.arows + k0 * elt, a_left);
+        const __amdgpu_buffer_rsrc_t rb = scalar_rsrc(src.B + (k0 * src.N + src.n0) * elt, b_left);
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const bool edge = k0 + kBK > src.K || src.n0 + BN > src.N;
         if (!edge) {
@@ -539,13 +561,12 @@ __device__ __forceinline__ void store_tile_as(
     const uint32_t rows = (uint32_t)(left < BM ? left : BM);
     const int64_t origin = ((int64_t)shard * s.S + row0) * s.N + (int64_t)n * BN;
     const uint32_t row_out = (uint32_t)s.N * (uint32_t)sizeof(Out);
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<Out*>(a.C) + origin, 0, (int)(rows * row_out), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rc =
+        scalar_rsrc(static_cast<Out*>(a.C) + origin, (int64_t)rows * row_out);
     __amdgpu_buffer_rsrc_t racc = rc;
     const uint32_t row_acc = (uint32_t)s.N * 4u;
     if constexpr (kKeepAcc)
-        racc = __builtin_amdgcn_make_buffer_rsrc(a.acc_out + origin, 0, (int)(rows * row_acc),
-                                                 kRsrcWord3);
+        racc = scalar_rsrc(a.acc_out + origin, (int64_t)rows * row_acc);
     const uint32_t lrow = (uint32_t)(wm + 4 * (lane >> 5));
     const int64_t col_lane = (int64_t)n * BN + wn + (lane & 31);
 #pragma unroll
@@ -724,8 +745,8 @@ __device__ bool split_reduce(const ConsumerArgs& a, const TileRef& t, int tid, i
     const Schedule& s = a.s;
     const int64_t tb = ((int64_t)t.shard * s.mt + t.m) * s.nt + t.n;
     // the tile's parts: ks x R x TH words, far below 2^31 bytes
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        a.partials + tb * s.ks * R * TH * 4, 0, s.ks * R * TH * 4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rp =
+        scalar_rsrc(a.partials + tb * s.ks * R * TH * 4, (int64_t)s.ks * R * TH * 4);
     const int own = t.kp * R * TH * 4 + tid * 4;
 #pragma unroll
     for (int i = 0; i < E::kTM; ++i)
@@ -754,7 +775,7 @@ __device__ bool split_reduce(const ConsumerArgs& a, const TileRef& t, int tid, i
         *last = ((old + w) & (kPieceTotal - 1)) == 0;
     }
     __syncthreads();
-    if (!*last) return false;
+    if (!uniform(*last)) return false;
     // pairs with the other parts' performed stores, seen through the ticket
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
@@ -835,9 +856,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
                 if (tid == 0) ok_sh = ok;
             }
             __syncthreads();
-            if (!ok_sh) break;   // the call has failed; every lane leaves
+            if (!uniform(ok_sh)) break;   // the call has failed; every lane leaves
             if (s.pv == 0) {
-                open_kb = covered_kblocks(s, rows_need, seen_sh[t.shard]);
+                open_kb = covered_kblocks(s, rows_need, uniform(seen_sh[t.shard]));
                 open_k = open_kb >= s.nkb ? INT32_MAX : (int32_t)(open_kb * s.kbk);
             }
         }
@@ -864,12 +885,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
                 wait_vm_lgkm0<63>();   // the LDS stores are done (loads may fly)
             }
             bare_barrier();
-            if (!ok_sh) {
+            if (!uniform(ok_sh)) {
                 failed = true;
                 open_k = INT32_MAX;
                 return;
             }
-            open_kb = covered_kblocks(s, rows_need, seen_sh[t.shard]);
+            open_kb = covered_kblocks(s, rows_need, uniform(seen_sh[t.shard]));
             open_k = open_kb >= s.nkb ? INT32_MAX : (int32_t)(open_kb * s.kbk);
         };
 

@@ -423,7 +423,10 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
     int rc = agg::make_plan(static_cast<agg::Kind>(kind), n_shards, M, K,
                             N, chunk_rows, opt, num_cus, &p);
     if (rc) return rc;
-    const agg::Schedule& s = p.sched;
+    // the placement the launch picks for a grid of consumer_wgs workgroups
+    agg::Schedule s = p.sched;
+    s.xf = agg::pick_xcd_split(s, p.consumer_wgs);
+    s.gm = agg::pick_group(s, p.consumer_wgs);
     if (info) {
         info->shard_rows = s.S;
         info->chunk_rows = s.cr;

@@ -91,6 +91,9 @@ struct Schedule {
     int order[kMaxShards]; // order[0] = local, order[1..n-1] = send order
     int slot[kMaxShards];  // workspace slot of each shard (-1: local)
     int xf;                // XCD blocking: n-tile groups per round (0 = none)
+    int gm;                // grouped placement (when xf is 0): row panels per
+                           // group, tiles column by column inside a group;
+                           // 0 = list order
     int ring;              // workspace stages per remote source (0 = a full
                            // slot of S rows); stage g holds the row panel
                            // (m-tile) m with m % ring == g
@@ -149,6 +152,28 @@ AGG_HD int64_t total_chunks(const Schedule& s)
     return (int64_t)(s.n_shards - 1) * s.cps;
 }
 
+// Index r of a run of `panels` row panels of nt tiles each -> (panel, n).
+// List order is panel by panel; the grouped placement takes gm panels at a
+// time and walks them column by column (n-tile after n-tile, the group's
+// panels inside each), so that a stretch of consecutive positions covers a
+// block of a few panels x a few n-tiles rather than one long panel.  Both
+// are bijections of [0, panels * nt).
+AGG_HD void group_decode(const Schedule& s, int64_t r, int64_t panels, int64_t* panel,
+                         int64_t* n)
+{
+    if (s.gm <= 0) {
+        *panel = r / s.nt;
+        *n = r % s.nt;
+        return;
+    }
+    const int64_t per_group = (int64_t)s.gm * s.nt;
+    const int64_t g = r / per_group, w = r % per_group;
+    const int64_t left = panels - g * s.gm;
+    const int64_t gsz = left < s.gm ? left : s.gm;   // the last group may be short
+    *panel = g * s.gm + w % gsz;
+    *n = w / gsz;
+}
+
 struct TileRef {
     int shard;   // source shard of the A rows
     int m;       // m-tile within the shard
@@ -196,10 +221,12 @@ AGG_HD TileRef tile_at(const Schedule& s, int64_t p)
         p -= (int64_t)t.kp * base;
     }
     int64_t local_tiles = (int64_t)s.mt * s.nt;
+    int64_t panel, n;
     if (p < local_tiles) {
+        group_decode(s, p, s.mt, &panel, &n);
         t.shard = s.local;
-        t.m = (int)(p / s.nt);
-        t.n = (int)(p % s.nt);
+        t.m = (int)panel;
+        t.n = (int)n;
         t.need = 0;
         return t;
     }
@@ -207,17 +234,17 @@ AGG_HD TileRef tile_at(const Schedule& s, int64_t p)
     int remotes = s.n_shards - 1;
     int src;
     if (s.link_model == 0) {
-        int64_t per_m = (int64_t)remotes * s.nt;
-        t.m = (int)(q / per_m);
-        int64_t r = q % per_m;
-        src = (int)(r / s.nt);
-        t.n = (int)(r % s.nt);
+        // panels (m, source) in m-major order
+        group_decode(s, q, (int64_t)s.mt * remotes, &panel, &n);
+        t.m = (int)(panel / remotes);
+        src = (int)(panel % remotes);
+        t.n = (int)n;
     } else {
         int64_t per_src = (int64_t)s.mt * s.nt;
         src = (int)(q / per_src);
-        int64_t r = q % per_src;
-        t.m = (int)(r / s.nt);
-        t.n = (int)(r % s.nt);
+        group_decode(s, q % per_src, s.mt, &panel, &n);
+        t.m = (int)panel;
+        t.n = (int)n;
     }
     t.shard = s.order[1 + src];
     t.need = need_chunks(s, t.m);
@@ -310,11 +337,40 @@ AGG_HD int pick_xcd_split(const Schedule& s, int64_t G)
     return best;
 }
 
+// Grouped placement, for the grids pick_xcd_split declines (rounds that do
+// not hold whole panels, such as 107 n-tiles on 256 workgroups): XCD x
+// takes the x-th stretch of G/8 consecutive positions of every round, and
+// the tile list is walked in groups of gm panels, column by column
+// (group_decode), so that stretch is a block of about gm panels x
+// G/(8 gm) n-tiles.  gm minimises the A and B rows one stretch fetches,
+// gm tm + (G / (8 gm)) tn, over the divisors of G/8 up to 16.  Not with a
+// workspace ring (a group could need more panels than the ring holds), the
+// barrier scheme or split-K, which keep list order.
+AGG_HD int pick_group(const Schedule& s, int64_t G)
+{
+    if (s.xf > 0 || G < kXcds || G % kXcds != 0 || s.ring > 0 || s.pv > 0 || s.ks > 1 ||
+        s.nt <= 0)
+        return 0;
+    const int64_t per = G / kXcds;
+    int best = 0;
+    int64_t best_cost = 0;
+    for (int g = 1; g <= 16 && g <= per; ++g) {
+        if (per % g != 0) continue;
+        const int64_t cost = (int64_t)g * s.tm + (per / g) * s.tn;
+        if (best == 0 || cost < best_cost) {
+            best = g;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 // First position (within round 0) of workgroup b; it then takes that
 // position plus multiples of G.  A permutation of [0, G) for every grid
-// pick_xcd_split accepted, the identity otherwise.
+// pick_xcd_split or pick_group accepted, the identity otherwise.
 AGG_HD int64_t wg_position(const Schedule& s, int64_t b, int64_t G)
 {
+    if (s.gm > 0) return (b % kXcds) * (G / kXcds) + b / kXcds;
     const int f = s.xf;
     if (f <= 0) return b;
     const int64_t P = G / s.nt;

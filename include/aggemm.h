@@ -438,7 +438,10 @@ typedef struct agg_plan_info {
  *   kind: 0 = fp16 path, 1 = int8 path, 2 = bf16 path, 3 = fp8 path; num_cus: CUs of
  *   the device to plan for (0 = 256).  tile_order (nullable, capacity total_tiles * 4 int32):
  *   per consumer position: shard, m-tile, n-tile, counter value waited for
- *   before the tile's first K-block (0 for the local shard); with split-K the positions run part after
+ *   before the tile's first K-block (0 for the local shard), for a grid of
+ *   consumer_wgs workgroups (when its rounds do not hold whole row panels,
+ *   positions walk groups of a few panels column by column, so that each
+ *   XCD's stretch of a round is a compact block); with split-K the positions run part after
  *   part, each part's positions in the same order, so each (shard, m-tile,
  *   n-tile) appears once per part.  chunk_order (nullable, capacity
  *   total_chunks * 2 int32): per producer position: shard, chunk index

@@ -33,6 +33,7 @@ using namespace agg;
 static int simulate(Schedule s, int ppc, int G, int P)
 {
     s.xf = pick_xcd_split(s, G);
+    s.gm = pick_group(s, G);
     const long tiles = total_tiles(s), chunks = total_chunks(s), items = chunks * ppc;
     std::vector<long> pnext(P), cnext(G, 0);
     for (int w = 0; w < P; ++w) pnext[w] = w;

@@ -2,7 +2,9 @@
 the kernels use (schedule.hpp is plain integer C++): for every grid the
 planner accepts, the workgroups of one round take each position exactly
 once, the workgroups of one XCD take a block of whole row panels x n-tile
-groups, and a grid it cannot split keeps list order."""
+groups, and a grid it cannot split keeps list order; where rounds do not
+hold whole panels, the grouped placement is a permutation of positions and
+of tiles, and each XCD's stretch of a round is a compact block."""
 import os
 import shutil
 import subprocess
@@ -241,3 +243,86 @@ def test_producer_cu_mask_spreads_over_xcds(tmp_path):
                     os.path.join(CSRC, "plan.cpp"), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+
+
+GROUPED = r"""
+#include <cstdio>
+#include <vector>
+#include "schedule.hpp"
+using namespace agg;
+int main() {
+    long checked = 0, grouped = 0;
+    for (int nt = 1; nt <= 120; nt += (nt < 20 ? 1 : 7))
+    for (int mt = 1; mt <= 40; mt += (mt < 8 ? 1 : 5))
+    for (int n_shards = 1; n_shards <= 4; ++n_shards)
+    for (int link = 0; link <= 1; ++link)
+    for (int G : {8, 16, 64, 200, 224, 256, 512}) {
+        Schedule s{};
+        s.nt = nt; s.mt = mt; s.tm = 256; s.tn = (nt % 3) ? 128 : 256;
+        s.n_shards = n_shards; s.local = 0; s.link_model = link; s.ks = 1;
+        s.S = (int64_t)mt * 256; s.cr = 64;
+        for (int q = 0; q < n_shards; ++q) s.order[q] = q;
+        s.xf = pick_xcd_split(s, G);
+        s.gm = pick_group(s, G);
+        if (s.xf && s.gm) { printf("both placements G=%d nt=%d\n", G, nt); return 1; }
+        if (!s.gm) continue;
+        ++grouped;
+        // positions of one round: a permutation of [0, G)
+        std::vector<int> seen(G, 0);
+        for (int b = 0; b < G; ++b) {
+            const long p = wg_position(s, b, G);
+            if (p < 0 || p >= G || seen[p]++) { printf("not a permutation G=%d\n", G); return 1; }
+        }
+        // tile list: each (shard, m, n) exactly once
+        const long T = total_tiles(s);
+        std::vector<char> hit((size_t)n_shards * mt * nt, 0);
+        for (long p = 0; p < T; ++p) {
+            const TileRef t = tile_at(s, p);
+            if (t.shard < 0 || t.shard >= n_shards || t.m < 0 || t.m >= mt || t.n < 0 || t.n >= nt) {
+                printf("tile out of range p=%ld\n", p); return 1;
+            }
+            char& h = hit[((size_t)t.shard * mt + t.m) * nt + t.n];
+            if (h++) { printf("tile twice p=%ld\n", p); return 1; }
+        }
+        // an XCD's stretch of a round that stays inside one group of the
+        // local segment spans the group's panels and about G / (8 gm) n-tiles
+        const long per = G / kXcds, local = (long)mt * nt;
+        for (long r0 = 0; r0 + G <= local; r0 += G)
+            for (int x = 0; x < kXcds; ++x) {
+                long p0 = r0 + x * per, p1 = p0 + per;
+                if (p0 / ((long)s.gm * nt) != (p1 - 1) / ((long)s.gm * nt)) continue;
+                int mlo = 1 << 30, mhi = -1, nlo = 1 << 30, nhi = -1;
+                for (long p = p0; p < p1; ++p) {
+                    const TileRef t = tile_at(s, p);
+                    mlo = t.m < mlo ? t.m : mlo; mhi = t.m > mhi ? t.m : mhi;
+                    nlo = t.n < nlo ? t.n : nlo; nhi = t.n > nhi ? t.n : nhi;
+                }
+                const long g = p0 / ((long)s.gm * nt), left = mt - g * s.gm;
+                const long gsz = left < s.gm ? left : s.gm;   // a short last group
+                if (mhi - mlo + 1 > gsz || nhi - nlo + 1 > (per + gsz - 1) / gsz + 1) {
+                    printf("loose block G=%d nt=%d mt=%d gm=%d\n", G, nt, mt, s.gm); return 1;
+                }
+            }
+        ++checked;
+    }
+    // the int8 workload's shape: 256 workgroups, 107 n-tiles of 256
+    Schedule s{}; s.nt = 107; s.mt = 32; s.tm = 256; s.tn = 256; s.ks = 1;
+    s.xf = pick_xcd_split(s, 256);
+    printf("%ld %ld %d %d\n", checked, grouped, s.xf, pick_group(s, 256));
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ needed")
+def test_grouped_placement_is_a_compact_permutation(tmp_path):
+    src = tmp_path / "grouped.cpp"
+    src.write_text(GROUPED)
+    exe = tmp_path / "grouped"
+    subprocess.run(["g++", "-O2", "-std=c++17", f"-I{CSRC}", str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout
+    checked, grouped, xf, gm = map(int, out.stdout.split())
+    assert grouped > 100 and checked == grouped
+    assert xf == 0 and gm == 4     # 32 workgroups per XCD: 4 panels x 8 n-tiles
