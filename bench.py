@@ -36,6 +36,12 @@ figure is reported only while those sources are unchanged.
 
 Helpers for those runs:
     python bench.py --copy-calibration      a 256 MiB device copy, 10 times
+    python bench.py --mfma-probe            the register-only matrix-core probe
+                                            (fp16 and fp8, random against
+                                            constant operands): TFLOP/s, GFX
+                                            clocks and board power under load
+    python bench.py --only KIND             only KIND's timed steps (f16 of
+                                            --case, bf16, fp8 or i8) in --mode
     python bench.py --pmc-summary DIR       mean counter value per dispatch
                                             and kernel, from rocprofv3 CSVs
     python bench.py --trace-summary DIR     per-kernel durations from a
@@ -108,6 +114,10 @@ def parse():
                          "because counter collection serializes the two kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the register-only matrix-core probe")
+    ap.add_argument("--only", choices=("bf16", "fp8", "i8"),
+                    help="only this variant's timed steps, in --mode (for counter runs)")
     ap.add_argument("--vendor-only", action="store_true",
                     help="only time hipBLASLt (torch.matmul) on the workload's gathered shape "
                          "(a reference for counter runs)")
@@ -294,11 +304,12 @@ def device_trace(torch, agg, call_with_trace, info):
         "consumer_span_us": round(float(cons[:, 2].max() - start) / 100.0, 2)}
 
 
-def gfx_clocks_under_load(torch, call, max_s=30.0):
+def gfx_clocks_under_load(torch, call, max_s=30.0, power=False):
     """GFX clocks (MHz, one per XCD) read with amd-smi while `call` keeps the
     GPU busy: about a second of calls is queued first (the clocks take some
     tenths of a second to rise from their idle level), and calls keep being
-    queued until the tool returns.  None without the tool."""
+    queued until the tool returns.  With power, also the board's power
+    readings (W).  None without the tool."""
     import shutil
     import subprocess
     import threading
@@ -310,7 +321,8 @@ def gfx_clocks_under_load(torch, call, max_s=30.0):
 
     def sample():
         try:
-            out["text"] = subprocess.run([tool, "metric", "--clock", "--json"],
+            what = ["--clock", "--power"] if power else ["--clock"]
+            out["text"] = subprocess.run([tool, "metric", *what, "--json"],
                                          capture_output=True, text=True, timeout=max_s).stdout
         except (OSError, subprocess.SubprocessError):
             out["text"] = ""
@@ -334,8 +346,76 @@ def gfx_clocks_under_load(torch, call, max_s=30.0):
         return None
     if not clocks:
         return None
-    return {"mean": round(float(np.mean(clocks)), 1), "min": min(clocks), "max": max(clocks),
-            "xcds": len(clocks), "tool": "amd-smi metric --clock, during pipelined calls"}
+    res = {"mean": round(float(np.mean(clocks)), 1), "min": min(clocks), "max": max(clocks),
+           "xcds": len(clocks), "tool": "amd-smi metric --clock, during pipelined calls"}
+    if power:
+        watts = {}
+        for k, v in (data[0].get("power") or {}).items():
+            if isinstance(v, dict) and isinstance(v.get("value"), (int, float)):
+                watts[k] = v["value"]
+            elif isinstance(v, (int, float)):
+                watts[k] = v
+        res["power_w"] = watts or None
+        res["tool"] = "amd-smi metric --clock --power"
+    return res
+
+
+PROBE_LIB = os.path.join(ROOT, "communication_gemm_amd", "libaggprobe.so")
+
+
+def mfma_probe(torch, seconds=1.5):
+    """The register-only matrix-core probe (libaggprobe.so): one workgroup of
+    eight waves per CU, each wave issuing matrix instructions on operands
+    held in registers, no memory traffic in the loop.  Per kind (fp16
+    32x32x16, fp8 E4M3 32x32x64) and operand pattern (random values, or one
+    constant): TFLOP/s over launches of about 10 ms, and the GFX clocks and
+    board power amd-smi reads while the probe runs."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: build with communication_gemm_amd/build.py")
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.agg_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"cus": cus, "waves_per_cu": 8, "peak_tflops": {"f16": PEAK_F16_TFLOPS,
+                                                          "fp8": PEAK_FP8_TFLOPS}}
+    # flops per instruction: 2 x 32 x 32 x 16 (fp16), 2 x 32 x 32 x 64 (fp8)
+    for kind, name, flop in ((0, "f16", 32768), (1, "fp8", 131072)):
+        for random, pattern in ((1, "random"), (0, "constant")):
+            def launch(iters):
+                rc = fn(kind, random, iters, cus, 1234, ctypes.c_void_p(out.data_ptr()),
+                        ctypes.c_void_p(stream))
+                if rc:
+                    raise SystemExit(f"probe launch failed: {rc}")
+            # size a launch to about 10 ms
+            launch(1000)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            launch(20000)
+            torch.cuda.synchronize()
+            per_iter = (time.perf_counter() - t0) / 20000
+            iters = max(1000, int(0.010 / per_iter))
+            ramp(torch, lambda: launch(iters), seconds=0.5)
+            t, _ = timed(torch, lambda ev: (lambda: launch(iters)), max(10, int(seconds / 0.010)),
+                         3, with_consumer=False)
+            flops = float(cus) * 8 * iters * 8 * flop
+            def blocking():
+                launch(iters)
+                torch.cuda.synchronize()
+            clocks = gfx_clocks_under_load(torch, blocking, power=True)
+            res[f"{name}_{pattern}"] = {
+                "ms_per_launch": round(t, 4), "iters": iters,
+                "tflops": round(flops / (t * 1e-3) / 1e12, 1),
+                "frac_of_peak": round(flops / (t * 1e-3) / 1e12 /
+                                      (PEAK_F16_TFLOPS if kind == 0 else PEAK_FP8_TFLOPS), 4),
+                "under_load": clocks}
+            print(json.dumps({"probe": f"{name}_{pattern}", **res[f"{name}_{pattern}"]}),
+                  flush=True)
+    return res
 
 
 class F16Workload:
@@ -497,9 +577,9 @@ def run_ring(args, torch, agg, synth):
     return out
 
 
-def run_variant(args, torch, agg, synth, kind):
+def run_variant(args, torch, agg, synth, kind, mode="pipelined"):
     """The bf16 or fp8 (E4M3) variant on the 8 x 1024-row fp16 workload's
-    shape, pipelined."""
+    shape, pipelined (or in `mode`)."""
     case = synth.CASES[args.case]
     if kind == "bf16":
         shards, B = synth.make_bf16(case.M, case.K, case.N, case.n_shards, "normal",
@@ -523,16 +603,35 @@ def run_variant(args, torch, agg, synth, kind):
                      device="cuda")
     agg.workspace_reset(ws)
     def make(ev):
-        return fn(ts, tB, C, 0, opts=agg.options(workspace=ws, consumer_events=ev), prepare=True)
+        return fn(ts, tB, C, 0, opts=agg.options(workspace=ws, mode=MODES[mode],
+                                                 consumer_events=ev), prepare=True)
+    if mode == "compute":
+        fn(ts, tB, C, 0, opts=agg.options(workspace=ws, mode=MODES["copy"]))
     ramp(torch, make(None), seconds=0.3)
     t, c = timed(torch, make, max(20, args.steps // 2), 20)
     if agg.check():
         raise SystemExit(f"{kind} run failed")
     flops = 2.0 * case.M * case.K * case.N
-    return {"workload": case.name.replace("f16", kind, 1), "ms": round(t, 5),
+    return {"workload": case.name.replace("f16", kind, 1), "mode": mode, "ms": round(t, 5),
             "consumer_ms": round(c, 5), "tflops": round(flops / (t * 1e-3) / 1e12, 2),
             "consumer_tflops": round(flops / (c * 1e-3) / 1e12, 2),
             "consumer_frac_of_peak": round(flops / (c * 1e-3) / 1e12 / peak, 4)}
+
+
+def only_variant(args, torch, agg, synth):
+    """--only: one variant's timed steps in --mode, nothing else (the
+    workload hardware-counter runs profile)."""
+    if args.only in ("bf16", "fp8"):
+        return run_variant(args, torch, agg, synth, args.only, args.mode)
+    c = synth.CASES[5]
+    w = I8Workload(torch, agg, c, synth.make_case(c))
+    ops = 2.0 * c.M * c.K * c.N
+    ramp(torch, w.calls[args.mode], seconds=0.3)
+    t, cm = timed(torch, lambda ev: w.prep(MODES[args.mode], ev), args.steps, args.warmup)
+    if agg.check():
+        raise SystemExit("int8 run failed")
+    return {"workload": c.name, "mode": args.mode, "ms": round(t, 5),
+            "consumer_ms": round(cm, 5), "consumer_tops": round(ops / (cm * 1e-3) / 1e12, 2)}
 
 
 PRODUCERS = {"kernel": dict(), "sdma": dict(producer=1), "kernel_32cus": dict(producer_cus=32),
@@ -696,6 +795,12 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.mfma_probe:
+        print(json.dumps({"mfma_probe": mfma_probe(torch)}), flush=True)
+        return
+    if args.only:
+        print(json.dumps(only_variant(args, torch, agg, synth)), flush=True)
         return
     case = synth.CASES[args.case]
     if case.kind != "f16":

@@ -1,4 +1,5 @@
-"""Build libaggemm.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Build libaggemm.so (the HIP kernels and the C ABI) in-tree for gfx950,
+and libaggprobe.so, the benchmark's register-only matrix-core probe.
 
     python communication_gemm_amd/build.py   (run by path: importing the
                                              package would load the library)
@@ -15,8 +16,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libaggemm.so")
+PROBE_LIB = os.path.join(PKG, "libaggprobe.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "producer.hip", "consumer.hip", "scratch.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 # Packed fp32 instructions are switched off for every HIP translation unit.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -33,13 +36,14 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source (always) and link libaggemm.so atomically."""
+    """Compile every source (always) and link libaggemm.so and
+    libaggprobe.so atomically."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     cc = hipcc()
     procs = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [cc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -60,10 +64,12 @@ def build(verbose: bool = False) -> str:
             print(out)
     if failed:
         raise RuntimeError("HIP build failed")
-    tmp = LIB + f".tmp{os.getpid()}"
-    link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    subprocess.run(link, check=True)
-    os.replace(tmp, LIB)
+    n = len(SOURCES)
+    for lib, part in ((LIB, objs[:n]), (PROBE_LIB, objs[n:])):
+        tmp = lib + f".tmp{os.getpid()}"
+        link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *part, "-o", tmp]
+        subprocess.run(link, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 
