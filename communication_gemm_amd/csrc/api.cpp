@@ -547,8 +547,8 @@ int run(const Call& c)
             if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
             if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
         } else {
-            e = consumer(c.st);
-            if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
+            e = launch_producer(pa, p.producer_wgs, d->side);
+            if (e == hipSuccess) e = consumer(c.st);
         }
     } else {
         if (run_producer)
