@@ -506,6 +506,9 @@ int run(const Call& c)
         //   consumer's start.
         ca.start = header + kStartOffset / 4;
         pa.start = header + kStartOffset / 4;
+        // every copy is written by some consumer workgroup
+        ca.start_copies = cwgs < kStartCopies ? cwgs : kStartCopies;
+        pa.start_copies = ca.start_copies;
         if (s.ring > 0) {
             ca.stages = reinterpret_cast<uint64_t*>(ws + kStageOffset);
             pa.stages = ca.stages;

@@ -816,7 +816,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     // tell the producer that the work ahead of the call on this stream is
     // done (any workgroup may be the first to run)
     if (a.start && tid == 0)
-        __hip_atomic_store(a.start, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.start + (blockIdx.x % a.start_copies) * (kStartStride / 4), a.epoch,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.trace_start && blockIdx.x == 0 && tid == 0) a.trace_start[0] = ticks();
     __syncthreads();
 

@@ -31,6 +31,8 @@ struct ProducerArgs {
     uint64_t limit;                // wait limit in clock ticks
     uint64_t* trace;               // optional timestamps (see agg_options.trace)
     const uint32_t* start;         // pipelined mode: wait until it holds the epoch
+                                   // (copy blockIdx % start_copies of it)
+    int start_copies;
                                    // before reading a shard (nullptr: no wait)
     uint64_t start_limit;          // bound of that wait in clock ticks: the work
                                    // queued ahead of the call on the caller's
@@ -59,6 +61,8 @@ struct ConsumerArgs {
     uint64_t* trace;               // optional timestamps, consumer part
     uint64_t* trace_start;         // word 0 of the timestamps (call start)
     uint32_t* start;               // pipelined mode: set to the epoch on entry
+                                   // (copy blockIdx % start_copies of it)
+    int start_copies;
     uint64_t* stages;              // workspace ring: count each finished remote
                                    // tile on its stage (nullptr: no count)
     // split-K (s.ks > 1): partial sums, [tile][part][register][thread] of 4

@@ -348,7 +348,20 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     const int64_t items = chunks * ppc;
     const int producer_cus =
         opt->mode == AGG_MODE_PIPELINED && opt->producer_cus ? opt->producer_cus : num_cus;
+    // Automatic producer grid: every CU, except in an unpaced pipelined
+    // call on all CUs, where half of them.  There the copy is far shorter
+    // than the GEMM and fewer producer waves take fewer issue slots and
+    // memory requests from the consumer beside them: 8 x 1024 rows, K = N =
+    // 4096 ran 249 us pipelined with 128 producer workgroups against 258
+    // with 256, the int8 2 x 8192 x 27392 x 4096 call 1580 against 1603 us;
+    // the first chunk lands no later (about 12 us after the consumer starts
+    // either way) and the small shapes did not change.  A paced producer
+    // keeps every CU: a wave waiting for its chunk's paced time holds back
+    // its next pieces, and fewer waves fell behind the pace.
     int pw = opt->producer_wgs ? opt->producer_wgs : producer_cus;
+    if (!opt->producer_wgs && opt->mode == AGG_MODE_PIPELINED && !(opt->link_gbps > 0.0) &&
+        !opt->producer_cus && opt->producer != AGG_PRODUCER_SDMA && num_cus >= 2)
+        pw = num_cus / 2;
     if (pw > items) pw = (int)(items > 0 ? items : 1);
     if (pw < 1) pw = 1;
     p.consumer_wgs = cw;

@@ -178,7 +178,9 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     // whatever the caller queued ahead of the call.
     if (a.start) {
         if (threadIdx.x == 0)
-            stop_sh = !reached(poll_until(a.start, a.epoch, a.err, a.epoch, a.start_limit),
+            stop_sh = !reached(poll_until(a.start + (blockIdx.x % a.start_copies) *
+                                                        (kStartStride / 4),
+                                          a.epoch, a.err, a.epoch, a.start_limit),
                                a.epoch);
         __syncthreads();
         if (stop_sh) return;

@@ -35,6 +35,12 @@ constexpr int kCounterStride = 128;                       // bytes
 constexpr int kErrorOffset = kMaxShards * kCounterStride; // uint32
 constexpr int kClockOffset = kErrorOffset + kCounterStride; // uint64
 constexpr int kStartOffset = kClockOffset + kCounterStride; // uint32
+// The start word is kept in kStartCopies copies kStartStride bytes apart:
+// consumer workgroup b writes copy b % copies and producer workgroup b
+// polls copy b % copies, so the producer's first polls do not all queue
+// on one memory channel.
+constexpr int kStartCopies = 8;
+constexpr int kStartStride = 896;
 constexpr int kFlagOffset = 16384;
 constexpr int kFlagCap = 1024;       // chunks per source the flag matrix holds
 constexpr int kPieceOffset = kFlagOffset + kMaxShards * kFlagCap * 4;
@@ -46,6 +52,8 @@ constexpr int kStageOffset = kPieceOffset + kMaxShards * kFlagCap * 8;
 constexpr int kTicketOffset = kStageOffset + kMaxShards * kMaxStages * 8;
 constexpr int kMaxSplitTiles = 4096;
 constexpr int kHeaderBytes = kTicketOffset + kMaxSplitTiles * 4;
+static_assert(kStartOffset + kStartCopies * kStartStride <= kFlagOffset,
+              "start word copies overlap the flag matrix");
 
 // The producer copies a chunk in pieces, dealt to its waves in send order,
 // so that a chunk is shared by many waves and all of them work on the

@@ -498,3 +498,17 @@ def test_producer_options_plans():
     info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0,
                           agg.options(producer_cus=32, mode=agg.MODE_SEQUENTIAL))
     assert info.consumer_wgs == 256 and info.producer_wgs == 256
+
+
+def test_automatic_producer_grid():
+    # unpaced pipelined calls: half the CUs; paced, copy-only and
+    # sequential calls, and an explicit grid: as asked or every CU
+    shape = ("f16", 8, 8192, 4096, 4096, 0)
+    assert agg.plan(*shape, agg.options())[0].producer_wgs == 128
+    assert agg.plan(*shape, agg.options(link_gbps=153.0))[0].producer_wgs == 256
+    assert agg.plan(*shape, agg.options(mode=agg.MODE_COPY_ONLY))[0].producer_wgs == 256
+    assert agg.plan(*shape, agg.options(mode=agg.MODE_SEQUENTIAL))[0].producer_wgs == 256
+    assert agg.plan(*shape, agg.options(producer_wgs=200))[0].producer_wgs == 200
+    assert agg.plan(*shape, agg.options(), num_cus=80)[0].producer_wgs == 40
+    # never more workgroups than pieces: 2 x 128 rows, K 256 has 8
+    assert agg.plan("f16", 2, 256, 256, 128, 32, agg.options())[0].producer_wgs == 8
