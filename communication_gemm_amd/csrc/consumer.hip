@@ -672,20 +672,34 @@ __device__ __forceinline__ uint32_t poll_ready(const ConsumerArgs& a, int shard,
 }
 
 // Wave 0 of a workgroup, before a tile: wait until chunks [0, need) of
-// source `shard` are released (poll_ready), then acquire: an agent-scope
-// fence, which invalidates this CU's L1 and this XCD's L2 and so drops any
-// line an earlier call left at these workspace addresses.  What the
-// workgroup has already seen of the source is kept in seen[shard], so a
-// satisfied wait touches no memory.  Returns 0 after a time-out or a
-// failure elsewhere in the call.
+// source `shard` are released (poll_ready), then, with `acquire`, an
+// agent-scope fence, which invalidates this CU's L1 and this XCD's L2 and
+// so drops any line an earlier call left at these workspace addresses.
+// What the workgroup has already seen of the source is kept in
+// seen[shard], so a satisfied wait touches no memory.  Returns 0 after a
+// time-out or a failure elsewhere in the call.
+//
+// Only a workgroup's first such wait in a call needs the fence (the
+// caller passes acquire = false after it), unless the workspace is a ring
+// of stages reused within the call.  Every workspace address is written
+// once per call, every load of one is issued after its chunk's release was
+// seen, and each workgroup fences before its first such load; so after
+// that fence its CU's L1 and its XCD's L2 can take a line at a workspace
+// address only from a load that follows the line's release, which reads
+// the released data.  A stale line could only be an earlier call's, and
+// the earlier call's consumer ended before this one started.  (The fence
+// costs some microseconds, and it empties the L2 of the panels every other
+// workgroup of the XCD is sharing.)
 __device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int need,
-                                           uint32_t* seen, int tid)
+                                           uint32_t* seen, int tid, bool acquire)
 {
     const uint32_t have = seen[shard];
-    if (have >= (uint32_t)need) return 1;
-    const uint32_t got = poll_ready(a, shard, have, (uint32_t)need, tid);
-    if (!got) return 0;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    uint32_t got = have;
+    if (have < (uint32_t)need) {
+        got = poll_ready(a, shard, have, (uint32_t)need, tid);
+        if (!got) return 0;
+    }
+    if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid == 0) seen[shard] = got;
     return 1;
 }
@@ -700,9 +714,11 @@ __device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int
 //     the address before the data was written.  In this call nobody reads
 //     a chunk before its release (every read is gated) and chunk edges are
 //     cache-line edges (rows and K-blocks are whole KiB), so such a line
-//     can only be left over from an earlier call -- and the acquire at this
-//     tile's first wait, after which this wave issues every load of the
-//     tile, dropped every such line from this CU's L1 and this XCD's L2.
+//     can only be left over from an earlier call -- and the workgroup's
+//     first acquire of the call (at this tile's first wait or an earlier
+//     tile's; at this tile's with a ring of stages), after which this wave
+//     issues every load of the tile, dropped every such line from this CU's
+//     L1 and this XCD's L2.
 __device__ __forceinline__ int wait_counter(const ConsumerArgs& a, int shard, int need,
                                             uint32_t* seen, int tid)
 {
@@ -824,6 +840,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     const int64_t tiles = total_tiles(s);
     typename E::Lane L;
     E::lane_offsets(L, s.K, s.N);
+    // whether this workgroup has fenced in this call (wait_source)
+    bool acquired = false;
 
     for (int64_t p = wg_position(s, blockIdx.x, gridDim.x); p < tiles; p += gridDim.x) {
         const TileRef t = tile_at(s, p);
@@ -848,16 +866,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
                 if (s.pv > 0) {
                     // barrier scheme: the iteration's rows of every source
                     for (int q = 1; q < s.n_shards && ok; ++q)
-                        ok = wait_source(a, s.order[q], t.need, seen_sh, tid);
+                        ok = wait_source(a, s.order[q], t.need, seen_sh, tid,
+                                         q == s.n_shards - 1 && (!acquired || s.ring > 0));
                 } else {
                     const int64_t pro = kb + (int64_t)(NS - 1) * E::kBK;
                     const int kb0 = kblock_of(s, (pro < ke ? pro : ke) - 1);
-                    ok = wait_source(a, t.shard, need_at(s, t.m, kb0), seen_sh, tid);
+                    ok = wait_source(a, t.shard, need_at(s, t.m, kb0), seen_sh, tid,
+                                     !acquired || s.ring > 0);
                 }
                 if (tid == 0) ok_sh = ok;
             }
             __syncthreads();
             if (!uniform(ok_sh)) break;   // the call has failed; every lane leaves
+            acquired = true;
             if (s.pv == 0) {
                 open_kb = covered_kblocks(s, rows_need, uniform(seen_sh[t.shard]));
                 open_k = open_kb >= s.nkb ? INT32_MAX : (int32_t)(open_kb * s.kbk);
