@@ -176,6 +176,13 @@ __global__ __launch_bounds__(kProducerThreads) void producer_kernel(ProducerArgs
     // cached panels, is needed here).
     // The bound of this wait is its own, far above a chunk's: it covers
     // whatever the caller queued ahead of the call.
+    // "Reached" (at least the epoch, modulo 2^32), not "equal": a workgroup
+    // with no item of its own may still be here when the next call's
+    // consumer has written a later epoch, and it must then pass.  Stale
+    // contents of a fresh or reused workspace cannot be read here: the
+    // reset that zeroes the header is ordered before this stream's next
+    // work (ag_gemm_workspace_reset and the internal allocation both do
+    // that).
     if (a.start) {
         if (threadIdx.x == 0)
             stop_sh = !reached(poll_until(a.start + (blockIdx.x % a.start_copies) *
