@@ -489,10 +489,12 @@ int run(const Call& c)
     const bool sdma = p.producer == AGG_PRODUCER_SDMA;
     hipError_t e = hipSuccess;
     if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer) {
-        // The consumer goes first so that its persistent workgroups are all
-        // resident; the producer's small workgroups fit beside them.  No
-        // event joins the two streams (a cross-stream dependency costs
-        // about 13 us on this stack, each way):
+        // In the default form the producer is queued first, so that its
+        // workgroups are dispatched while the consumer's start; each
+        // kernel fits beside the other on a CU, so neither order keeps a
+        // consumer workgroup off the chip.  No event joins the two streams
+        // (a cross-stream dependency costs about 13 us on this stack, each
+        // way):
         // - the producer waits on the device for the consumer's start word
         //   instead of an event on the caller's stream;
         // - the caller's stream does not wait for the producer: the
