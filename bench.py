@@ -128,11 +128,22 @@ def parse():
     return ap.parse_args()
 
 
+def code_only(text):
+    """C++ source without its comments and blank lines, each line stripped:
+    what the compiler sees, so that an edited comment does not disown the
+    counters taken on unchanged code.  (The sources quote no "//" or
+    "/*" inside string literals.)"""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.strip() for ln in text.splitlines() if ln.strip())
+
+
 def consumer_digest():
     h = hashlib.sha256()
     for name in CONSUMER_SOURCES:
-        with open(os.path.join(ROOT, "communication_gemm_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "communication_gemm_amd", "csrc", name)) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()
 
 

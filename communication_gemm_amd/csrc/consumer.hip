@@ -7,18 +7,20 @@
 // their rows arrive (PTO-ISA AllGather+GEMM README: phase 1 computes the
 // local row-group with no wait, phase 2 waits on each remote source's
 // summary counter and computes as soon as the rows are there).  Before a
-// remote tile, one lane waits until the source's counter covers the tile's
-// last row; what a workgroup has already seen of a counter is remembered,
-// so most tiles pass without touching it.
+// remote tile, wave 0 waits until the chunks of the tile's rows in its
+// first K-block are released (the source's counter, or the chunk flags);
+// inside the K loop it waits again only where a slice enters a K-block not
+// yet known to be in.  What a workgroup has already seen of a source is
+// remembered, so most waits pass without touching memory.
 //
 // Tile main loop (PTO-ISA README: continuous K accumulation, multi-level
-// buffering): 4 waves, each owning a (BM/2) x (BN/2) block of 32x32 MFMA
-// accumulators kept in registers for the whole K loop.  K is walked in
-// slices of SB bytes per row; NS slices live in an LDS ring, NS-1 of them
-// in flight from HBM while the oldest is multiplied.  Inside a slice the
-// operand reads of MFMA step s+1 are issued before the MFMAs of step s, and
-// the last step's MFMAs run across the barrier that publishes the next
-// slice.
+// buffering): WM x WN waves (four, or eight with two per SIMD), each owning
+// a (BM/WM) x (BN/WN) block of 32x32 MFMA accumulators kept in registers
+// for the whole K loop.  K is walked in slices of SB bytes per row; NS
+// slices live in an LDS ring, NS-1 of them in flight from HBM while the
+// oldest is multiplied.  Inside a slice the operand reads of MFMA step s+1
+// are issued between the MFMAs of step s, and the last step's MFMAs run
+// across the barrier that publishes the next slice.
 //
 // HBM -> LDS moves use the gfx950 direct global-to-LDS load (16 bytes per
 // lane, written lane by lane at the instruction's LDS base), so no

@@ -118,3 +118,14 @@ def test_timed_brackets_one_call_in_five(steps, expect):
     assert sum(ev is not None for ev in ran[3:]) == expect
     assert [i for i, ev in enumerate(ran[3:]) if ev is not None] == list(range(0, steps, 5))
     assert len(per) == expect and c == 1.0
+
+
+def test_consumer_digest_ignores_comments():
+    import bench
+    a = "int f(int x) {  // add one\n    return x + 1; /* the sum */\n}\n"
+    b = "// header\nint f(int x) {\n\n    return x + 1;\n}\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench.code_only(a) == bench.code_only(b)
+    assert bench.code_only(a) != bench.code_only(c)
+    # the stored counter note is tied to the consumer's code as it stands
+    assert bench.stored_traffic("f16 8x1024 rows M=8192 K=4096 N=4096") is not None
