@@ -40,6 +40,10 @@ Helpers for those runs:
                                             (fp16 and fp8, random against
                                             constant operands): TFLOP/s, GFX
                                             clocks and board power under load
+    python bench.py --load-probe            the operand-movement probe: one
+                                            64 KiB K slice per CU into LDS
+                                            and 192 KiB out of it, per
+                                            iteration, in several patterns
     python bench.py --only KIND             only KIND's timed steps (f16 of
                                             --case, bf16, fp8 or i8) in --mode
     python bench.py --pmc-summary DIR       mean counter value per dispatch
@@ -116,6 +120,8 @@ def parse():
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only run the register-only matrix-core probe")
+    ap.add_argument("--load-probe", action="store_true",
+                    help="only run the operand-movement probe (loads into LDS, LDS reads)")
     ap.add_argument("--only", choices=("bf16", "fp8", "i8"),
                     help="only this variant's timed steps, in --mode (for counter runs)")
     ap.add_argument("--vendor-only", action="store_true",
@@ -629,6 +635,87 @@ def run_variant(args, torch, agg, synth, kind, mode="pipelined"):
             "consumer_frac_of_peak": round(flops / (c * 1e-3) / 1e12 / peak, 4)}
 
 
+def load_probe(torch, iters=1024):
+    """The operand-movement probe (libaggprobe.so): per iteration each of
+    256 workgroups (one per CU) moves one 64 KiB K slice into LDS with the
+    direct global-to-LDS load, reads 192 KiB out of LDS, or both, then waits
+    and meets at a barrier: one K slice of the 256 x 256 fp16 consumer
+    tile.  Microseconds per iteration, per pattern."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: build with communication_gemm_amd/build.py")
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.agg_probe_loads
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
+                   ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    wgs = 256
+    pitch_max = 8320
+    A = torch.ones(4096 * pitch_max, dtype=torch.uint8, device="cuda")
+    B = torch.ones(64 * 64 * pitch_max, dtype=torch.uint8, device="cuda")
+    out = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    cases = [
+        ("contiguous 64 KiB, loads", 0, 1, 8192, 64),
+        ("tile pattern, pitch 8192, loads", 1, 1, 8192, 64),
+        ("tile pattern, pitch 8320, loads", 1, 1, 8320, 64),
+        ("tile pattern, 4 slices (L2-resident), loads", 1, 1, 8192, 4),
+        ("LDS reads only (192 KiB)", 1, 2, 8192, 64),
+        ("tile pattern loads + LDS reads", 1, 3, 8192, 64),
+    ]
+    res = {}
+    for name, pattern, what, pitch, ns in cases:
+        a_bytes, b_bytes = 4096 * pitch, 64 * 64 * pitch
+        def launch(n=iters):
+            rc = fn(pattern, what, n, wgs, ctypes.c_void_p(A.data_ptr()), a_bytes,
+                    ctypes.c_void_p(B.data_ptr()), b_bytes, pitch, ns,
+                    ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+            if rc:
+                raise SystemExit(f"load probe launch failed: {rc}")
+        ramp(torch, launch, calls=5)
+        t, _ = timed(torch, lambda ev: launch, 5, 1, with_consumer=False)
+        res[name] = round(t * 1e3 / iters, 3)
+        print(json.dumps({"load_probe": name, "us_per_slice": res[name]}), flush=True)
+    del A, B
+    # whole-matrix streaming into LDS: an int8 16384 x 7168 weight (117 MB),
+    # one launch reading all of it, on one buffer (which the 256 MB
+    # last-level cache then holds) or rotating over three (351 MB, so each
+    # launch reads HBM)
+    sfn = lib.agg_probe_stream
+    sfn.restype = ctypes.c_int
+    sfn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint32,
+                    ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    rows, row_bytes = 16384, 7168
+    mats = [torch.ones(rows * row_bytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    stream_cases = [
+        ("64-byte column strips, 2 parts (224 workgroups)", 0, 2),
+        ("contiguous ranges, 224 workgroups", 1, 224),
+        ("contiguous ranges, 448 workgroups", 1, 448),
+    ]
+    srate = {}
+    for name, pattern, n in stream_cases:
+        for rot in (1, 3):
+            k = [0]
+            def launch():
+                m = mats[k[0] % rot]
+                k[0] += 1
+                rc = sfn(pattern, n, ctypes.c_void_p(m.data_ptr()), rows, row_bytes,
+                         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+                if rc:
+                    raise SystemExit(f"stream probe launch failed: {rc}")
+            ramp(torch, launch, calls=20)
+            t, _ = timed(torch, lambda ev: launch, 60, 3, with_consumer=False)
+            key = f"{name}, {'one buffer' if rot == 1 else 'three buffers'}"
+            srate[key] = {"us": round(t * 1e3, 2),
+                          "TB_per_s": round(rows * row_bytes / (t * 1e-3) / 1e12, 2)}
+            print(json.dumps({"stream_probe": key, **srate[key]}), flush=True)
+    return {"us_per_iteration": res, "workgroups": wgs, "iterations": iters,
+            "note": "one 64 KiB slice per CU per iteration (A 256 rows x 128 B, B 64 rows x "
+                    "512 B), 192 KiB of ds_read_b128 per CU, wait and barrier each iteration",
+            "stream_int8_16384x7168": srate}
+
+
 def only_variant(args, torch, agg, synth):
     """--only: one variant's timed steps in --mode, nothing else (the
     workload hardware-counter runs profile)."""
@@ -809,6 +896,9 @@ def main():
         return
     if args.mfma_probe:
         print(json.dumps({"mfma_probe": mfma_probe(torch)}), flush=True)
+        return
+    if args.load_probe:
+        print(json.dumps({"load_probe": load_probe(torch)}), flush=True)
         return
     if args.only:
         print(json.dumps(only_variant(args, torch, agg, synth)), flush=True)
