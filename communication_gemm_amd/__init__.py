@@ -13,7 +13,7 @@ only binds it.
 from ._native import (  # noqa: F401
     AGG_E_HIP, AGG_E_INVALID, AGG_E_NOMEM, AGG_E_TIMEOUT, AGG_E_TOO_LARGE, AGG_E_UNSUPPORTED,
     AGG_OK, LIB_PATH, NOALLOC_MAX_BYTES, LINKS_PARALLEL, LINKS_SERIAL, MAX_SHARDS, MODE_COMPUTE_ONLY, MODE_COPY_ONLY,
-    MODE_PIPELINED, MODE_SEQUENTIAL, PRODUCER_KERNEL, PRODUCER_SDMA, SCHEME_BARRIER,
+    MODE_PIPELINED, MODE_SEQUENTIAL, PRODUCER_KERNEL, PRODUCER_SDMA, PRODUCER_SEPARATE, PRODUCER_FUSED, SCHEME_BARRIER,
     SCHEME_COUNTERS, AggError, Options,
     PlanInfo, Prepared, ag_gemm_bf16, ag_gemm_f16, ag_gemm_f16_noalloc, ag_gemm_fp8,
     ag_gemm_i8_dequant, check,

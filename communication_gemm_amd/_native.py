@@ -20,7 +20,7 @@ NOALLOC_MAX_BYTES = 64 << 20   # AGG_NOALLOC_MAX_BYTES
 MODE_PIPELINED, MODE_COMPUTE_ONLY, MODE_SEQUENTIAL, MODE_COPY_ONLY = range(4)
 SCHEME_COUNTERS, SCHEME_BARRIER = range(2)
 LINKS_PARALLEL, LINKS_SERIAL = range(2)
-PRODUCER_KERNEL, PRODUCER_SDMA = range(2)
+PRODUCER_KERNEL, PRODUCER_SDMA, PRODUCER_SEPARATE, PRODUCER_FUSED = range(4)
 MAX_SHARDS = 64
 
 
@@ -87,6 +87,7 @@ class PlanInfo(ctypes.Structure):
         ("k_splits", ctypes.c_int),
         ("k_blocks", ctypes.c_int),
         ("k_block", ctypes.c_int64),
+        ("producer_fused", ctypes.c_int),
     ]
 
 

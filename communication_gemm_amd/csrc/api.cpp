@@ -25,6 +25,13 @@ struct Track {
     uint32_t checked;
     int device;
     bool used;                 // a call ran on it since the last check
+    // A stream other than the caller's on which a producer of this
+    // workspace was queued last (the library's side stream or a CU-masked
+    // one), or null.  Such a producer can still be finishing its last
+    // counter update when the call's consumer has ended; a producer queued
+    // elsewhere must not start before that, or the two would work on the
+    // same counters out of order.
+    hipStream_t pending;
 };
 
 struct Device {
@@ -35,6 +42,7 @@ struct Device {
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr;  // orders a ring-mode producer after the consumer
     hipEvent_t join = nullptr;  // joins a CU-masked consumer back to the caller
+    hipEvent_t drain = nullptr; // orders a producer after one on another stream
     hipStream_t pmask[3] = {};  // CU-masked producer / consumer streams, by
     hipStream_t cmask[3] = {};  //   producer CUs / 32 (made on first use)
     char* scratch = nullptr;   // the allocation-free entry point's array here
@@ -103,6 +111,8 @@ int device_ready(Device& d, hipStream_t st)
     if (!d.fork && hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) != hipSuccess)
         return AGG_E_HIP;
     if (!d.join && hipEventCreateWithFlags(&d.join, hipEventDisableTiming) != hipSuccess)
+        return AGG_E_HIP;
+    if (!d.drain && hipEventCreateWithFlags(&d.drain, hipEventDisableTiming) != hipSuccess)
         return AGG_E_HIP;
     void* p = nullptr;
     if (scratch_address(&p) != hipSuccess) {
@@ -462,6 +472,8 @@ int run(const Call& c)
 
     int occ = occupancy(*d, kind, p.shape.id);
     if (occ < 1) return AGG_E_HIP;
+    // the plan's rule for a fused launch and the kernels built agree
+    if (p.fused && !fused_built(kind, p.shape.id)) return AGG_E_UNSUPPORTED;
     int cwgs = p.consumer_wgs;
     // a persistent grid larger than what can be resident at once gains
     // nothing, and its waiting workgroups would sit in front of the producer
@@ -487,8 +499,28 @@ int run(const Call& c)
     };
 
     const bool sdma = p.producer == AGG_PRODUCER_SDMA;
+    // the producer of this call goes on stream x: after this workspace's
+    // last producer if that one was queued on another stream (a one-time
+    // cross-stream wait when calls change how they run)
+    auto producer_on = [&](hipStream_t x) -> hipError_t {
+        hipError_t r = hipSuccess;
+        if (tr->pending && tr->pending != x) {
+            r = hipEventRecord(d->drain, tr->pending);
+            if (r == hipSuccess) r = hipStreamWaitEvent(x, d->drain, 0);
+        }
+        tr->pending = x == c.st ? nullptr : x;
+        return r;
+    };
     hipError_t e = hipSuccess;
-    if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer) {
+    if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer && p.fused) {
+        // One launch on the caller's stream, the producer's workgroups
+        // first; stream order replaces the start word.
+        e = producer_on(c.st);
+        if (e == hipSuccess && cev[0]) e = hipEventRecord(cev[0], c.st);
+        if (e == hipSuccess)
+            e = launch_fused(kind, ca, pa, p.shape.id, cwgs, p.producer_wgs, c.st);
+        if (e == hipSuccess && cev[1]) e = hipEventRecord(cev[1], c.st);
+    } else if (p.mode == AGG_MODE_PIPELINED && run_producer && run_consumer) {
         // In the default form the producer is queued first, so that its
         // workgroups are dispatched while the consumer's start; each
         // kernel fits beside the other on a CU, so neither order keeps a
@@ -520,7 +552,8 @@ int run(const Call& c)
             // stream, recorded before the consumer, holds them back until
             // the work ahead of the call is done.  The join is as above:
             // the counter writes follow the copies on the library's stream.
-            e = hipEventRecord(d->fork, c.st);
+            e = producer_on(d->side);
+            if (e == hipSuccess) e = hipEventRecord(d->fork, c.st);
             if (e == hipSuccess) e = consumer(c.st);
             if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
             if (e == hipSuccess) e = enqueue_sdma(s, pa, p.elt, d->side);
@@ -533,7 +566,8 @@ int run(const Call& c)
             hipStream_t ps = nullptr, cs = nullptr;
             rc = masked_streams(*d, p.producer_cus, &ps, &cs);
             if (rc) return rc;
-            e = hipEventRecord(d->fork, c.st);
+            e = producer_on(ps);
+            if (e == hipSuccess) e = hipEventRecord(d->fork, c.st);
             if (e == hipSuccess) e = hipStreamWaitEvent(cs, d->fork, 0);
             if (e == hipSuccess) e = consumer(cs);
             if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, ps);
@@ -547,17 +581,23 @@ int run(const Call& c)
             // producer back until the work ahead of the call is done, by
             // which time the consumer's grid has been dispatched.  (Should
             // a wait still starve, it ends at the time limit as an error.)
-            e = hipEventRecord(d->fork, c.st);
+            e = producer_on(d->side);
+            if (e == hipSuccess) e = hipEventRecord(d->fork, c.st);
             if (e == hipSuccess) e = consumer(c.st);
             if (e == hipSuccess) e = hipStreamWaitEvent(d->side, d->fork, 0);
             if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
         } else {
-            e = launch_producer(pa, p.producer_wgs, d->side);
+            e = producer_on(d->side);
+            if (e == hipSuccess) e = launch_producer(pa, p.producer_wgs, d->side);
             if (e == hipSuccess) e = consumer(c.st);
         }
     } else {
-        if (run_producer)
-            e = sdma ? enqueue_sdma(s, pa, p.elt, c.st) : launch_producer(pa, p.producer_wgs, c.st);
+        if (run_producer) {
+            e = producer_on(c.st);
+            if (e == hipSuccess)
+                e = sdma ? enqueue_sdma(s, pa, p.elt, c.st)
+                         : launch_producer(pa, p.producer_wgs, c.st);
+        }
         if (e == hipSuccess && run_consumer) e = consumer(c.st);
     }
     if (e != hipSuccess) return AGG_E_HIP;

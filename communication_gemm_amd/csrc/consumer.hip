@@ -32,6 +32,7 @@
 // of one column.  16-byte pieces are XOR-swizzled per row, the swizzle
 // applied by choosing which global piece each lane fetches.
 #include "kernels.hpp"
+#include "producer_body.hpp"
 #include "sync.hpp"
 
 namespace agg {
@@ -827,14 +828,26 @@ __device__ bool split_reduce(const ConsumerArgs& a, const TileRef& t, int tid, i
     return true;
 }
 
+// Workgroup-shared state of a consumer workgroup: what it has seen of each
+// source, and two flags wave 0 hands the other waves.  Declared by each
+// kernel that runs the consumer (with the dynamic LDS of the tile ring) and
+// handed in, so that every LDS variable belongs to one kernel.
+struct ConsumerShared {
+    uint32_t seen[kMaxShards];
+    int ok;
+    int last;
+};
+
+// The consumer: workgroup `block` of `blocks` (blockIdx.x and gridDim.x in
+// the consumer kernel; past the producer workgroups in the fused one).
 template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs a)
+__device__ __forceinline__ void consume(const ConsumerArgs& a, uint32_t block, uint32_t blocks,
+                                        ConsumerShared& sh, char* lds)
 {
     typedef Engine<T, BM, BN, SB, NS, WM, WN> E;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ uint32_t seen_sh[kMaxShards];
-    __shared__ int ok_sh;
-    __shared__ int last_sh;
+    uint32_t* seen_sh = sh.seen;
+    int& ok_sh = sh.ok;
+    int& last_sh = sh.last;
 
     const Schedule& s = a.s;
     const int tid = threadIdx.x;
@@ -842,9 +855,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     // tell the producer that the work ahead of the call on this stream is
     // done (any workgroup may be the first to run)
     if (a.start && tid == 0)
-        __hip_atomic_store(a.start + (blockIdx.x % a.start_copies) * (kStartStride / 4), a.epoch,
+        __hip_atomic_store(a.start + (block % a.start_copies) * (kStartStride / 4), a.epoch,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (a.trace_start && blockIdx.x == 0 && tid == 0) a.trace_start[0] = ticks();
+    if (a.trace_start && block == 0 && tid == 0) a.trace_start[0] = ticks();
     __syncthreads();
 
     const int64_t tiles = total_tiles(s);
@@ -853,7 +866,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     // whether this workgroup has fenced in this call (wait_source)
     bool acquired = false;
 
-    for (int64_t p = wg_position(s, blockIdx.x, gridDim.x); p < tiles; p += gridDim.x) {
+    for (int64_t p = wg_position(s, block, blocks); p < tiles; p += blocks) {
         const TileRef t = tile_at(s, p);
         // K range: all of K, or part kp of a split-K tile (parts hold a
         // multiple of 256 k, a whole number of slices)
@@ -959,6 +972,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs 
     }
 }
 
+template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void consumer_kernel(ConsumerArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ ConsumerShared sh;
+    consume<T, BM, BN, SB, NS, WM, WN>(a, blockIdx.x, gridDim.x, sh, lds);
+}
+
+// Producer and consumer in one launch on the caller's stream: workgroups
+// 0 .. producers - 1 run the producer, the others the consumer.  The
+// producer workgroups come first, so they are dispatched before any
+// consumer workgroup that could wait for them, and they wait for nothing
+// themselves (stream order replaces the start word): the launch cannot
+// starve even when its workgroups do not all fit on the device at once.
+// Built for the four-wave tiles of up to 128 x 128, whose workgroups have
+// the producer's four waves.
+template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void fused_kernel(ConsumerArgs a, ProducerArgs p,
+                                                                 int producers)
+{
+    static_assert(WM * WN == prod::kProducerWaves, "producer workgroups of four waves");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ ConsumerShared sh;
+    __shared__ prod::ProducerShared psh;
+    if ((int)blockIdx.x < producers) {
+        prod::produce(p, blockIdx.x, (uint32_t)producers, psh);
+        return;
+    }
+    consume<T, BM, BN, SB, NS, WM, WN>(a, blockIdx.x - (uint32_t)producers,
+                                        gridDim.x - (uint32_t)producers, sh, lds);
+}
+
 // Tile configurations: output tile, slice width (bytes of K per row), LDS
 // ring depth and wave grid, by the id the host plans with.  The big tiles
 // walk K in 64-byte slices with four stages (three in flight) or in
@@ -1006,6 +1051,26 @@ struct Kern {
                            dim3(wgs), dim3(E::kThreads), (size_t)E::kLds, st, a);
         return hipGetLastError();
     }
+    static const void* fused_fn()
+    {
+        return reinterpret_cast<const void*>(
+            fused_kernel<T, C::BM, C::BN, C::SB, C::NS, C::WM, C::WN>);
+    }
+    static hipError_t launch_fused(const ConsumerArgs& a, const ProducerArgs& p, int wgs,
+                                   int producers, hipStream_t st)
+    {
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(
+                fused_fn(), hipFuncAttributeMaxDynamicSharedMemorySize, E::kLds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL((fused_kernel<T, C::BM, C::BN, C::SB, C::NS, C::WM, C::WN>),
+                           dim3(producers + wgs), dim3(E::kThreads), (size_t)E::kLds, st, a, p,
+                           producers);
+        return hipGetLastError();
+    }
     static int occupancy()
     {
         int n = 0;
@@ -1042,6 +1107,25 @@ hipError_t launch_id(const ConsumerArgs& a, int wgs, hipStream_t st)
         return hipErrorInvalidValue;
 }
 
+// Whether the fused kernel is built for configuration ID and traits T: the
+// four-wave tiles of up to 128 x 128 (the small calls it is for).
+template <class T, int ID>
+constexpr bool fusable()
+{
+    typedef Cfg<ID> C;
+    return supported<T, ID>() && C::WM * C::WN == 4 && C::BM * C::BN <= 128 * 128;
+}
+
+template <class T, int ID>
+hipError_t launch_fused_id(const ConsumerArgs& a, const ProducerArgs& p, int wgs, int producers,
+                           hipStream_t st)
+{
+    if constexpr (fusable<T, ID>())
+        return Kern<T, ID>::launch_fused(a, p, wgs, producers, st);
+    else
+        return hipErrorInvalidValue;
+}
+
 template <class T, int ID>
 int occupancy_id()
 {
@@ -1070,6 +1154,33 @@ hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t 
     case 13: return launch_id<T, 13>(a, wgs, st);
     case 14: return launch_id<T, 14>(a, wgs, st);
     default: return hipErrorInvalidValue;
+    }
+}
+
+template <class T>
+hipError_t launch_fused_kind(const ConsumerArgs& a, const ProducerArgs& p, int tile_id, int wgs,
+                             int producers, hipStream_t st)
+{
+    switch (tile_id) {
+    case 2: return launch_fused_id<T, 2>(a, p, wgs, producers, st);
+    case 3: return launch_fused_id<T, 3>(a, p, wgs, producers, st);
+    case 12: return launch_fused_id<T, 12>(a, p, wgs, producers, st);
+    case 13: return launch_fused_id<T, 13>(a, p, wgs, producers, st);
+    case 14: return launch_fused_id<T, 14>(a, p, wgs, producers, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class T>
+bool fused_kind(int tile_id)
+{
+    switch (tile_id) {
+    case 2: return fusable<T, 2>();
+    case 3: return fusable<T, 3>();
+    case 12: return fusable<T, 12>();
+    case 13: return fusable<T, 13>();
+    case 14: return fusable<T, 14>();
+    default: return false;
     }
 }
 
@@ -1115,6 +1226,23 @@ hipError_t launch_consumer_i8(const ConsumerArgs& a, int tile_id, int wgs, hipSt
 hipError_t launch_consumer_fp8(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t st)
 {
     return launch_kind<FP8>(a, tile_id, wgs, st);
+}
+
+hipError_t launch_fused(int kind, const ConsumerArgs& a, const ProducerArgs& p, int tile_id,
+                        int wgs, int producers, hipStream_t st)
+{
+    return kind == 0 ? launch_fused_kind<F16>(a, p, tile_id, wgs, producers, st)
+         : kind == 2 ? launch_fused_kind<BF16>(a, p, tile_id, wgs, producers, st)
+         : kind == 3 ? launch_fused_kind<FP8>(a, p, tile_id, wgs, producers, st)
+                     : launch_fused_kind<I8>(a, p, tile_id, wgs, producers, st);
+}
+
+bool fused_built(int kind, int tile_id)
+{
+    return kind == 0 ? fused_kind<F16>(tile_id)
+         : kind == 2 ? fused_kind<BF16>(tile_id)
+         : kind == 3 ? fused_kind<FP8>(tile_id)
+                     : fused_kind<I8>(tile_id);
 }
 
 int consumer_occupancy(int kind, int tile_id)

@@ -81,6 +81,12 @@ hipError_t launch_consumer_bf16(const ConsumerArgs& a, int tile_id, int wgs,
 hipError_t launch_consumer_fp8(const ConsumerArgs& a, int tile_id, int wgs,
                                hipStream_t st);
 hipError_t launch_header_reset(uint32_t* header, size_t bytes, hipStream_t st);
+// Producer and consumer in one launch on `st`: `producers` producer
+// workgroups, then `wgs` consumer workgroups (kind: 0 fp16, 1 int8, 2 bf16,
+// 3 fp8).  Built for the tiles fused_built() names.
+hipError_t launch_fused(int kind, const ConsumerArgs& c, const ProducerArgs& p, int tile_id,
+                        int wgs, int producers, hipStream_t st);
+bool fused_built(int kind, int tile_id);
 
 // The allocation-free entry point's workspace: a file-scope device array of
 // kScratchBytes per GPU.  scratch_address() gives its address on the

@@ -151,7 +151,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     if (opt->k_splits < 0) return AGG_E_INVALID;
     if (!(opt->timeout_ms >= 0.0)) return AGG_E_INVALID;
     if (!(opt->debug_delay_us >= 0.0) || isinf(opt->debug_delay_us)) return AGG_E_INVALID;
-    if (opt->producer != AGG_PRODUCER_KERNEL && opt->producer != AGG_PRODUCER_SDMA)
+    if (opt->producer < AGG_PRODUCER_KERNEL || opt->producer > AGG_PRODUCER_FUSED)
         return AGG_E_INVALID;
     if (opt->producer_cus < 0) return AGG_E_INVALID;
     const bool sdma = opt->producer == AGG_PRODUCER_SDMA;
@@ -364,6 +364,22 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         pw = num_cus / 2;
     if (pw > items) pw = (int)(items > 0 ? items : 1);
     if (pw < 1) pw = 1;
+    // One launch for both (pipelined): by default when the consumer's tile
+    // has a fused build and the two grids fit on the CUs together, each
+    // workgroup on a CU of its own -- the calls that leave most of the
+    // device idle, whose time is the launches'.  An automatic producer
+    // grid is then rounded up to whole multiples of 8 workgroups, so the
+    // consumer's workgroups, which follow them in the grid, keep their
+    // XCDs (workgroup b runs on XCD b mod 8).
+    bool fused = false;
+    if (opt->mode == AGG_MODE_PIPELINED &&
+        (opt->producer == AGG_PRODUCER_KERNEL || opt->producer == AGG_PRODUCER_FUSED)) {
+        const bool can = fusable_tile(p.shape) && s.ring == 0 && !opt->producer_cus;
+        if (opt->producer == AGG_PRODUCER_FUSED && !can) return AGG_E_UNSUPPORTED;
+        const int pw_fused = opt->producer_wgs ? pw : (pw + 7) / 8 * 8;
+        fused = can && (opt->producer == AGG_PRODUCER_FUSED || cw + pw_fused <= num_cus);
+        if (fused) pw = pw_fused;
+    }
     p.consumer_wgs = cw;
     p.producer_wgs = pw;
     p.ppc = ppc;
@@ -381,6 +397,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     }
     p.drop_chunk = opt->debug_drop_chunk;
     p.producer = opt->producer;
+    p.fused = fused;
     p.producer_cus = opt->mode == AGG_MODE_PIPELINED ? opt->producer_cus : 0;
     *out = p;
     return AGG_OK;
@@ -459,6 +476,7 @@ int ag_gemm_plan(int kind, int n_shards, int64_t M, int64_t K, int64_t N,
         info->k_splits = s.ks;
         info->k_blocks = s.nkb;
         info->k_block = s.kbk;
+        info->producer_fused = p.fused ? 1 : 0;
     }
     if (tile_order) {
         int64_t T = agg::total_tiles(s);

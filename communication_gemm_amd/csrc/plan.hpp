@@ -30,6 +30,11 @@ constexpr int kSplitTile = 14;
 // Output tiles the consumer kernels are built for, per path.
 const TileShape* tile_shapes(Kind kind, int* count);
 
+// Whether the fused kernel (producer and consumer in one launch) is built
+// for a tile: four waves, like a producer workgroup, and at most 128 x 128
+// outputs (the small calls whose time is launch cost).
+inline bool fusable_tile(const TileShape& t) { return t.threads == 256 && t.tm * t.tn <= 128 * 128; }
+
 struct Plan {
     Schedule sched;
     TileShape shape;
@@ -45,7 +50,8 @@ struct Plan {
     size_t ws_bytes;    // workspace bytes this call needs
     size_t part_off;    // split-K partial sums: offset in the workspace
     int drop_chunk;
-    int producer;       // AGG_PRODUCER_KERNEL or AGG_PRODUCER_SDMA
+    int producer;       // enum agg_producer, as asked
+    bool fused;         // pipelined: producer and consumer in one launch
     int producer_cus;   // CUs the pipelined producer is masked to (0: all)
 };
 

@@ -34,7 +34,8 @@
  * share the workspace and race.
  *
  * Streams (pipelined mode): the consumer GEMM runs on `stream`; the producer
- * runs on a stream of the library's own, with no event between the two.
+ * runs on a stream of the library's own, with no event between the two
+ * (unless both run in one launch on `stream`: AGG_PRODUCER_FUSED).
  * The producer reads no shard before the consumer has started (the
  * consumer's start, in `stream` order, proves that the work queued ahead of
  * the call is done; the producer waits for it on the device, for at most
@@ -98,8 +99,14 @@ enum agg_scheme {
  * communication runs on engines of its own beside the compute). */
 enum agg_producer {
     AGG_PRODUCER_KERNEL = 0, /* the producer kernel: compute-unit loads and
-                                stores, per-piece release (default)        */
-    AGG_PRODUCER_SDMA = 1    /* the DMA engines: one copy per row group of
+                                stores, per-piece release (default).  In a
+                                pipelined call whose consumer tile has four
+                                waves and at most 128 x 128 outputs, and
+                                whose producer and consumer grids fit on
+                                the device's CUs together, both run in one
+                                launch (as AGG_PRODUCER_FUSED); otherwise as
+                                AGG_PRODUCER_SEPARATE                      */
+    AGG_PRODUCER_SDMA = 1,   /* the DMA engines: one copy per row group of
                                 one m-tile and source, in send order, on the
                                 library's stream, each followed by a stream
                                 write of the source's counter (the release,
@@ -107,6 +114,20 @@ enum agg_producer {
                                 compute unit moves data.  Chunks span all of
                                 K; no pacing, workspace ring, trace of
                                 releases or test hooks (AGG_E_UNSUPPORTED)  */
+    AGG_PRODUCER_SEPARATE = 2, /* the producer kernel as a launch of its own:
+                                on the library's stream in pipelined calls
+                                (see "Streams" above)                      */
+    AGG_PRODUCER_FUSED = 3   /* pipelined calls: producer and consumer in one
+                                launch on `stream`, the producer's
+                                workgroups first in the grid (one host
+                                launch instead of two; the small calls are
+                                bound by launch cost).  Stream order puts
+                                the work ahead of the call before it, so
+                                there is no start word.  Consumer tiles with
+                                four waves and at most 128 x 128 outputs
+                                only; no workspace ring or producer_cus
+                                (AGG_E_UNSUPPORTED).  Outside the pipelined
+                                mode, as AGG_PRODUCER_KERNEL              */
 };
 
 /* How the emulated links are paced when link_gbps > 0. */
@@ -431,6 +452,7 @@ typedef struct agg_plan_info {
     int k_splits;           /* parts of K per output tile (1: no split-K)   */
     int k_blocks;           /* K-blocks per row chunk (1: chunks span K)    */
     int64_t k_block;        /* elements of K per K-block (K when 1 block)   */
+    int producer_fused;     /* 1: producer and consumer in one launch        */
 } agg_plan_info;
 
 /*

@@ -467,7 +467,12 @@ def test_automatic_chunks(kind, n, M, K, N, opts, cr, nkb):
 # ---- producer options: DMA engines, CU-masked producer ---------------
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(producer=2), agg.AGG_E_INVALID),
+    (dict(producer=4), agg.AGG_E_INVALID),
+    (dict(producer=-1), agg.AGG_E_INVALID),
+    (dict(producer=3), agg.AGG_E_UNSUPPORTED),               # 8-wave automatic tile
+    (dict(producer=3, tile=13, workspace_stages=2), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=3, tile=13, producer_cus=32), agg.AGG_E_UNSUPPORTED),
+    (dict(producer=3, tile=6), agg.AGG_E_UNSUPPORTED),       # 256 x 256
     (dict(producer_cus=-8), agg.AGG_E_INVALID),
     (dict(producer_cus=12), agg.AGG_E_UNSUPPORTED),
     (dict(producer_cus=16), agg.AGG_E_UNSUPPORTED),
@@ -498,6 +503,43 @@ def test_producer_options_plans():
     info, _, _ = agg.plan("f16", 8, 8192, 4096, 4096, 0,
                           agg.options(producer_cus=32, mode=agg.MODE_SEQUENTIAL))
     assert info.consumer_wgs == 256 and info.producer_wgs == 256
+
+
+def test_fused_launch_choice():
+    # pipelined calls whose two grids fit on the CUs together, on a tile the
+    # fused kernel is built for, run in one launch; the automatic producer
+    # grid is then whole multiples of 8 workgroups
+    small = ("f16", 2, 256, 256, 128, 0)
+    info = agg.plan(*small, agg.options())[0]
+    assert info.producer_fused == 1 and info.tile_id == 13
+    assert info.producer_wgs % 8 == 0 and info.producer_wgs + info.consumer_wgs <= 256
+    for kind in ("bf16", "fp8", "i8"):
+        assert agg.plan(kind, 2, 256, 256, 128, 0, agg.options())[0].producer_fused == 1
+    assert agg.plan(*small, agg.options(link_gbps=153.0))[0].producer_fused == 1
+    # an explicit producer grid is kept as asked
+    info = agg.plan(*small, agg.options(producer_wgs=3))[0]
+    assert info.producer_fused == 1 and info.producer_wgs == 3
+    # not fused: the separate kernel asked for, other modes, the DMA engines,
+    # a CU-masked producer, a workspace ring, grids that fill the device,
+    # the 8-wave tiles
+    for kw in (dict(producer=2), dict(mode=agg.MODE_SEQUENTIAL), dict(mode=agg.MODE_COPY_ONLY),
+               dict(producer=1), dict(producer_cus=32), dict(tile=8)):
+        assert agg.plan(*small, agg.options(**kw))[0].producer_fused == 0, kw
+    ringed = ("f16", 2, 1024, 256, 128, 0)
+    assert agg.plan(*ringed, agg.options())[0].producer_fused == 1
+    info = agg.plan(*ringed, agg.options(workspace_stages=2))[0]
+    assert info.workspace_stages == 2 and info.producer_fused == 0
+    assert agg.plan("f16", 2, 2048, 2048, 1024, 0, agg.options())[0].producer_fused == 0
+    assert agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options())[0].producer_fused == 0
+    assert agg.plan("i8", 2, 64, 16384, 7168, 0, agg.options())[0].producer_fused == 0
+    # asked for: fused whatever the grids (producer workgroups come first in
+    # the launch, so a grid larger than the device still cannot starve);
+    # outside the pipelined mode the producer runs as a kernel of its own
+    info = agg.plan("f16", 8, 8192, 4096, 4096, 0, agg.options(producer=3, tile=13))[0]
+    assert info.producer_fused == 1 and info.consumer_wgs == 256
+    for tile in (2, 3, 12, 13, 14):
+        assert agg.plan(*small, agg.options(producer=3, tile=tile))[0].producer_fused == 1
+    assert agg.plan(*small, agg.options(producer=3, mode=agg.MODE_SEQUENTIAL))[0].producer_fused == 0
 
 
 def test_automatic_producer_grid():
