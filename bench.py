@@ -153,9 +153,10 @@ def consumer_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload):
+def stored_traffic(workload, tile_id=None):
     """HBM bytes per consumer launch from the counter note, or None when the
-    note is missing, is for another workload, or predates the sources."""
+    note is missing, is for another workload or tile, or predates the
+    sources."""
     try:
         with open(TRAFFIC_NOTE) as f:
             kv = dict(line.strip()[2:].split(": ", 1) for line in f
@@ -165,6 +166,8 @@ def stored_traffic(workload):
     if kv.get("consumer_sources_sha256") != consumer_digest():
         return None
     if kv.get("workload") != workload:
+        return None
+    if tile_id is not None and kv.get("tile_id") != str(tile_id):
         return None
     return float(kv["hbm_bytes_per_launch"])
 
@@ -399,9 +402,12 @@ def mfma_probe(torch, seconds=1.5):
     out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     res = {"cus": cus, "waves_per_cu": 8, "peak_tflops": {"f16": PEAK_F16_TFLOPS,
-                                                          "fp8": PEAK_FP8_TFLOPS}}
-    # flops per instruction: 2 x 32 x 32 x 16 (fp16), 2 x 32 x 32 x 64 (fp8)
-    for kind, name, flop in ((0, "f16", 32768), (1, "fp8", 131072)):
+                                                          "fp8": PEAK_FP8_TFLOPS,
+                                                          "i8": PEAK_I8_TOPS}}
+    # flops per chain and iteration: one 2 x 32 x 32 x 16 (fp16), one
+    # 2 x 32 x 32 x 64 (fp8), two 2 x 16 x 16 x 32 (fp16 16x16x32)
+    for kind, name, flop in ((0, "f16", 32768), (2, "f16_16x16x32", 32768), (1, "fp8", 131072),
+                             (3, "i8", 65536), (4, "i8_16x16x64", 65536)):
         for random, pattern in ((1, "random"), (0, "constant")):
             def launch(iters):
                 rc = fn(kind, random, iters, cus, 1234, ctypes.c_void_p(out.data_ptr()),
@@ -428,7 +434,8 @@ def mfma_probe(torch, seconds=1.5):
                 "ms_per_launch": round(t, 4), "iters": iters,
                 "tflops": round(flops / (t * 1e-3) / 1e12, 1),
                 "frac_of_peak": round(flops / (t * 1e-3) / 1e12 /
-                                      (PEAK_F16_TFLOPS if kind == 0 else PEAK_FP8_TFLOPS), 4),
+                                      (PEAK_FP8_TFLOPS if kind == 1 else PEAK_I8_TOPS
+                                       if kind in (3, 4) else PEAK_F16_TFLOPS), 4),
                 "under_load": clocks}
             print(json.dumps({"probe": f"{name}_{pattern}", **res[f"{name}_{pattern}"]}),
                   flush=True)
@@ -956,7 +963,7 @@ def main():
             "bound": "mfma", "achieved": round(w.flops / (c_step * 1e-3) / 1e12, 2),
             "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(w.flops / (c_step * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
-            "traffic": stored_traffic(case.name) if args.tile == 0 else None,
+            "traffic": stored_traffic(case.name, info.tile_id) if args.tile == 0 else None,
             "kernel": "consumer (persistent MFMA GEMM)", "kernel_ms": round(c_step, 5)},
         "overlap": overlap,
         "baseline_note": "vs_baseline divides by the PTO-ISA page's 8-card 8192x4096x4096 "

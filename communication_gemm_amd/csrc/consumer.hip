@@ -31,6 +31,8 @@
 // and read with the LDS transpose loads, which hand each lane consecutive k
 // of one column.  16-byte pieces are XOR-swizzled per row, the swizzle
 // applied by choosing which global piece each lane fetches.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "producer_body.hpp"
 #include "sync.hpp"
@@ -42,6 +44,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx16 __attribute__((ext_vector_type(16)));
 typedef int intx2 __attribute__((ext_vector_type(2)));
@@ -70,6 +73,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 struct F16 {
     static constexpr int kElt = 2;        // bytes per element
     static constexpr int kPair = 1;       // 16-byte pieces per MFMA operand
+    static constexpr int kBlk = 32;       // MFMA block: kBlk x kBlk outputs
+    static constexpr int kAccN = 16;      // accumulators per lane and block
     static constexpr bool kDequant = false;
     typedef floatx16 Acc;
     typedef float Out;                    // element of C
@@ -138,6 +143,8 @@ struct BF16 : F16 {
 struct I8 {
     static constexpr int kElt = 1;
     static constexpr int kPair = 1;
+    static constexpr int kBlk = 32;
+    static constexpr int kAccN = 16;
     static constexpr bool kDequant = true;   // + bias, x scale, -> fp16
     typedef intx16 Acc;
     typedef _Float16 Out;
@@ -208,6 +215,125 @@ struct FP8 : I8 {
     }
 };
 
+// 16 x 16 blocks (v_mfma_*_16x16x32 for 16-bit inputs, 16x16x64 for int8):
+// the same products in instructions that draw less power per flop than the
+// 32 x 32 ones -- with operands that toggle many bits the board's power
+// limit holds them at a higher clock (2.13 against 1.79 GHz in the
+// register-only probe, 19% more flops per second).  Lane l holds row
+// (column) l % 16 of a block and k = 8(l / 16) + 0..7 of a 32-element
+// group of K (16-bit; int8: 16(l / 16) + 0..15 of 64), so an operand is
+// still one 16-byte piece, and a step covers 64 bytes of K: lane group
+// l / 16 takes piece 4q + l / 16 of group q.  Accumulator r (0..3) of lane
+// l is row 4(l / 16) + r, column l % 16.  B is read with the same
+// transpose loads, lane group g taking rows 8g.. (16-bit; int8: 16g..) of
+// all 16 columns; the swizzle spreads the 16 pieces a half-wave reads (rows
+// k and k + 8 of it, int8: k and k + 16) over distinct banks, for rows of
+// 256 bytes or more.
+struct F16x {
+    static constexpr int kElt = 2;
+    static constexpr int kPair = 1;
+    static constexpr int kBlk = 16;
+    static constexpr int kAccN = 4;
+    static constexpr bool kDequant = false;
+    typedef floatx4 Acc;
+    typedef float Out;
+
+    __device__ static Acc zero() { Acc z; for (int i = 0; i < 4; ++i) z[i] = 0.f; return z; }
+
+    __device__ static Acc mma(const uint4 (&a)[1], const uint4 (&b)[1], const Acc& c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(half8, a[0]), __builtin_bit_cast(half8, b[0]), c, 0, 0, 0);
+    }
+
+    template <int LB>
+    __device__ static int swz_b(int k)
+    {
+        static_assert(LB >= 256, "16-column blocks read rows of 256 bytes or more");
+        return 2 * (k & 3) + 8 * ((k >> 3) & 1);
+    }
+
+    // lane group g = lane / 16 reads rows 8g + (lane % 16) / 4 (and 4 on),
+    // 4 columns each, so that lane i of the group receives column i
+    template <int LB>
+    __device__ static int b_offset(int lane, int n_base)
+    {
+        const int g = lane >> 4, jj = lane & 15;
+        const int n = n_base + 4 * (jj & 3);
+        const int k = 8 * g + (jj >> 2);
+        const int phys = (n >> 3) ^ (swz_b<LB>(k) & (LB / 16 - 1));
+        return k * LB + phys * 16 + (n & 7) * 2;
+    }
+
+    template <int LB>
+    __device__ static uint4 read_b(const char* p, int kk)
+    {
+        short4_ v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_PTR short4_*)(p + (32 * kk + 4 * h) * LB));
+        uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+};
+
+struct BF16x : F16x {
+    __device__ static Acc mma(const uint4 (&a)[1], const uint4 (&b)[1], const Acc& c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a[0]), __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+    }
+};
+
+struct I8x {
+    static constexpr int kElt = 1;
+    static constexpr int kPair = 1;
+    static constexpr int kBlk = 16;
+    static constexpr int kAccN = 4;
+    static constexpr bool kDequant = true;
+    typedef intx4 Acc;
+    typedef _Float16 Out;
+
+    __device__ static Acc zero() { Acc z; for (int i = 0; i < 4; ++i) z[i] = 0; return z; }
+
+    __device__ static Acc mma(const uint4 (&a)[1], const uint4 (&b)[1], const Acc& c)
+    {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            __builtin_bit_cast(intx4, a[0]), __builtin_bit_cast(intx4, b[0]), c, 0, 0, 0);
+    }
+
+    template <int LB>
+    __device__ static int swz_b(int k)
+    {
+        static_assert(LB >= 256, "16-column blocks read rows of 256 bytes or more");
+        return (k & 7) + 8 * ((k >> 4) & 1);
+    }
+
+    // lane group g reads rows 16g + (lane % 16) / 2 (and 8 on), 8 columns
+    // each, so that lane i of the group receives column i
+    template <int LB>
+    __device__ static int b_offset(int lane, int n_base)
+    {
+        const int g = lane >> 4, jj = lane & 15;
+        const int n = n_base + 8 * (jj & 1);
+        const int k = 16 * g + (jj >> 1);
+        const int phys = (n >> 4) ^ (swz_b<LB>(k) & (LB / 16 - 1));
+        return k * LB + phys * 16 + (n & 15);
+    }
+
+    template <int LB>
+    __device__ static uint4 read_b(const char* p, int kk)
+    {
+        intx2 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            v[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (LDS_PTR intx2*)(p + (64 * kk + 8 * h) * LB));
+        return make_uint4(v[0][0], v[0][1], v[1][0], v[1][1]);
+    }
+};
+
 // The lane index, hidden from the optimiser: addresses derived from it are
 // recomputed where they are used (a few VALU ops beside the MFMAs) instead
 // of being hoisted out of the K loop, where they would pin dozens of
@@ -271,12 +397,18 @@ template <class T, int BM, int BN, int SB, int NS, int WM, int WN>
 struct Engine {
     static constexpr int kWaves = WM * WN;          // WM x WN grid of waves
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kTM = BM / (32 * WM);      // 32x32 blocks per wave along M
-    static constexpr int kTN = BN / (32 * WN);      // ... along N
+    static constexpr int kBE = T::kBlk;             // MFMA block edge (32 or 16)
+    static constexpr int kTM = BM / (kBE * WM);     // blocks per wave along M
+    static constexpr int kTN = BN / (kBE * WN);     // ... along N
     static constexpr int kPieces = SB / 16;         // 16-byte pieces per A row
     static constexpr int kP = T::kPair;             // pieces per MFMA operand
-    static constexpr int kHalfSteps = SB / 32;      // 32-byte groups of K per slice
+    static constexpr int kLG = 64 / kBE;            // lane groups: pieces per K group
+    static constexpr int kHalfSteps = SB / (16 * kLG);  // K groups per slice
     static constexpr int kSteps = kHalfSteps / kP;  // MFMA steps per slice
+    // 16 x 16 blocks keep one operand set, each block re-read for the next
+    // step as soon as its last MFMA of this one is issued (two sets would
+    // not fit beside the accumulators); 32 x 32 blocks alternate two sets
+    static constexpr bool kRoll = kBE == 16;
     static constexpr int kBK = SB / T::kElt;        // k per slice
     static constexpr int kLB = BN * T::kElt;        // bytes per B row in LDS
     static constexpr int kABytes = BM * SB;         // A part of a stage
@@ -314,7 +446,7 @@ struct Engine {
     struct Lane {
         uint32_t a_ld[kAPer];   // A piece of load u: row * K + k, in bytes
         uint32_t b_ld[kBPer];   // B piece of load u: row * N + n, in bytes
-        uint32_t a_rd[kHalfSteps];  // A piece of 32-byte group g, block 0
+        uint32_t a_rd[kHalfSteps];  // A piece of K group g, block 0
         uint32_t b_rd[kTN];     // first transpose load of block j (step 0, half 0)
     };
 
@@ -339,13 +471,13 @@ struct Engine {
         }
 #pragma unroll
         for (int g = 0; g < kHalfSteps; ++g) {
-            const int r = wm + (lane & 31);
-            const int piece = 2 * g + (lane >> 5);
+            const int r = wm + (lane % kBE);
+            const int piece = kLG * g + lane / kBE;
             L.a_rd[g] = (uint32_t)(r * SB + ((piece ^ swz_a(r)) << 4));
         }
 #pragma unroll
         for (int j = 0; j < kTN; ++j)
-            L.b_rd[j] = (uint32_t)(kABytes + T::template b_offset<kLB>(lane, wn + j * 32));
+            L.b_rd[j] = (uint32_t)(kABytes + T::template b_offset<kLB>(lane, wn + j * kBE));
     }
 
     // Loads of one slice into `stage`.  Rows of A past the tile and rows of
@@ -419,7 +551,7 @@ struct Engine {
 #pragma unroll
             for (int i = 1; i < kTM; ++i)
                 f.a[i][q] = *reinterpret_cast<const uint4*>(st + L.a_rd[kP * kk + q] +
-                                                            i * 32 * SB);
+                                                            i * kBE * SB);
         }
     }
 
@@ -452,6 +584,29 @@ struct Engine {
         }
     }
 
+    // 16 x 16 blocks: the MFMAs of one step on the operands in f, column
+    // block by column block, each operand block of f re-read from step kk
+    // of `st` once its last MFMA here is issued: B block j after the column's
+    // kTM MFMAs (kTN (kTM - 1) + 1 MFMAs ahead of its next use), A block i
+    // after its MFMA in the last column (kTM - 1 MFMAs ahead).  A fence after
+    // each MFMA and its reads keeps that order.
+    __device__ __forceinline__ static void step_roll(Step& f, const char* st, const Lane& L,
+                                                     int kk, typename T::Acc (&acc)[kTM][kTN])
+    {
+        static_assert(kP == 1, "one piece per operand");
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                acc[i][j] = T::mma(f.a[i], f.b[j], acc[i][j]);
+                if (j == kTN - 1)
+                    f.a[i][0] = *reinterpret_cast<const uint4*>(st + L.a_rd[kk] + i * kBE * SB);
+                if (i == kTM - 1) f.b[j][0] = T::template read_b<kLB>(st + L.b_rd[j], kk);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
     // Wait until at most `behind` slices of this wave's loads are still in
     // flight (and every LDS read has returned).
     // `behind` is at most NS - 2.
@@ -478,6 +633,15 @@ struct Engine {
     {
         if (load) load_slice(ld, src, L, k_load);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kRoll) {
+            // f0 is the one operand set: step st - 1's MFMAs, step st's reads
+#pragma unroll
+            for (int st = 1; st < kSteps; ++st) step_roll(f0, cur, L, st, acc);
+            wait_slices(behind);
+            bare_barrier();
+            step_roll(f0, nxt, L, 0, acc);
+            return;
+        }
 #pragma unroll
         for (int st = 1; st < kSteps; ++st) {
             read_step(cur, L, st, (st & 1) ? f1 : f0);
@@ -535,7 +699,9 @@ struct Engine {
 
 // Epilogue.  Accumulator element r of lane l in a 32x32 block belongs to
 // row 8(r/4) + 4(l/32) + r%4 and column l%32, so each store instruction
-// writes two 32-column row segments.  The stores go through a buffer
+// writes two 32-column row segments; in a 16x16 block to row 4(l/16) + r
+// and column l%16 (pairs of blocks are regrouped to the same two-segment
+// stores, below).  The stores go through a buffer
 // descriptor that starts at the tile's first output row and ends after its
 // last valid row: rows past the shard fall out of range and are dropped,
 // columns past N get an out-of-range lane offset, so no store needs a
@@ -561,8 +727,9 @@ __device__ __forceinline__ uint32_t acc_read(int32_t x)
 template <class T, int BM, int BN, int WM, int WN, bool kKeepAcc>
 __device__ __forceinline__ void store_tile_as(
     const ConsumerArgs& a, int shard, int m, int n,
-    typename T::Acc (&acc)[BM / (32 * WM)][BN / (32 * WN)])
+    typename T::Acc (&acc)[BM / (T::kBlk * WM)][BN / (T::kBlk * WN)])
 {
+    constexpr int kE = T::kBlk;             // block edge
     typedef typename T::Out Out;
     const Schedule& s = a.s;
     const int lane = opaque_lane(), wave = threadIdx.x >> 6;
@@ -578,27 +745,86 @@ __device__ __forceinline__ void store_tile_as(
     const uint32_t row_acc = (uint32_t)s.N * 4u;
     if constexpr (kKeepAcc)
         racc = scalar_rsrc(a.acc_out + origin, (int64_t)rows * row_acc);
-    const uint32_t lrow = (uint32_t)(wm + 4 * (lane >> 5));
-    const int64_t col_lane = (int64_t)n * BN + wn + (lane & 31);
+    if constexpr (kE == 16) {
+        // 16 x 16 blocks, column blocks in pairs (2jp, 2jp + 1): one
+        // v_permlane16_swap per accumulator pair trades the pair's odd
+        // 16-lane rows for the other's even ones, after which lanes 0-31 of
+        // each result hold 32 consecutive columns of one output row (rows
+        // r and 8 + r of the block in the first result, 4 + r and 12 + r in
+        // the second), so every store writes two whole 128-byte row
+        // segments, as in the 32 x 32 blocks' epilogue.
+        constexpr int kTN = BN / (kE * WN);
+        static_assert(kTN % 2 == 0, "column blocks in pairs");
+        const uint32_t lrow = (uint32_t)(wm + 8 * (lane >> 5));
+        const int64_t col_lane = (int64_t)n * BN + wn + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < BN / (32 * WN); ++j) {
-        const bool in = col_lane + 32 * j < s.N;
-        const uint32_t c = (uint32_t)(wn + (lane & 31) + 32 * j);
+        for (int jp = 0; jp < kTN / 2; ++jp) {
+            const bool in = col_lane + 32 * jp < s.N;
+            const uint32_t c = (uint32_t)(wn + (lane & 31) + 32 * jp);
+            const uint32_t vo = in ? lrow * row_out + c * (uint32_t)sizeof(Out) : kOutOfRange;
+            const uint32_t vacc = in ? lrow * row_acc + c * 4u : kOutOfRange;
+            int32_t bias = 0;
+            float scale = 0.f;
+            if constexpr (T::kDequant) {
+                if (in) {
+                    bias = a.bias[col_lane + 32 * jp];
+                    scale = a.scale[col_lane + 32 * jp];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < BM / (kE * WM); ++i) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const auto x0 = acc[i][2 * jp][r], x1 = acc[i][2 * jp + 1][r];
+                    const auto sw = __builtin_amdgcn_permlane16_swap(
+                        __builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1),
+                        false, false);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t roff = (uint32_t)(i * 16 + 4 * h + r);
+                        const uint32_t bits = sw[h];
+                        if constexpr (!T::kDequant) {
+                            __builtin_amdgcn_raw_buffer_store_b32(bits, rc, vo + roff * row_out,
+                                                                  0, kStoreStream);
+                        } else {
+                            const uint32_t v = bits + (uint32_t)bias;
+                            if constexpr (kKeepAcc)
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    v, racc, vacc + roff * row_acc, 0, kStoreStream);
+                            const _Float16 hv = (_Float16)((float)(int32_t)v * scale);
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hv),
+                                                                  rc, vo + roff * row_out, 0,
+                                                                  kStoreStream);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        return;
+    }
+    const uint32_t lrow = (uint32_t)(wm + 4 * (lane / kE));
+    const int64_t col_lane = (int64_t)n * BN + wn + (lane % kE);
+#pragma unroll
+    for (int j = 0; j < BN / (kE * WN); ++j) {
+        const bool in = col_lane + kE * j < s.N;
+        const uint32_t c = (uint32_t)(wn + (lane % kE) + kE * j);
         const uint32_t vo = in ? lrow * row_out + c * (uint32_t)sizeof(Out) : kOutOfRange;
         const uint32_t vacc = in ? lrow * row_acc + c * 4u : kOutOfRange;
         int32_t bias = 0;
         float scale = 0.f;
         if constexpr (T::kDequant) {
             if (in) {
-                bias = a.bias[col_lane + 32 * j];
-                scale = a.scale[col_lane + 32 * j];
+                bias = a.bias[col_lane + kE * j];
+                scale = a.scale[col_lane + kE * j];
             }
         }
 #pragma unroll
-        for (int i = 0; i < BM / (32 * WM); ++i) {
+        for (int i = 0; i < BM / (kE * WM); ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint32_t roff = (uint32_t)(i * 32 + 8 * (r >> 2) + (r & 3));
+            for (int r = 0; r < T::kAccN; ++r) {
+                const uint32_t roff =
+                    (uint32_t)(i * kE + (kE == 32 ? 8 * (r >> 2) + (r & 3) : r));
                 if constexpr (!T::kDequant) {
                     // the element is copied out first: a bit cast applied
                     // to a vector element directly reads element 0
@@ -615,8 +841,8 @@ __device__ __forceinline__ void store_tile_as(
                                                           vo + roff * row_out, 0, kStoreStream);
                 }
             }
-            // one 32x32 block at a time: the scheduler would otherwise copy
-            // many blocks' accumulators into VGPRs ahead of their stores
+            // one block at a time: the scheduler would otherwise copy many
+            // blocks' accumulators into VGPRs ahead of their stores
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -625,7 +851,7 @@ __device__ __forceinline__ void store_tile_as(
 template <class T, int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void store_tile(
     const ConsumerArgs& a, int shard, int m, int n,
-    typename T::Acc (&acc)[BM / (32 * WM)][BN / (32 * WN)])
+    typename T::Acc (&acc)[BM / (T::kBlk * WM)][BN / (T::kBlk * WN)])
 {
     if constexpr (T::kDequant) {
         if (a.acc_out) {
@@ -690,17 +916,18 @@ __device__ __forceinline__ uint32_t poll_ready(const ConsumerArgs& a, int shard,
 // seen[shard], so a satisfied wait touches no memory.  Returns 0 after a
 // time-out or a failure elsewhere in the call.
 //
-// Only a workgroup's first such wait in a call needs the fence (the
-// caller passes acquire = false after it), unless the workspace is a ring
-// of stages reused within the call.  Every workspace address is written
-// once per call, every load of one is issued after its chunk's release was
-// seen, and each workgroup fences before its first such load; so after
-// that fence its CU's L1 and its XCD's L2 can take a line at a workspace
-// address only from a load that follows the line's release, which reads
-// the released data.  A stale line could only be an earlier call's, and
-// the earlier call's consumer ended before this one started.  (The fence
-// costs some microseconds, and it empties the L2 of the panels every other
-// workgroup of the XCD is sharing.)
+// Without a workspace ring a workgroup needs one such fence per call, and
+// the consumer takes it on entry, before any load (the caller passes
+// acquire = false); with a ring of stages reused within the call, every
+// wait fences.  Every workspace address is written once per call, every
+// load of one is issued after its chunk's release was seen, and each
+// workgroup fences before its first such load; so after that fence its
+// CU's L1 and its XCD's L2 can take a line at a workspace address only
+// from a load that follows the line's release, which reads the released
+// data.  A stale line could only be an earlier call's, and the earlier
+// call's consumer ended before this one started.  (The fence costs some
+// microseconds, and it empties the L2 of the panels every other workgroup
+// of the XCD is sharing: on entry there are none yet.)
 __device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int need,
                                            uint32_t* seen, int tid, bool acquire)
 {
@@ -765,6 +992,7 @@ template <class T, class E>
 __device__ bool split_reduce(const ConsumerArgs& a, const TileRef& t, int tid, int* last,
                              typename T::Acc (&acc)[E::kTM][E::kTN])
 {
+    static_assert(T::kBlk == 32, "split-K parts are built on 32 x 32 blocks");
     constexpr int R = E::kTM * E::kTN * 16;   // accumulators per thread
     constexpr int TH = E::kThreads;
     constexpr int kDevice = 16;               // device-scope cache policy
@@ -858,13 +1086,23 @@ __device__ __forceinline__ void consume(const ConsumerArgs& a, uint32_t block, u
         __hip_atomic_store(a.start + (block % a.start_copies) * (kStartStride / 4), a.epoch,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.trace_start && block == 0 && tid == 0) a.trace_start[0] = ticks();
+    // the call's one acquire fence without a workspace ring (see below);
+    // the barrier holds the other waves until it is done
+    if (!a.no_wait && s.ring == 0 && tid < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __syncthreads();
 
     const int64_t tiles = total_tiles(s);
     typename E::Lane L;
     E::lane_offsets(L, s.K, s.N);
-    // whether this workgroup has fenced in this call (wait_source)
-    bool acquired = false;
+    // Whether this workgroup has fenced in this call (wait_source).  Without
+    // a workspace ring one fence per call suffices, and it is taken here,
+    // before any load: it drops the lines an earlier call left at workspace
+    // addresses from this CU's L1 and this XCD's L2, and every later load
+    // of a workspace line follows that line's release.  Taken at the first
+    // remote tile instead, it came mid-call for the workgroups whose first
+    // tile is local, and each such fence emptied the L2 of the panels the
+    // XCD's other workgroups were sharing.
+    bool acquired = !a.no_wait && s.ring == 0;   // (fenced in the prologue)
 
     for (int64_t p = wg_position(s, block, blocks); p < tiles; p += blocks) {
         const TileRef t = tile_at(s, p);
@@ -1028,9 +1266,21 @@ template <> struct Cfg<13> { static constexpr int BM = 64, BN = 64, SB = 256, NS
 // 32 rows x 256 columns for decode-like shapes (split-K): B is read in rows
 // of 256 elements, one 32 x 64 block per wave, three slices in flight.
 template <> struct Cfg<14> { static constexpr int BM = 32, BN = 256, SB = 128, NS = 4, WM = 1, WN = 4; };
+// id 8's tile, pipeline and wave grid on 16 x 16 MFMA blocks (fp16, bf16,
+// int8): each wave owns 8 x 4 blocks of 16 x 16.
+template <> struct Cfg<15> { static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WM = 2, WN = 4; };
 
-template <class T, int ID>
+// The element traits a configuration is built with: the path's own (32 x 32
+// blocks), or its 16 x 16 form for id 15 (void: not built).
+template <class T, int ID> struct TraitsFor { typedef T type; };
+template <> struct TraitsFor<F16, 15> { typedef F16x type; };
+template <> struct TraitsFor<BF16, 15> { typedef BF16x type; };
+template <> struct TraitsFor<I8, 15> { typedef I8x type; };
+template <> struct TraitsFor<FP8, 15> { typedef void type; };
+
+template <class T0, int ID>
 struct Kern {
+    typedef typename TraitsFor<T0, ID>::type T;
     typedef Cfg<ID> C;
     typedef Engine<T, C::BM, C::BN, C::SB, C::NS, C::WM, C::WN> E;
     static const void* fn()
@@ -1088,14 +1338,21 @@ struct Kern {
 // and loop state -- times the waves per SIMD must leave 48 of the 512 for
 // a producer wave.  (The compiler's own count is checked by the tests;
 // this only keeps configurations that cannot fit from being built.)
-template <class T, int ID>
+template <class T0, int ID>
 constexpr bool supported()
 {
-    typedef Cfg<ID> C;
-    constexpr int tm = C::BM / (32 * C::WM), tn = C::BN / (32 * C::WN);
-    constexpr int regs = tm * tn * 16 + 2 * T::kPair * 4 * (tm + tn) + 40;
-    constexpr int per_simd = C::WM * C::WN / 4;
-    return C::SB % (64 * T::kPair) == 0 && per_simd * regs <= 512 - 48;
+    typedef typename TraitsFor<T0, ID>::type T;
+    if constexpr (std::is_void_v<T>) {
+        return false;
+    } else {
+        typedef Cfg<ID> C;
+        constexpr int tm = C::BM / (T::kBlk * C::WM), tn = C::BN / (T::kBlk * C::WN);
+        // operand fragments: two sets of 32 x 32 blocks, one of 16 x 16
+        constexpr int sets = T::kBlk == 16 ? 1 : 2;
+        constexpr int regs = tm * tn * T::kAccN + sets * T::kPair * 4 * (tm + tn) + 40;
+        constexpr int per_simd = C::WM * C::WN / 4;
+        return C::SB % (64 * T::kPair) == 0 && per_simd * regs <= 512 - 48;
+    }
 }
 
 template <class T, int ID>
@@ -1153,6 +1410,7 @@ hipError_t launch_kind(const ConsumerArgs& a, int tile_id, int wgs, hipStream_t 
     case 12: return launch_id<T, 12>(a, wgs, st);
     case 13: return launch_id<T, 13>(a, wgs, st);
     case 14: return launch_id<T, 14>(a, wgs, st);
+    case 15: return launch_id<T, 15>(a, wgs, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1202,6 +1460,7 @@ int occupancy_kind(int tile_id)
     case 12: return occupancy_id<T, 12>();
     case 13: return occupancy_id<T, 13>();
     case 14: return occupancy_id<T, 14>();
+    case 15: return occupancy_id<T, 15>();
     default: return 0;
     }
 }

@@ -31,7 +31,11 @@ constexpr int kAutoKBlocks = 4;
 // of the same size (at 2 x 1024 rows, K = N = 4096, id 11 ran 75 us
 // compute-only against 96 us for id 4).
 const TileShape kF16Shapes[] = {
-    {8, 256, 256, 512, true},
+    // 256 x 256 on 16 x 16 MFMA blocks: the same tile as id 8 at a higher
+    // clock under the board's power limit (8 x 1024 rows, K = N = 4096,
+    // compute-only: 226 against 240 us, fp16 and bf16 alike)
+    {15, 256, 256, 512, true},
+    {8, 256, 256, 512, false},
     {11, 128, 256, 512, true},
     {10, 256, 128, 512, true},
     {2, 128, 128, 256, true},
@@ -61,6 +65,10 @@ const TileShape kI8Shapes[] = {
     {11, 128, 256, 512, false},
     {12, 64, 64, 256, false},
     {14, 32, 256, 256, false},
+    // id 8 on 16 x 16 blocks: it holds a higher clock but moves the same
+    // operands, and the int8 slices are bound by that (2 x 8192 rows, K
+    // 27392: 1566 against 1569 us); id 8 stays first
+    {15, 256, 256, 512, false},
 };
 // fp8: the configurations whose slices hold whole 64-byte MFMA steps in
 // pairs (128- or 256-byte slices).  The 8-wave 256 x 256 tile is left out:

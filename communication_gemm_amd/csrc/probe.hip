@@ -15,7 +15,10 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChains = 8;   // independent accumulators per wave
 
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(512, 1) void mfma_probe(int64_t iters, uint32_t see
     floatx16 acc[kChains];
     for (int c = 0; c < kChains; ++c)
         for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
-    if constexpr (KIND == 0) {
+    if constexpr (KIND == 0 || KIND == 2) {
         half8 a[2], b[2];
         for (int v = 0; v < 2; ++v) {
             uint32_t wa[4], wb[4];
@@ -64,11 +67,63 @@ __global__ __launch_bounds__(512, 1) void mfma_probe(int64_t iters, uint32_t see
             a[v] = __builtin_bit_cast(half8, *reinterpret_cast<uint4*>(wa));
             b[v] = __builtin_bit_cast(half8, *reinterpret_cast<uint4*>(wb));
         }
-        for (int64_t i = 0; i < iters; ++i)
+        if constexpr (KIND == 0) {
+            for (int64_t i = 0; i < iters; ++i)
 #pragma unroll
+                for (int c = 0; c < kChains; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c & 1], b[(c >> 1) & 1],
+                                                                     acc[c], 0, 0, 0);
+        } else {
+            // two 16x16x32 instructions per chain and iteration: the same
+            // flops as one 32x32x16, on four-register accumulators
+            floatx4 acc4[2 * kChains];
+            for (int c = 0; c < 2 * kChains; ++c)
+                for (int e = 0; e < 4; ++e) acc4[c][e] = 0.f;
+            for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+                for (int c = 0; c < 2 * kChains; ++c)
+                    acc4[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c & 1], b[(c >> 1) & 1],
+                                                                      acc4[c], 0, 0, 0);
             for (int c = 0; c < kChains; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c & 1], b[(c >> 1) & 1],
-                                                                 acc[c], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) {
+                    acc[c][e] = acc4[2 * c][e];
+                    acc[c][4 + e] = acc4[2 * c + 1][e];
+                }
+        }
+    } else if constexpr (KIND == 3 || KIND == 4) {
+        // int8: random bytes, or 1 in every byte
+        intx4 a[2], b[2];
+        for (int v = 0; v < 2; ++v)
+            for (int w = 0; w < 4; ++w) {
+                a[v][w] = random ? (int)mix(seed ^ (tid * 16 + v * 8 + w)) : 0x01010101;
+                b[v][w] = random ? (int)mix(~seed ^ (tid * 16 + v * 8 + w + 4)) : 0x01010101;
+            }
+        if constexpr (KIND == 3) {
+            intx16 acc_i[kChains];
+            for (int c = 0; c < kChains; ++c)
+                for (int e = 0; e < 16; ++e) acc_i[c][e] = 0;
+            for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+                for (int c = 0; c < kChains; ++c)
+                    acc_i[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c & 1], b[(c >> 1) & 1],
+                                                                      acc_i[c], 0, 0, 0);
+            for (int c = 0; c < kChains; ++c)
+                for (int e = 0; e < 16; ++e) acc[c][e] = (float)acc_i[c][e];
+        } else {
+            intx4 acc_i[2 * kChains];
+            for (int c = 0; c < 2 * kChains; ++c)
+                for (int e = 0; e < 4; ++e) acc_i[c][e] = 0;
+            for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+                for (int c = 0; c < 2 * kChains; ++c)
+                    acc_i[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[c & 1], b[(c >> 1) & 1],
+                                                                      acc_i[c], 0, 0, 0);
+            for (int c = 0; c < kChains; ++c)
+                for (int e = 0; e < 4; ++e) {
+                    acc[c][e] = (float)acc_i[2 * c][e];
+                    acc[c][4 + e] = (float)acc_i[2 * c + 1][e];
+                }
+        }
     } else {
         intx8 a[2], b[2];
         for (int v = 0; v < 2; ++v)
@@ -211,15 +266,24 @@ extern "C" {
 // Launches the probe: `wgs` workgroups of 8 waves (two per SIMD, one
 // workgroup per CU), each wave issuing iters x 8 matrix instructions
 // (kind 0: fp16 32x32x16, 32768 flops each; kind 1: fp8 E4M3 32x32x64,
-// 131072 flops each).  out: wgs * 512 floats of device memory.  stream:
-// a hipStream_t (nullptr = the null stream).  Returns a hipError_t.
+// 131072 flops each) or iters x 16 (kind 2: fp16 16x16x32, 16384 flops
+// each; kind 3: int8 32x32x32, 65536 operations each; kind 4: int8
+// 16x16x64, two per chain and iteration, 32768 each).  out: wgs * 512
+// floats of device memory.  stream: a hipStream_t (nullptr = the null
+// stream).  Returns a hipError_t.
 int agg_probe_mfma(int kind, int random, int64_t iters, int wgs, uint32_t seed, float* out,
                    void* stream)
 {
-    if (kind < 0 || kind > 1 || iters < 0 || wgs < 1 || !out) return (int)hipErrorInvalidValue;
+    if (kind < 0 || kind > 4 || iters < 0 || wgs < 1 || !out) return (int)hipErrorInvalidValue;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (kind == 0)
         hipLaunchKernelGGL(mfma_probe<0>, dim3(wgs), dim3(512), 0, st, iters, seed, random, out);
+    else if (kind == 2)
+        hipLaunchKernelGGL(mfma_probe<2>, dim3(wgs), dim3(512), 0, st, iters, seed, random, out);
+    else if (kind == 3)
+        hipLaunchKernelGGL(mfma_probe<3>, dim3(wgs), dim3(512), 0, st, iters, seed, random, out);
+    else if (kind == 4)
+        hipLaunchKernelGGL(mfma_probe<4>, dim3(wgs), dim3(512), 0, st, iters, seed, random, out);
     else
         hipLaunchKernelGGL(mfma_probe<1>, dim3(wgs), dim3(512), 0, st, iters, seed, random, out);
     return (int)hipGetLastError();

@@ -31,6 +31,8 @@ def test_stored_traffic_only_for_current_sources_and_workload(tmp_path, monkeypa
     digest = bench.consumer_digest()
     monkeypatch.setattr(bench, "TRAFFIC_NOTE", _note(tmp_path, digest))
     assert bench.stored_traffic("w 1") == 123456.0
+    assert bench.stored_traffic("w 1", 8) == 123456.0
+    assert bench.stored_traffic("w 1", 15) is None      # counters of another kernel
     assert bench.stored_traffic("another workload") is None
     monkeypatch.setattr(bench, "TRAFFIC_NOTE", _note(tmp_path, "0" * 64))
     assert bench.stored_traffic("w 1") is None

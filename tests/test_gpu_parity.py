@@ -82,7 +82,7 @@ def test_large_cases_full(agg, orc, cid):
     print(c.name, "max err/S", check_f16(C, Co, So, c.name))
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 15])
 @pytest.mark.parametrize("n,S,K,N,cr", [
     (3, 100, 296, 168, 7),     # ragged rows, k tail, n tail, ragged last chunk
     (2, 300, 520, 264, 0),
@@ -195,7 +195,7 @@ def test_i8_small_full(agg, orc):
     check_i8(acc, D, ao, Do, "int8 small")
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 15])
 def test_i8_ragged(agg, orc, tile):
     shards, B, bias, scale = synth.make_i8(3 * 77, 16 * 37, 8 * 19, 3, 41000 + tile)
     acc, D = run_i8(agg, shards, B, bias, scale, 9, dict(tile=tile))
@@ -238,6 +238,24 @@ def test_i8_cases_stratified_rows(agg, orc, cid):
     assert freivalds_i8(acc, shards, B, bias) == c.M
 
 
+def test_block16_full_sizes(agg, orc):
+    """The 16 x 16-block form of the 256 x 256 tile (id 15) at full size:
+    C4 fp16, every element of C; C5 int8 on stratified rows, every
+    accumulator by projection."""
+    c = synth.CASES[4]
+    shards, B = synth.make_case(c)
+    C = run_f16(agg, shards, B, c.chunk_rows, agg.options(tile=15))
+    Co, So = orc.ag_gemm_f16(shards, B)
+    print(c.name, "tile 15 max err/S", check_f16(C, Co, So, c.name + " tile 15"))
+    c = synth.CASES[5]
+    shards, B, bias, scale = synth.make_case(c)
+    acc, D = run_i8(agg, shards, B, bias, scale, 0, dict(tile=15))
+    rows = stratified_rows(c.M, c.n_shards, agg.pick_chunk_rows(c.shard_rows), extra=6)
+    ao, Do = orc.ag_gemm_i8_dequant(shards, B, bias, scale, rows=rows)
+    check_i8(acc[rows], D[rows], ao, Do, c.name + " tile 15")
+    assert freivalds_i8(acc, shards, B, bias) == c.M
+
+
 def test_i8_small_m_full(agg, orc):
     """The decode-like shape: 64 gathered rows, so every shard is a
     single, partial m-tile and the grid is set by the n-tiles."""
@@ -272,7 +290,7 @@ def test_bf16_small_full(agg, orc):
     check_f16(C, Co, So, "bf16 small")
 
 
-@pytest.mark.parametrize("tile", [3, 8, 6, 11])
+@pytest.mark.parametrize("tile", [3, 8, 6, 11, 15])
 def test_bf16_ragged(agg, orc, tile):
     shards, B = synth.make_bf16(3 * 100, 296, 168, 3, "uniform", 35100 + tile)
     C = run_bf16(agg, shards, B, 7, agg.options(tile=tile))

@@ -228,8 +228,9 @@ def test_empty_problems_are_no_ops():
 
 
 @pytest.mark.parametrize("kind,n,S,K,N,tile", [
-    ("f16", 8, 1024, 4096, 4096, 8),     # 512 tiles of 256 x 256
-    ("f16", 4, 1024, 4096, 4096, 8),     # 256 of them: one per CU
+    ("f16", 8, 1024, 4096, 4096, 15),    # 512 tiles of 256 x 256 (16 x 16 blocks)
+    ("f16", 4, 1024, 4096, 4096, 15),    # 256 of them: one per CU
+    ("bf16", 8, 1024, 4096, 4096, 15),
     ("f16", 2, 1024, 4096, 4096, 11),    # 128 x 256, eight waves
     ("bf16", 2, 1024, 4096, 4096, 11),
     ("f16", 2, 1024, 2048, 1024, 13),    # 2 x 1024 rows, N = 1024: 64 x 64
@@ -288,7 +289,7 @@ def test_split_k_rejected(kw, status):
 def test_fp8_plans_only_tiles_built_for_it():
     """The fp8 path runs the configurations whose slices hold pairs of
     64-byte MFMA steps; the automatic choice stays among them."""
-    for tile in (1, 4, 5, 7, 8, 9):
+    for tile in (1, 4, 5, 7, 8, 9, 15):
         with pytest.raises(agg.AggError) as e:
             agg.plan("fp8", 8, 8192, 4096, 4096, 0, agg.options(tile=tile))
         assert e.value.status == agg.AGG_E_INVALID

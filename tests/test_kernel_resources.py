@@ -68,6 +68,10 @@ def shape_table():
     return tables
 
 
+# configurations built on 16 x 16 MFMA blocks, with the path's "x" traits
+BLOCK16_IDS = (15,)
+
+
 def consumer_report(cons, kind, bm, bn, sb, ns, wm, wn):
     key = (f"consumer_kernelINS0_{len(kind)}{kind}ELi{bm}ELi{bn}ELi{sb}ELi{ns}E"
            f"Li{wm}ELi{wn}EEEv")
@@ -86,9 +90,10 @@ def test_every_consumer_leaves_room_for_the_producer(reports):
     prod_lds = pk.get("LDS Size [bytes/block]", 0)
     assert pk.get("ScratchSize [bytes/lane]", 0) == 0
     table = shape_table()
-    assert len(table) == 50
+    assert len(table) == 53
     for (kind, i), (bm, bn, sb, ns, wm, wn) in table.items():
-        r = consumer_report(cons, kind, bm, bn, sb, ns, wm, wn)
+        r = consumer_report(cons, kind + ("x" if i in BLOCK16_IDS else ""),
+                            bm, bn, sb, ns, wm, wn)
         regs = align8(r["VGPRs"]) + align8(r["AGPRs"])
         per_simd = wm * wn // 4          # waves of one workgroup on each SIMD
         # consumer workgroups on a CU: bounded by registers and by the LDS
