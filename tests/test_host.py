@@ -151,7 +151,7 @@ def test_schedule_chunk_larger_than_tile():
     (dict(mode=9), agg.AGG_E_INVALID),
     (dict(link_model=3), agg.AGG_E_INVALID),
     (dict(link_gbps=-1.0), agg.AGG_E_INVALID),
-    (dict(tile=17), agg.AGG_E_INVALID),
+    (dict(tile=99), agg.AGG_E_INVALID),
     (dict(producer_piece_bytes=-8192), agg.AGG_E_INVALID),
     (dict(producer_piece_bytes=1000), agg.AGG_E_INVALID),      # not whole sweeps
     (dict(producer_piece_bytes=8192 + 16), agg.AGG_E_INVALID),
