@@ -75,6 +75,7 @@ struct F16 {
     static constexpr int kPair = 1;       // 16-byte pieces per MFMA operand
     static constexpr int kBlk = 32;       // MFMA block: kBlk x kBlk outputs
     static constexpr int kAccN = 16;      // accumulators per lane and block
+    static constexpr bool kRoll = false;  // one rolling operand set (see Engine)
     static constexpr bool kDequant = false;
     typedef floatx16 Acc;
     typedef float Out;                    // element of C
@@ -145,6 +146,7 @@ struct I8 {
     static constexpr int kPair = 1;
     static constexpr int kBlk = 32;
     static constexpr int kAccN = 16;
+    static constexpr bool kRoll = false;
     static constexpr bool kDequant = true;   // + bias, x scale, -> fp16
     typedef intx16 Acc;
     typedef _Float16 Out;
@@ -215,6 +217,13 @@ struct FP8 : I8 {
     }
 };
 
+// fp8 on the eight-wave 256 x 256 tile: the same 32 x 32 blocks, with one
+// rolling operand set (two sets of 32-byte operands would not fit beside
+// the 128 accumulators of a 128 x 64 wave block and a producer wave).
+struct FP8x : FP8 {
+    static constexpr bool kRoll = true;
+};
+
 // 16 x 16 blocks (v_mfma_*_16x16x32 for 16-bit inputs, 16x16x64 for int8):
 // the same products in instructions that draw less power per flop than the
 // 32 x 32 ones -- with operands that toggle many bits the board's power
@@ -234,6 +243,7 @@ struct F16x {
     static constexpr int kPair = 1;
     static constexpr int kBlk = 16;
     static constexpr int kAccN = 4;
+    static constexpr bool kRoll = true;
     static constexpr bool kDequant = false;
     typedef floatx4 Acc;
     typedef float Out;
@@ -291,6 +301,7 @@ struct I8x {
     static constexpr int kPair = 1;
     static constexpr int kBlk = 16;
     static constexpr int kAccN = 4;
+    static constexpr bool kRoll = true;
     static constexpr bool kDequant = true;
     typedef intx4 Acc;
     typedef _Float16 Out;
@@ -405,10 +416,12 @@ struct Engine {
     static constexpr int kLG = 64 / kBE;            // lane groups: pieces per K group
     static constexpr int kHalfSteps = SB / (16 * kLG);  // K groups per slice
     static constexpr int kSteps = kHalfSteps / kP;  // MFMA steps per slice
-    // 16 x 16 blocks keep one operand set, each block re-read for the next
-    // step as soon as its last MFMA of this one is issued (two sets would
-    // not fit beside the accumulators); 32 x 32 blocks alternate two sets
-    static constexpr bool kRoll = kBE == 16;
+    // The eight-wave 256 x 256 tile on 16 x 16 blocks (and fp8's 32-byte
+    // operands on 32 x 32 blocks) keeps one operand set, each block re-read
+    // for the next step as soon as its last MFMA of this one is issued (two
+    // sets would not fit beside the accumulators); the other configurations
+    // alternate two sets
+    static constexpr bool kRoll = T::kRoll;
     static constexpr int kBK = SB / T::kElt;        // k per slice
     static constexpr int kLB = BN * T::kElt;        // bytes per B row in LDS
     static constexpr int kABytes = BM * SB;         // A part of a stage
@@ -584,7 +597,7 @@ struct Engine {
         }
     }
 
-    // 16 x 16 blocks: the MFMAs of one step on the operands in f, column
+    // One operand set: the MFMAs of one step on the operands in f, column
     // block by column block, each operand block of f re-read from step kk
     // of `st` once its last MFMA here is issued: B block j after the column's
     // kTM MFMAs (kTN (kTM - 1) + 1 MFMAs ahead of its next use), A block i
@@ -593,15 +606,19 @@ struct Engine {
     __device__ __forceinline__ static void step_roll(Step& f, const char* st, const Lane& L,
                                                      int kk, typename T::Acc (&acc)[kTM][kTN])
     {
-        static_assert(kP == 1, "one piece per operand");
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
 #pragma unroll
             for (int i = 0; i < kTM; ++i) {
                 acc[i][j] = T::mma(f.a[i], f.b[j], acc[i][j]);
-                if (j == kTN - 1)
-                    f.a[i][0] = *reinterpret_cast<const uint4*>(st + L.a_rd[kk] + i * kBE * SB);
-                if (i == kTM - 1) f.b[j][0] = T::template read_b<kLB>(st + L.b_rd[j], kk);
+#pragma unroll
+                for (int q = 0; q < kP; ++q) {
+                    if (j == kTN - 1)
+                        f.a[i][q] = *reinterpret_cast<const uint4*>(
+                            st + L.a_rd[kP * kk + q] + i * kBE * SB);
+                    if (i == kTM - 1)
+                        f.b[j][q] = T::template read_b<kLB>(st + L.b_rd[j], kP * kk + q);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -1270,13 +1287,14 @@ template <> struct Cfg<14> { static constexpr int BM = 32, BN = 256, SB = 128, N
 // int8): each wave owns 8 x 4 blocks of 16 x 16.
 template <> struct Cfg<15> { static constexpr int BM = 256, BN = 256, SB = 128, NS = 2, WM = 2, WN = 4; };
 
-// The element traits a configuration is built with: the path's own (32 x 32
-// blocks), or its 16 x 16 form for id 15 (void: not built).
+// The element traits a configuration is built with: the path's own (two
+// operand sets), or for id 15 its one-set form -- on 16 x 16 blocks for
+// fp16, bf16 and int8, on 32 x 32 blocks for fp8.
 template <class T, int ID> struct TraitsFor { typedef T type; };
 template <> struct TraitsFor<F16, 15> { typedef F16x type; };
 template <> struct TraitsFor<BF16, 15> { typedef BF16x type; };
 template <> struct TraitsFor<I8, 15> { typedef I8x type; };
-template <> struct TraitsFor<FP8, 15> { typedef void type; };
+template <> struct TraitsFor<FP8, 15> { typedef FP8x type; };
 
 template <class T0, int ID>
 struct Kern {
@@ -1347,8 +1365,8 @@ constexpr bool supported()
     } else {
         typedef Cfg<ID> C;
         constexpr int tm = C::BM / (T::kBlk * C::WM), tn = C::BN / (T::kBlk * C::WN);
-        // operand fragments: two sets of 32 x 32 blocks, one of 16 x 16
-        constexpr int sets = T::kBlk == 16 ? 1 : 2;
+        // operand fragments: two sets, or one rolling set
+        constexpr int sets = T::kRoll ? 1 : 2;
         constexpr int regs = tm * tn * T::kAccN + sets * T::kPair * 4 * (tm + tn) + 40;
         constexpr int per_simd = C::WM * C::WN / 4;
         return C::SB % (64 * T::kPair) == 0 && per_simd * regs <= 512 - 48;

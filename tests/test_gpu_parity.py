@@ -312,7 +312,7 @@ def test_bf16_large_full(agg, orc):
 # of 2^-24 sum|ab| per instruction, far inside the bound (the largest
 # ratio err / sum|ab| is printed).
 
-FP8_TILES = [2, 3, 6, 10, 11, 12, 13]
+FP8_TILES = [2, 3, 6, 10, 11, 12, 13, 15]
 
 
 def run_fp8(agg, shards, B, chunk_rows=0, opts=None, as_float8=False):
@@ -350,12 +350,17 @@ def test_fp8_rejects_unbuilt_tile(agg):
         run_fp8(agg, shards, B, 0, agg.options(tile=8))
 
 
-def test_fp8_large_full(agg, orc):
+@pytest.mark.parametrize("tile", [0, 6, 15])
+def test_fp8_large_full(agg, orc, tile):
+    """The 8 x 1024-row, K = N = 4096 fp8 call in full, with the automatic
+    tile and with both 256 x 256 tiles (four waves, and eight waves on one
+    rolling operand set)."""
     n, S, K, N = 8, 1024, 4096, 4096
     shards, B = synth.make_fp8(n * S, K, N, n, "normal", 36200)
-    C = run_fp8(agg, shards, B)
+    C = run_fp8(agg, shards, B, 0, agg.options(tile=tile))
     Co, So = orc.ag_gemm_fp8(shards, B)
-    print("fp8 8x1024x4096x4096: max err/S", check_f16(C, Co, So, "fp8 large"))
+    print(f"fp8 8x1024x4096x4096 tile {tile}: max err/S",
+          check_f16(C, Co, So, f"fp8 large tile {tile}"))
 
 
 # ---------------------------------------------------------------- K-blocks
