@@ -479,8 +479,13 @@ class F16Workload:
         return 2.0 * self.case.M * self.case.K * self.case.N
 
     def plan(self):
+        """The plan of the workload's pipelined calls (the same options)."""
         info, _, _ = self.agg.plan("f16", self.case.n_shards, self.case.M, self.case.K,
-                                   self.case.N, self.cr, self.agg.options(tile=self.tile))
+                                   self.case.N, self.cr,
+                                   self.agg.options(tile=self.tile, link_gbps=self.gbps,
+                                                    mode=MODES["pipelined"]),
+                                   num_cus=self.torch.cuda.get_device_properties(
+                                       self.torch.cuda.current_device()).multi_processor_count)
         return info
 
     def entry(self, steps, warmup=10, trace=False, timed_steps=None):

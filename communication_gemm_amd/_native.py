@@ -230,10 +230,25 @@ def options(**kw) -> Options:
             setattr(o, k, v.data_ptr() if hasattr(v, "data_ptr") else int(v))
             if k == "workspace" and hasattr(v, "numel"):
                 o.workspace_bytes = v.numel() * v.element_size()
+            if k == "trace" and hasattr(v, "numel"):
+                o._trace_words = v.numel() * v.element_size() // 8
         else:
             setattr(o, k, v)
     o._keep = keep   # keep ctypes arrays alive with the struct
     return o
+
+
+def _check_trace(kind, n_shards, M, K, N, chunk_rows, opts):
+    """A trace tensor must hold the call's plan's trace_words: the library
+    takes a bare pointer and writes that many words."""
+    words = getattr(opts, "_trace_words", None) if opts is not None else None
+    if words is None:
+        return
+    import torch
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    need = plan(kind, n_shards, M, K, N, chunk_rows, opts, num_cus=cus)[0].trace_words
+    if words < need:
+        raise ValueError(f"trace holds {words} words; this call's plan needs {need}")
 
 
 def _stream_handle(stream):
@@ -297,6 +312,7 @@ def ag_gemm_f16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | 
     table, S = _shard_ptrs(shards, torch.float16, K)
     M = S * len(shards)
     _check_out(C, (M, N), torch.float32)
+    _check_trace("f16", len(shards), M, K, N, int(chunk_rows), opts)
     st = _stream_handle(stream)
     r = _invoke(lib.ag_gemm_f16, lib.ag_gemm_f16_ex,
                 (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st),
@@ -318,6 +334,7 @@ def ag_gemm_f16_noalloc(shards, B, C, chunk_rows: int = 0, stream=None,
     table, S = _shard_ptrs(shards, torch.float16, K)
     M = S * len(shards)
     _check_out(C, (M, N), torch.float32)
+    _check_trace("f16", len(shards), M, K, N, int(chunk_rows), opts)
     st = _stream_handle(stream)
     args = (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st,
             ctypes.byref(opts) if opts is not None else None)
@@ -338,6 +355,7 @@ def ag_gemm_bf16(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options |
     table, S = _shard_ptrs(shards, torch.bfloat16, K)
     M = S * len(shards)
     _check_out(C, (M, N), torch.float32)
+    _check_trace("bf16", len(shards), M, K, N, int(chunk_rows), opts)
     st = _stream_handle(stream)
     r = _invoke(lib.ag_gemm_bf16, lib.ag_gemm_bf16_ex,
                 (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st),
@@ -365,6 +383,7 @@ def ag_gemm_fp8(shards, B, C, chunk_rows: int = 0, stream=None, opts: Options | 
     table, S = _shard_ptrs(shards, dt, K)
     M = S * len(shards)
     _check_out(C, (M, N), torch.float32)
+    _check_trace("fp8", len(shards), M, K, N, int(chunk_rows), opts)
     st = _stream_handle(stream)
     r = _invoke(lib.ag_gemm_fp8, lib.ag_gemm_fp8_ex,
                 (table, len(shards), B.data_ptr(), C.data_ptr(), M, K, N, int(chunk_rows), st),
@@ -385,6 +404,7 @@ def ag_gemm_i8_dequant(shards, B, bias, scale, C, chunk_rows: int = 0, stream=No
     _check_vec(bias, N, torch.int32, "bias")
     _check_vec(scale, N, torch.float32, "scale")
     _check_out(C, (M, N), torch.float16)
+    _check_trace("i8", len(shards), M, K, N, int(chunk_rows), opts)
     st = _stream_handle(stream)
     r = _invoke(lib.ag_gemm_i8_dequant, lib.ag_gemm_i8_dequant_ex,
                 (table, len(shards), B.data_ptr(), bias.data_ptr(), scale.data_ptr(),

@@ -11,6 +11,7 @@ namespace {
 
 // K-blocks of the automatic 2-D chunks.
 constexpr int kAutoKBlocks = 4;
+constexpr int kAutoKBlocksPaced = 8;
 
 // Output tiles the consumer kernels are instantiated for, largest first.
 // Ids 1, 6, 7, 8 and 9 are the same 256 x 256 tile with different K
@@ -294,14 +295,23 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         s.nkb = (int)(K / s.kbk);           // the last K-block takes the rest
     } else if (opt->k_block == 0 && chunk_rows == 0 && two_d_ok && K % (kAutoKBlocks * kib) == 0 &&
                n_shards > 1 && S > 0) {
+        // Paced links and three or more remote sources (below): eight
+        // K-blocks where K allows, so that a remote tile's first K-block of
+        // its rows crosses the link in half the time.  (With one remote
+        // source, 2 x 1024 rows at K = N = 4096 paced at 153 GB/s, four
+        // K-blocks on every CU stayed ahead: 89.3-89.9 against 91.7 us.)
+        const bool paced =
+            opt->link_gbps > 0.0 && opt->mode == AGG_MODE_PIPELINED && n_shards >= 4;
+        const int nkb = paced && K % (kAutoKBlocksPaced * kib) == 0 ? kAutoKBlocksPaced
+                                                                     : kAutoKBlocks;
         // Automatic chunks where K-blocks are allowed: S/16 rows x a quarter
         // of K, still 64 chunks per source (the PTO-ISA README's 64-128).
         // Measured against whole-K chunks of S/64 rows (interleaved, one
         // box): 147 against 176 us on 4 x 1024 rows at K = N = 4096 paced at
         // 153 GB/s per link, level (277 / 279 us, 40 / 39 us) on 8 x 1024
         // rows at K = N = 4096 and on 2 x 1024 rows at K = 2048, N = 1024.
-        s.kbk = K / kAutoKBlocks;
-        s.nkb = kAutoKBlocks;
+        s.kbk = K / nkb;
+        s.nkb = nkb;
         s.cr = (int)(S / 16 > 0 ? S / 16 : 1);
     }
     s.rcs = S > 0 ? (int)cdiv(S, s.cr) : 0;
@@ -368,11 +378,22 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
     // the first chunk lands no later (about 12 us after the consumer starts
     // either way) and the small shapes did not change.  A paced producer
     // keeps every CU: a wave waiting for its chunk's paced time holds back
-    // its next pieces, and fewer waves fell behind the pace.
+    // its next pieces, and fewer waves fell behind the pace -- except with
+    // the automatic paced chunks of eight K-blocks, where a quarter of the
+    // CUs still keep up with the pace (the last chunk of 4 x 1024 rows at
+    // K = N = 4096, 153 GB/s per link, lands at 61 us against 55 by the
+    // pace) and take less from the consumer: 124.1-126.9 us pipelined
+    // against 128.5-134.4 with four K-blocks on every CU (three boxes);
+    // eight K-blocks on every CU took 136.1-138.1 us, and on 8 x 1024 rows
+    // the quarter grid changed nothing (239-240 us, mesh or ring).
     int pw = opt->producer_wgs ? opt->producer_wgs : producer_cus;
-    if (!opt->producer_wgs && opt->mode == AGG_MODE_PIPELINED && !(opt->link_gbps > 0.0) &&
-        !opt->producer_cus && opt->producer != AGG_PRODUCER_SDMA && num_cus >= 2)
-        pw = num_cus / 2;
+    if (!opt->producer_wgs && opt->mode == AGG_MODE_PIPELINED && !opt->producer_cus &&
+        opt->producer != AGG_PRODUCER_SDMA && num_cus >= 4) {
+        if (!(opt->link_gbps > 0.0))
+            pw = num_cus / 2;
+        else if (s.nkb == kAutoKBlocksPaced && opt->k_block == 0 && chunk_rows == 0)
+            pw = num_cus / 4;
+    }
     if (pw > items) pw = (int)(items > 0 ? items : 1);
     if (pw < 1) pw = 1;
     // One launch for both (pipelined): by default when the consumer's tile
@@ -390,6 +411,17 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         const int pw_fused = opt->producer_wgs ? pw : (pw + 7) / 8 * 8;
         fused = can && (opt->producer == AGG_PRODUCER_FUSED || cw + pw_fused <= num_cus);
         if (fused) pw = pw_fused;
+        // The separate producer kernel on every CU waits for the consumer's
+        // start word, and a consumer workgroup needs all but one producer
+        // wave's registers of each SIMD: more producer workgroups than CUs
+        // could take every CU's room before any consumer workgroup starts
+        // (the producers would then wait out their start bound), or leave
+        // producer workgroups, and the chunks they copy, queued behind a
+        // consumer grid that waits for those chunks.  One producer
+        // workgroup per CU at most: workgroups are dealt to the XCDs in
+        // turn, so no XCD gets more of them than it has CUs, and each
+        // XCD keeps room for consumer workgroups to start.
+        if (!fused && !opt->producer_cus && pw > num_cus) return AGG_E_UNSUPPORTED;
     }
     p.consumer_wgs = cw;
     p.producer_wgs = pw;

@@ -148,7 +148,10 @@ typedef struct agg_options {
     int mode;               /* enum agg_mode (default PIPELINED)              */
     double link_gbps;       /* per-link pacing in GB/s (1e9 B/s); 0 = none    */
     int link_model;         /* enum agg_link_model (default PARALLEL)         */
-    int producer_wgs;       /* producer workgroups; 0 = automatic            */
+    int producer_wgs;       /* producer workgroups; 0 = automatic; a
+                               pipelined call with the producer kernel on
+                               every CU (no producer_cus, not fused) takes at
+                               most one per CU (AGG_E_UNSUPPORTED above)      */
     int consumer_wgs;       /* consumer workgroups; 0 = automatic; at most
                                as many as can be resident at once are used */
     int tile;               /* consumer tile shape id; 0 = automatic          */

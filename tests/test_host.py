@@ -453,12 +453,18 @@ def test_k_block_chunk_cap_and_split_k():
     ("f16", 8, 8192, 4096, 4096, {"workspace_stages": 2}, 16, 1),
     ("f16", 8, 8192, 4096, 4096, {"scheme": 1}, 16, 1),
     ("f16", 8, 8192, 4096, 4096, {"k_block": 4096}, 16, 1),   # explicitly whole K
+    ("f16", 4, 4096, 4096, 4096, {"link_gbps": 153.0}, 64, 8),  # paced: K/8
+    ("f16", 4, 4096, 4096, 4096, {"link_gbps": 153.0, "link_model": 1}, 64, 8),
+    ("f16", 2, 2048, 4096, 4096, {"link_gbps": 153.0}, 64, 4),  # one remote source
+    ("f16", 4, 4096, 2048, 1024, {"link_gbps": 153.0}, 64, 4),  # K/8 not whole KiB
+    ("f16", 4, 4096, 6144, 4096, {"link_gbps": 153.0}, 64, 4),
+    ("f16", 4, 4096, 4096, 4096, {"link_gbps": 153.0, "mode": 2}, 64, 4),  # sequential
 ])
 def test_automatic_chunks(kind, n, M, K, N, opts, cr, nkb):
     info, _, _ = agg.plan(kind, n, M, K, N, 0, agg.options(**opts))
     assert (info.chunk_rows, info.k_blocks) == (cr, nkb)
     if nkb > 1:
-        assert info.chunks_per_source == 64 and info.k_block == K // 4
+        assert info.chunks_per_source == 16 * nkb and info.k_block == K // nkb
     # an explicit chunk size keeps whole-K chunks
     info, _, _ = agg.plan(kind, n, M, K, N, 8, agg.options(**{k: v for k, v in opts.items()
                                                                if k != "k_block"}))
@@ -548,10 +554,36 @@ def test_automatic_producer_grid():
     # sequential calls, and an explicit grid: as asked or every CU
     shape = ("f16", 8, 8192, 4096, 4096, 0)
     assert agg.plan(*shape, agg.options())[0].producer_wgs == 128
-    assert agg.plan(*shape, agg.options(link_gbps=153.0))[0].producer_wgs == 256
+    # paced with the automatic eight K-blocks: a quarter of the CUs; paced
+    # with other chunks: every CU
+    assert agg.plan(*shape, agg.options(link_gbps=153.0))[0].producer_wgs == 64
+    assert agg.plan(*shape[:5], 64, agg.options(link_gbps=153.0))[0].producer_wgs == 256
+    assert agg.plan(*shape, agg.options(link_gbps=153.0, k_block=512))[0].producer_wgs == 256
     assert agg.plan(*shape, agg.options(mode=agg.MODE_COPY_ONLY))[0].producer_wgs == 256
     assert agg.plan(*shape, agg.options(mode=agg.MODE_SEQUENTIAL))[0].producer_wgs == 256
     assert agg.plan(*shape, agg.options(producer_wgs=200))[0].producer_wgs == 200
     assert agg.plan(*shape, agg.options(), num_cus=80)[0].producer_wgs == 40
     # never more workgroups than pieces: 2 x 128 rows, K 256 has 8
     assert agg.plan("f16", 2, 256, 256, 128, 32, agg.options())[0].producer_wgs == 8
+
+
+def test_producer_grid_leaves_room_for_the_consumer():
+    """A pipelined call whose separate producer kernel shares every CU with
+    the consumer takes at most one producer workgroup per CU: more could
+    fill the CUs before any consumer workgroup starts, and the producer
+    waits for the consumer's start.  Copy-only and sequential calls, the
+    fused launch and a producer on CUs of its own have no such limit."""
+    shape = ("f16", 8, 8192, 4096, 4096, 0)
+    for kw in (dict(producer_wgs=257), dict(producer_wgs=512, link_gbps=153.0)):
+        with pytest.raises(agg.AggError) as e:
+            agg.plan(*shape, agg.options(**kw))
+        assert e.value.status == agg.AGG_E_UNSUPPORTED, kw
+    with pytest.raises(agg.AggError):
+        agg.plan(*shape, agg.options(producer_wgs=81), num_cus=80)
+    assert agg.plan(*shape, agg.options(producer_wgs=256))[0].producer_wgs == 256
+    for kw in (dict(mode=agg.MODE_COPY_ONLY), dict(mode=agg.MODE_SEQUENTIAL),
+               dict(producer_cus=32)):
+        assert agg.plan(*shape, agg.options(producer_wgs=512, **kw))[0].producer_wgs == 512
+    small = ("f16", 2, 256, 256, 128, 32)
+    info = agg.plan(*small, agg.options(producer=3, producer_wgs=8, tile=13))[0]
+    assert info.producer_fused == 1
