@@ -295,15 +295,19 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         s.nkb = (int)(K / s.kbk);           // the last K-block takes the rest
     } else if (opt->k_block == 0 && chunk_rows == 0 && two_d_ok && K % (kAutoKBlocks * kib) == 0 &&
                n_shards > 1 && S > 0) {
-        // Paced links and three or more remote sources (below): eight
-        // K-blocks where K allows, so that a remote tile's first K-block of
-        // its rows crosses the link in half the time.  (With one remote
-        // source, 2 x 1024 rows at K = N = 4096 paced at 153 GB/s, four
-        // K-blocks on every CU stayed ahead: 89.3-89.9 against 91.7 us.)
-        const bool paced =
-            opt->link_gbps > 0.0 && opt->mode == AGG_MODE_PIPELINED && n_shards >= 4;
-        const int nkb = paced && K % (kAutoKBlocksPaced * kib) == 0 ? kAutoKBlocksPaced
-                                                                     : kAutoKBlocks;
+        // Pipelined calls with three or more remote sources: eight K-blocks
+        // where K allows.  A remote tile's first K-block of its rows is then
+        // half the bytes, and a chunk of it (S/16 rows) half the sweeps of
+        // a producer wave, so it lands sooner, paced or not: 8 x 1024 rows
+        // at K = N = 4096 ran 239.7 against 243.0 us and 235.8 against
+        // 238.0 (two boxes; 8 KiB or 16 KiB pieces alike, 128-row chunks
+        // 240.8), and paced at 153 GB/s per link the 4 x 1024 rows below.
+        // (With one remote source, 2 x 1024 rows at K = N = 4096 paced at
+        // 153 GB/s, four K-blocks on every CU stayed ahead: 89.3-89.9
+        // against 91.7 us.)
+        const bool eight = opt->mode == AGG_MODE_PIPELINED && n_shards >= 4 &&
+                           K % (kAutoKBlocksPaced * kib) == 0;
+        const int nkb = eight ? kAutoKBlocksPaced : kAutoKBlocks;
         // Automatic chunks where K-blocks are allowed: S/16 rows x a quarter
         // of K, still 64 chunks per source (the PTO-ISA README's 64-128).
         // Measured against whole-K chunks of S/64 rows (interleaved, one

@@ -107,25 +107,26 @@ def test_trace_k_blocks_gate_every_block(agg):
 def test_trace_buffer_must_hold_the_calls_plan(agg):
     """The library writes the plan's trace_words through a bare pointer, so
     the binding refuses a trace tensor that is too small for the call it is
-    given to -- here a paced call whose automatic plan (eight K-blocks) has
-    more chunks than the same shape's unpaced one -- before anything runs;
-    with the paced plan's size the trace is whole."""
+    given to -- here one sized for whole-K chunks while the call's automatic
+    plan cuts K into eight blocks -- before anything runs; with the call's
+    own plan's size the trace is whole."""
     n, S, K, N = 4, 1024, 4096, 512
     M = n * S
     shards, B = synth.make_f16(M, K, N, n, "normal", 60020)
     ts = [dev(s, torch) for s in shards]
     tB = dev(B, torch)
-    paced = agg.plan("f16", n, M, K, N, 0, agg.options(link_gbps=153.0))[0]
-    plain = agg.plan("f16", n, M, K, N, 0)[0]
-    assert paced.k_blocks == 8 and plain.k_blocks == 4
-    assert paced.trace_words > plain.trace_words
+    auto = agg.plan("f16", n, M, K, N, 0, agg.options(link_gbps=153.0))[0]
+    whole = agg.plan("f16", n, M, K, N, 64, agg.options(link_gbps=153.0))[0]
+    assert auto.k_blocks == 8 and whole.k_blocks == 1
+    assert auto.trace_words > whole.trace_words
     C = torch.full((M, N), float("nan"), device="cuda")
-    small = torch.zeros(plain.trace_words, dtype=torch.int64, device="cuda")
-    with pytest.raises(ValueError):
-        agg.ag_gemm_f16(ts, tB, C, 0, opts=agg.options(trace=small, link_gbps=153.0))
+    for words in (whole.trace_words, auto.trace_words - 1):
+        small = torch.zeros(words, dtype=torch.int64, device="cuda")
+        with pytest.raises(ValueError):
+            agg.ag_gemm_f16(ts, tB, C, 0, opts=agg.options(trace=small, link_gbps=153.0))
     assert torch.isnan(C).all()                  # nothing ran
-    trace = torch.zeros(paced.trace_words + 1, dtype=torch.int64, device="cuda")
+    trace = torch.zeros(auto.trace_words + 1, dtype=torch.int64, device="cuda")
     agg.ag_gemm_f16(ts, tB, C, 0, opts=agg.options(trace=trace, link_gbps=153.0))
     assert agg.check() == 0
     tr = trace.cpu().numpy()
-    assert (tr[:paced.trace_words] > 0).all() and tr[paced.trace_words] == 0
+    assert (tr[:auto.trace_words] > 0).all() and tr[auto.trace_words] == 0

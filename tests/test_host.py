@@ -443,11 +443,12 @@ def test_k_block_chunk_cap_and_split_k():
 
 
 @pytest.mark.parametrize("kind,n,M,K,N,opts,cr,nkb", [
-    ("f16", 8, 8192, 4096, 4096, {}, 64, 4),          # S/16 rows x K/4
-    ("f16", 4, 4096, 4096, 4096, {}, 64, 4),
-    ("f16", 2, 2048, 2048, 1024, {}, 64, 4),
-    ("bf16", 8, 8192, 4096, 4096, {}, 64, 4),
-    ("fp8", 8, 8192, 4096, 4096, {}, 64, 4),          # int8/fp8: K/4 whole KiB
+    ("f16", 8, 8192, 4096, 4096, {}, 64, 8),          # 3+ remote sources: S/16 rows x K/8
+    ("f16", 4, 4096, 4096, 4096, {}, 64, 8),
+    ("f16", 2, 2048, 2048, 1024, {}, 64, 4),          # S/16 rows x K/4
+    ("f16", 8, 8192, 4096, 4096, {"mode": 2}, 64, 4),  # sequential: K/4
+    ("bf16", 8, 8192, 4096, 4096, {}, 64, 8),
+    ("fp8", 8, 8192, 4096, 4096, {}, 64, 4),          # int8/fp8: K/8 not whole KiB
     ("i8", 2, 16384, 27392, 4096, {}, 128, 1),        # K not a multiple of 4 KiB
     ("f16", 2, 256, 256, 128, {}, 2, 1),              # K too small: S/64 rows
     ("f16", 8, 8192, 4096, 4096, {"workspace_stages": 2}, 16, 1),
