@@ -289,8 +289,11 @@ void ag_gemm_options_init(agg_options *opt);
  *              also 0 and K-blocks allowed (K a multiple of 4 KiB of
  *              elements, the counters scheme, no workspace ring or
  *              split-K), S/16 rows x one quarter of K (64 chunks per
- *              source); otherwise ag_gemm_pick_chunk_rows(S) rows x all of
- *              K.  agg_plan_info reports the choice.
+ *              source), or x one eighth of K (128 chunks per source) in a
+ *              pipelined call with three or more remote shards where K is
+ *              a multiple of 8 KiB of elements; otherwise
+ *              ag_gemm_pick_chunk_rows(S) rows x all of K.  agg_plan_info
+ *              reports the choice.
  * Requires K % 8 == 0 and N % 8 == 0 (AGG_E_UNSUPPORTED otherwise).
  * Size limits (both paths, AGG_E_UNSUPPORTED past them): n_shards <= 64,
  * S <= 2^30, K <= 2^21, N <= 2^20, at most 1024 chunks per shard, and one
