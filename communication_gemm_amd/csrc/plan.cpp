@@ -9,9 +9,10 @@ namespace agg {
 
 namespace {
 
-// K-blocks of the automatic 2-D chunks.
+// K-blocks of the automatic 2-D chunks: four, or eight for pipelined calls
+// with three or more remote sources (make_plan).
 constexpr int kAutoKBlocks = 4;
-constexpr int kAutoKBlocksPaced = 8;
+constexpr int kAutoKBlocksFine = 8;
 
 // Output tiles the consumer kernels are instantiated for, largest first.
 // Ids 1, 6, 7, 8 and 9 are the same 256 x 256 tile with different K
@@ -306,10 +307,11 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         // 153 GB/s, four K-blocks on every CU stayed ahead: 89.3-89.9
         // against 91.7 us.)
         const bool eight = opt->mode == AGG_MODE_PIPELINED && n_shards >= 4 &&
-                           K % (kAutoKBlocksPaced * kib) == 0;
-        const int nkb = eight ? kAutoKBlocksPaced : kAutoKBlocks;
+                           K % (kAutoKBlocksFine * kib) == 0;
+        const int nkb = eight ? kAutoKBlocksFine : kAutoKBlocks;
         // Automatic chunks where K-blocks are allowed: S/16 rows x a quarter
-        // of K, still 64 chunks per source (the PTO-ISA README's 64-128).
+        // of K, still 64 chunks per source (the PTO-ISA README's 64-128;
+        // 128 with eight K-blocks).
         // Measured against whole-K chunks of S/64 rows (interleaved, one
         // box): 147 against 176 us on 4 x 1024 rows at K = N = 4096 paced at
         // 153 GB/s per link, level (277 / 279 us, 40 / 39 us) on 8 x 1024
@@ -395,7 +397,7 @@ int make_plan(Kind kind, int n_shards, int64_t M, int64_t K, int64_t N,
         opt->producer != AGG_PRODUCER_SDMA && num_cus >= 4) {
         if (!(opt->link_gbps > 0.0))
             pw = num_cus / 2;
-        else if (s.nkb == kAutoKBlocksPaced && opt->k_block == 0 && chunk_rows == 0)
+        else if (s.nkb == kAutoKBlocksFine && opt->k_block == 0 && chunk_rows == 0)
             pw = num_cus / 4;
     }
     if (pw > items) pw = (int)(items > 0 ? items : 1);
