@@ -456,6 +456,18 @@ int run(const Call& c)
     pa.pieces = reinterpret_cast<uint32_t*>(ws + kPieceOffset);
     pa.piece = p.piece;
     pa.ppc = p.ppc;
+    // Piece flags (a chunk counts as released once each of its pieces is
+    // flagged, before the last piece's running-total add returns): for the
+    // producer kernel with at most kPieceFlags pieces a chunk, unpaced --
+    // a paced chunk must not be seen before its paced time, which only its
+    // chunk flag waits for -- and three or more remote sources, whose
+    // round-0 tiles wait for the first chunks (on 2 x 1024 rows, K 2048,
+    // N 1024 they cost 1 us a call).
+    const bool piece_flags = p.producer != AGG_PRODUCER_SDMA && p.ppc <= kPieceFlags &&
+                             !(p.link_gbps > 0) && c.n >= 4;
+    pa.piece_flags = piece_flags ? header + kPieceFlagOffset / 4 : nullptr;
+    ca.piece_flags = pa.piece_flags;
+    ca.ppc = p.ppc;
     pa.err = header + kErrorOffset / 4;
     pa.clock = reinterpret_cast<uint64_t*>(ws + kClockOffset);
     pa.epoch = epoch;

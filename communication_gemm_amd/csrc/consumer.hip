@@ -885,25 +885,46 @@ __device__ __forceinline__ void store_tile(
 // `need`, or the chunk flags of [have, need) all holding the call's epoch.
 // The counter moves only once the chunk before the first unflagged one is
 // flagged (and then in a compare-and-swap after a flag walk), so it lags the
-// flags; the flags alone cost one wave-wide load per 64 chunks.  Each poll
-// issues the counter load and the flag loads together: one memory round
-// trip.  A flag is stored only after its chunk's data (every piece of it,
-// whoever copied it) was performed in memory, and the counter passes a
-// chunk only after some wave saw its flag, so either vouches for the data.
-// Returns the chunks now known released (>= need), or 0 after a time-out or
-// a failure elsewhere in the call.
+// flags; the flags alone cost one wave-wide load per 64 chunks.  Where the
+// call keeps piece flags, a chunk whose pieces are all flagged counts as
+// released too (for the first 16 chunks of a poll: four lanes a chunk);
+// they come about two round trips before the chunk flag, which waits for
+// the last piece's running-total add to return.  Each poll issues the
+// counter load and the flag loads together: one memory round trip.  A
+// piece flag is stored only after its piece's data was performed in
+// memory, a chunk flag only after every piece of the chunk was, and the
+// counter passes a chunk only after some wave saw its flag, so each
+// vouches for the data.  Returns the chunks now known released (>= need),
+// or 0 after a time-out or a failure elsewhere in the call.  kPieces: look
+// at the piece flags too (the wait before a tile; inside the K loop the
+// registers the extra lanes' work takes are not there to spare, and the
+// chunk flags are in by then as a rule).
+template <bool kPieces>
 __device__ __forceinline__ uint32_t poll_ready(const ConsumerArgs& a, int shard, uint32_t have,
                                                uint32_t need, int tid)
 {
     const uint32_t base = a.base[shard];
     const uint32_t* ctr = a.counters + shard * (kCounterStride / 4);
     const uint32_t* fl = a.flags + shard * kFlagCap;
+    const uint32_t* pf =
+        kPieces && a.piece_flags ? a.piece_flags + shard * kFlagCap * kPieceFlags : nullptr;
     uint64_t t0 = 0;
     uint32_t spins = 0;
     for (;;) {
         const uint32_t c = load_agent(ctr);          // one request for the wave
         const uint32_t j = have + (uint32_t)tid;
-        const bool set = j >= need || load_agent(fl + j) == a.epoch;
+        bool set = j >= need || load_agent(fl + j) == a.epoch;
+        if (kPieces && pf) {
+            // lane 4i + q: piece q of chunk have + i
+            const uint32_t jp = have + (uint32_t)tid / kPieceFlags;
+            const uint32_t q = (uint32_t)tid % kPieceFlags;
+            const bool pset = jp >= need || q >= (uint32_t)a.ppc ||
+                              load_agent(pf + jp * kPieceFlags + q) == a.epoch;
+            uint64_t m = __builtin_amdgcn_ballot_w64(pset);
+            m &= m >> 1;
+            m &= m >> 2;                              // bit 4i: all of chunk have + i
+            set = set || (tid < 64 / kPieceFlags && ((m >> (kPieceFlags * tid)) & 1));
+        }
         const uint32_t cur = __builtin_amdgcn_readfirstlane(c) - base;
         if (cur >= need && cur <= (uint32_t)kFlagCap) return cur;
         const uint64_t unset = __builtin_amdgcn_ballot_w64(!set);
@@ -945,13 +966,14 @@ __device__ __forceinline__ uint32_t poll_ready(const ConsumerArgs& a, int shard,
 // call's consumer ended before this one started.  (The fence costs some
 // microseconds, and it empties the L2 of the panels every other workgroup
 // of the XCD is sharing: on entry there are none yet.)
+template <bool kPieces>
 __device__ __forceinline__ int wait_source(const ConsumerArgs& a, int shard, int need,
                                            uint32_t* seen, int tid, bool acquire)
 {
     const uint32_t have = seen[shard];
     uint32_t got = have;
     if (have < (uint32_t)need) {
-        got = poll_ready(a, shard, have, (uint32_t)need, tid);
+        got = poll_ready<kPieces>(a, shard, have, (uint32_t)need, tid);
         if (!got) return 0;
     }
     if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -979,7 +1001,7 @@ __device__ __forceinline__ int wait_counter(const ConsumerArgs& a, int shard, in
 {
     const uint32_t have = seen[shard];
     if (have >= (uint32_t)need) return 1;
-    const uint32_t got = poll_ready(a, shard, have, (uint32_t)need, tid);
+    const uint32_t got = poll_ready<false>(a, shard, have, (uint32_t)need, tid);
     if (!got) return 0;
     if (tid == 0) seen[shard] = got;
     return 1;
@@ -1090,6 +1112,10 @@ __device__ __forceinline__ void consume(const ConsumerArgs& a, uint32_t block, u
                                         ConsumerShared& sh, char* lds)
 {
     typedef Engine<T, BM, BN, SB, NS, WM, WN> E;
+    // the wait before a tile looks at piece flags on the 256-row tiles,
+    // whose round-0 waits the first chunks' release sets; the small tiles
+    // keep the plain wait (the extra loads cost them more than they gain)
+    constexpr bool kPieceWait = BM * BN >= 256 * 128;
     uint32_t* seen_sh = sh.seen;
     int& ok_sh = sh.ok;
     int& last_sh = sh.last;
@@ -1144,12 +1170,12 @@ __device__ __forceinline__ void consume(const ConsumerArgs& a, uint32_t block, u
                 if (s.pv > 0) {
                     // barrier scheme: the iteration's rows of every source
                     for (int q = 1; q < s.n_shards && ok; ++q)
-                        ok = wait_source(a, s.order[q], t.need, seen_sh, tid,
+                        ok = wait_source<kPieceWait>(a, s.order[q], t.need, seen_sh, tid,
                                          q == s.n_shards - 1 && (!acquired || s.ring > 0));
                 } else {
                     const int64_t pro = kb + (int64_t)(NS - 1) * E::kBK;
                     const int kb0 = kblock_of(s, (pro < ke ? pro : ke) - 1);
-                    ok = wait_source(a, t.shard, need_at(s, t.m, kb0), seen_sh, tid,
+                    ok = wait_source<kPieceWait>(a, t.shard, need_at(s, t.m, kb0), seen_sh, tid,
                                      !acquired || s.ring > 0);
                 }
                 if (tid == 0) ok_sh = ok;

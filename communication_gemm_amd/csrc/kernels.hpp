@@ -17,6 +17,7 @@ struct ProducerArgs {
     uint32_t* counters;            // header base; counter of shard i at i * 32
     uint32_t* flags;               // chunk flag matrix: [shard][kFlagCap]
     uint32_t* pieces;              // piece running totals: [shard][kFlagCap]
+    uint32_t* piece_flags;         // [shard][kFlagCap][kPieceFlags], or nullptr: none
     int ppc;                       // pieces per chunk (the last chunk's may be empty)
     int64_t piece;                 // bytes per piece, a multiple of kWaveSweepBytes
     uint32_t* err;
@@ -49,6 +50,8 @@ struct ConsumerArgs {
     void* C;
     uint32_t* counters;
     const uint32_t* flags;         // chunk flag matrix
+    const uint32_t* piece_flags;   // [shard][kFlagCap][kPieceFlags], or nullptr: none
+    int ppc;                       // pieces per chunk, with piece_flags
     uint32_t* err;
     uint32_t base[kMaxShards];
     uint32_t epoch;

@@ -227,7 +227,7 @@ __device__ __forceinline__ void produce(const ProducerArgs& a, uint32_t block, u
     // (Positions and total indices fit 32 bits: at most kMaxShards x
     // kFlagCap chunks.)
     int32_t pend = -1, cnt = -1;
-    uint32_t pend_total = 0, pend_w = 0, cnt_w = 0, old = 0;
+    uint32_t pend_total = 0, pend_w = 0, pend_q = 0, cnt_w = 0, old = 0;
 
     // The piece being copied: item chunk * ppc + q (producer position
     // `chunk`, piece q of it), stepped by `waves` items without dividing;
@@ -386,9 +386,15 @@ __device__ __forceinline__ void produce(const ProducerArgs& a, uint32_t block, u
             cnt = -1;
         }
         if (pend >= 0) {
-            if (lane == 0)
+            // the piece's stores are performed (the wait above): count it,
+            // and flag it where piece flags are kept
+            if (lane == 0) {
                 old = __hip_atomic_fetch_add(a.pieces + pend_total, pend_w, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
+                if (a.piece_flags && pend != a.drop)
+                    __hip_atomic_store(a.piece_flags + pend_total * kPieceFlags + pend_q, a.epoch,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             cnt = pend;
             cnt_w = pend_w;
             pend = -1;
@@ -422,6 +428,7 @@ __device__ __forceinline__ void produce(const ProducerArgs& a, uint32_t block, u
             pend = chunk;
             pend_total = total;
             pend_w = weight;
+            pend_q = q;
             chunk += step_c;
             q += step_q;
             if (q >= ppc) {
