@@ -26,8 +26,14 @@ def agg():
     return m
 
 
-def test_litmus_changing_contents_across_xcds(agg):
-    n, S, K = 4, 64, 1024
+@pytest.mark.parametrize("S,tile,iters", [
+    (64, 0, ITERS),
+    # 256 x 256 tiles: their wait takes a chunk whose pieces are all
+    # flagged (unpaced calls, three remote sources)
+    (256, 15, ITERS // 2),
+])
+def test_litmus_changing_contents_across_xcds(agg, S, tile, iters):
+    n, K = 4, 1024
     M = n * S
     ts = [torch.empty((S, K), dtype=torch.float16, device="cuda") for _ in range(n)]
     eye = torch.eye(K, dtype=torch.float16, device="cuda")
@@ -37,20 +43,20 @@ def test_litmus_changing_contents_across_xcds(agg):
     i = torch.arange(M, device="cuda", dtype=torch.int64)[:, None]
     k = torch.arange(K, device="cuda", dtype=torch.int64)[None, :]
     base = i * 7 + k * 13                       # integers, exact in fp16 below
-    bad = torch.zeros(ITERS, dtype=torch.int64, device="cuda")
+    bad = torch.zeros(iters, dtype=torch.int64, device="cuda")
     shapes = [dict(cr=1), dict(cr=3), dict(cr=16), dict(cr=8, k_block=512),
               dict(cr=1, k_block=512), dict(cr=0)]
     extras = [dict(), dict(link_gbps=100.0), dict(debug_delay_us=15.0)]
     opts = []
-    for it in range(ITERS):
+    for it in range(iters):
         sh = dict(shapes[it % len(shapes)])
         ex = dict(extras[(it // len(shapes)) % len(extras)])
         if "debug_delay_us" in ex:
             ex["debug_delay_seed"] = it
         cr = sh.pop("cr")
-        opts.append((cr, agg.options(workspace=ws, **sh, **ex), sh, ex))
+        opts.append((cr, agg.options(workspace=ws, tile=tile, **sh, **ex), sh, ex))
     checked = 0
-    for it in range(ITERS):
+    for it in range(iters):
         A = ((base + it * 101) % 2047 - 1023).to(torch.float16)
         for s in range(n):
             ts[s].copy_(A[s * S:(s + 1) * S])
@@ -58,7 +64,7 @@ def test_litmus_changing_contents_across_xcds(agg):
         cr, o, sh, ex = opts[it]
         agg.ag_gemm_f16(ts, eye, C, cr, opts=o)
         bad[it] = (C != A.float()).sum()
-        if it % 200 == 199 or it == ITERS - 1:
+        if it % 200 == 199 or it == iters - 1:
             rc = agg.check()
             assert rc == 0, f"call {it}: {agg.status_string(rc)}"
             b = bad[:it + 1].nonzero()
@@ -66,4 +72,4 @@ def test_litmus_changing_contents_across_xcds(agg):
                 f"first mismatch at call {int(b[0])}: {int(bad[int(b[0])])} elements; "
                 f"options {opts[int(b[0])][2]} {opts[int(b[0])][3]}")
             checked = it + 1
-    assert checked == ITERS
+    assert checked == iters
