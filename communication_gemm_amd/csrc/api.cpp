@@ -458,13 +458,13 @@ int run(const Call& c)
     pa.ppc = p.ppc;
     // Piece flags (a chunk counts as released once each of its pieces is
     // flagged, before the last piece's running-total add returns): for the
-    // producer kernel with at most kPieceFlags pieces a chunk, unpaced --
-    // a paced chunk must not be seen before its paced time, which only its
-    // chunk flag waits for -- and three or more remote sources, whose
-    // round-0 tiles wait for the first chunks (on 2 x 1024 rows, K 2048,
-    // N 1024 they cost 1 us a call).
+    // producer kernel with at most kPieceFlags pieces a chunk and three or
+    // more remote sources, whose round-0 tiles wait for the first chunks (on
+    // 2 x 1024 rows, K 2048, N 1024 they cost 1 us a call).  Paced, the
+    // consumer takes a piece-flagged chunk only once the chunk's paced time
+    // has passed (parallel links: a source's own bytes set it).
     const bool piece_flags = p.producer != AGG_PRODUCER_SDMA && p.ppc <= kPieceFlags &&
-                             !(p.link_gbps > 0) && c.n >= 4;
+                             c.n >= 4 && !(p.link_gbps > 0 && s.link_model != 0);
     pa.piece_flags = piece_flags ? header + kPieceFlagOffset / 4 : nullptr;
     ca.piece_flags = pa.piece_flags;
     ca.ppc = p.ppc;
@@ -476,6 +476,15 @@ int run(const Call& c)
     pa.delay_seed = opt->debug_delay_seed;
     pa.delay_max = (uint32_t)(opt->debug_delay_us * 1e-6 * d->clock_hz);
     pa.ticks_per_byte = p.link_gbps > 0 ? d->clock_hz / (p.link_gbps * 1e9) : 0.0;
+    {
+        // the paced time a consumer gives a piece-flagged chunk is never
+        // earlier than the chunk flag's: whole KiB and ticks per KiB both
+        // rounded up, one tick added
+        const double q = std::ceil(pa.ticks_per_byte * p.elt * 1024.0 * 65536.0);
+        ca.ticks_per_kib_q16 =
+            p.link_gbps > 0 ? (q < 4294967295.0 && q >= 1.0 ? (uint32_t)q : 0xffffffffu) : 0;
+        ca.clock = pa.clock;
+    }
     pa.limit = limit;
     // the producer's wait for the consumer's start covers the work queued
     // ahead of the call on the caller's stream, not a chunk: its own bound

@@ -879,6 +879,26 @@ __device__ __forceinline__ void store_tile(
     store_tile_as<T, BM, BN, WM, WN, false>(a, shard, m, n, acc);
 }
 
+// Paced calls: whether chunk j of a source (K-block j / rcs, row group
+// j % rcs) is past its paced time, the time the emulated link could have
+// carried the source's bytes up to and including it (parallel links),
+// measured from this call's pacing origin; false while the producer has
+// not set the origin yet.  The bytes are counted in whole KiB of elements,
+// rounded up, as the ticks per KiB are: never earlier than the chunk flag's
+// own paced time.
+__device__ __forceinline__ bool paced_time_passed(const ConsumerArgs& a, uint32_t j)
+{
+    const uint64_t slot = __hip_atomic_load(a.clock, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t mask = (1ull << 40) - 1;
+    if ((slot >> 40) != (uint64_t)(a.epoch & 0xffffffu)) return false;
+    const Schedule& s = a.s;
+    const int kb = (int)(j / (uint32_t)s.rcs), jr = (int)(j % (uint32_t)s.rcs);
+    const int64_t k0 = kblock_begin(s, kb);
+    const int64_t elts = k0 * s.S + chunk_row_end(s, jr) * (kblock_end(s, kb) - k0);
+    const uint64_t due = ((uint64_t)((elts + 1023) >> 10) * a.ticks_per_kib_q16 >> 16) + 1;
+    return ((ticks() - (slot & mask)) & mask) >= due;
+}
+
 // Wave 0 of a workgroup: wait until chunks [0, need) of source `shard` are
 // known released, `have` of them known already.  Either of the PTO-ISA
 // README's two structures says so: the source's summary counter covering
@@ -918,8 +938,10 @@ __device__ __forceinline__ uint32_t poll_ready(const ConsumerArgs& a, int shard,
             // lane 4i + q: piece q of chunk have + i
             const uint32_t jp = have + (uint32_t)tid / kPieceFlags;
             const uint32_t q = (uint32_t)tid % kPieceFlags;
-            const bool pset = jp >= need || q >= (uint32_t)a.ppc ||
-                              load_agent(pf + jp * kPieceFlags + q) == a.epoch;
+            bool pset = jp >= need || q >= (uint32_t)a.ppc ||
+                        load_agent(pf + jp * kPieceFlags + q) == a.epoch;
+            if (a.ticks_per_kib_q16 && jp < need)
+                pset = pset && paced_time_passed(a, jp);
             uint64_t m = __builtin_amdgcn_ballot_w64(pset);
             m &= m >> 1;
             m &= m >> 2;                              // bit 4i: all of chunk have + i
@@ -1112,10 +1134,12 @@ __device__ __forceinline__ void consume(const ConsumerArgs& a, uint32_t block, u
                                         ConsumerShared& sh, char* lds)
 {
     typedef Engine<T, BM, BN, SB, NS, WM, WN> E;
-    // the wait before a tile looks at piece flags on the 256-row tiles,
-    // whose round-0 waits the first chunks' release sets; the small tiles
-    // keep the plain wait (the extra loads cost them more than they gain)
-    constexpr bool kPieceWait = BM * BN >= 256 * 128;
+    // the wait before a tile looks at piece flags on the large eight-wave
+    // tiles, whose round-0 waits the first chunks' release sets; the small
+    // tiles keep the plain wait (the extra loads cost them more than they
+    // gain), and so do the four-wave 256 x 256 ones and the int8 ones, whose
+    // accumulators (in AGPRs for int8) leave no registers for it
+    constexpr bool kPieceWait = BM * BN >= 256 * 128 && E::kWaves == 8 && !T::kDequant;
     uint32_t* seen_sh = sh.seen;
     int& ok_sh = sh.ok;
     int& last_sh = sh.last;

@@ -52,6 +52,11 @@ struct ConsumerArgs {
     const uint32_t* flags;         // chunk flag matrix
     const uint32_t* piece_flags;   // [shard][kFlagCap][kPieceFlags], or nullptr: none
     int ppc;                       // pieces per chunk, with piece_flags
+    // paced calls with piece flags: a piece-flagged chunk counts only once
+    // its paced time (clock ticks per 1024 elements, 16 fraction bits,
+    // rounded up) has passed since the pacing origin in *clock; 0: unpaced
+    uint32_t ticks_per_kib_q16;
+    const uint64_t* clock;
     uint32_t* err;
     uint32_t base[kMaxShards];
     uint32_t epoch;

@@ -300,6 +300,7 @@ __device__ __forceinline__ void produce(const ProducerArgs& a, uint32_t block, u
         const int64_t k0 = kblock_begin(s, r.kb);
         const int64_t sb = (kblock_end(s, r.kb) - k0) * a.elt;   // bytes per row segment
         const int64_t bytes = rows * sb;
+
         const int64_t begin = q * a.piece;
         const int64_t end = begin + a.piece < bytes ? begin + a.piece : bytes;
         // an empty piece of a short last chunk copies nothing but counts
@@ -391,6 +392,8 @@ __device__ __forceinline__ void produce(const ProducerArgs& a, uint32_t block, u
             if (lane == 0) {
                 old = __hip_atomic_fetch_add(a.pieces + pend_total, pend_w, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
+                // (paced calls: the consumer takes a piece-flagged chunk
+                // only once the chunk's paced time has passed)
                 if (a.piece_flags && pend != a.drop)
                     __hip_atomic_store(a.piece_flags + pend_total * kPieceFlags + pend_q, a.epoch,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

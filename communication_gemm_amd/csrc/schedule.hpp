@@ -53,10 +53,12 @@ constexpr int kTicketOffset = kStageOffset + kMaxShards * kMaxStages * 8;
 constexpr int kMaxSplitTiles = 4096;
 // Piece flags: one 32-bit word per source, chunk and piece (at most
 // kPieceFlags pieces a chunk), the epoch of the call whose piece's stores
-// were performed.  Unpaced calls with three or more remote sources whose
-// chunks have at most kPieceFlags pieces store them, and a consumer may
-// take a chunk whose piece flags are all set as released, without waiting
-// for the chunk flag that the last piece's running-total add leads to.
+// were performed.  Calls with three or more remote sources whose chunks
+// have at most kPieceFlags pieces store them (not with one serial paced
+// link), and a consumer may take a chunk whose piece flags are all set as
+// released -- in a paced call once the chunk's paced time has passed --
+// without waiting for the chunk flag that the last piece's running-total
+// add leads to.
 constexpr int kPieceFlags = 4;
 constexpr int kPieceFlagOffset = kTicketOffset + kMaxSplitTiles * 4;
 constexpr int kHeaderBytes = kPieceFlagOffset + kMaxShards * kFlagCap * kPieceFlags * 4;
