@@ -300,7 +300,6 @@ __device__ __forceinline__ void produce(const ProducerArgs& a, uint32_t block, u
         const int64_t k0 = kblock_begin(s, r.kb);
         const int64_t sb = (kblock_end(s, r.kb) - k0) * a.elt;   // bytes per row segment
         const int64_t bytes = rows * sb;
-
         const int64_t begin = q * a.piece;
         const int64_t end = begin + a.piece < bytes ? begin + a.piece : bytes;
         // an empty piece of a short last chunk copies nothing but counts
