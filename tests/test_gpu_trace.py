@@ -130,3 +130,40 @@ def test_trace_buffer_must_hold_the_calls_plan(agg):
     assert agg.check() == 0
     tr = trace.cpu().numpy()
     assert (tr[:auto.trace_words] > 0).all() and tr[auto.trace_words] == 0
+
+
+def test_paced_piece_flags_keep_the_pace(agg):
+    """A paced call on 256 x 256 tiles, whose waits take piece-flagged
+    chunks: no remote tile gets past its first wait before the emulated
+    link could have carried the rows it needs (the source's bytes up to
+    and including its K-block 0 chunk of the panel's last row group),
+    counted from the consumer's start -- the pacing origin is the first
+    producer workgroup's start, no earlier -- and the result is exact."""
+    n, S, K, N, gbps = 4, 1024, 4096, 512, 20.0
+    M = n * S
+    shards, B = synth.make_f16(M, K, N, n, "normal", 60030)
+    ts = [dev(s, torch) for s in shards]
+    tB = dev(B, torch)
+    opts = dict(link_gbps=gbps, tile=15)
+    info, tiles, chunks = agg.plan("f16", n, M, K, N, 0, agg.options(**opts), orders=True)
+    assert info.k_blocks == 8 and info.tile_id == 15
+    trace = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
+    C = torch.empty((M, N), device="cuda")
+    agg.ag_gemm_f16(ts, tB, C, 0, opts=agg.options(trace=trace, **opts))
+    assert agg.check() == 0
+    ref = torch.empty_like(C)
+    agg.ag_gemm_f16(ts, tB, ref, 64)           # whole-K chunks, no piece flags
+    assert agg.check() == 0
+    assert torch.equal(C, ref)
+    tr = trace.cpu().numpy().view(np.uint64).astype(np.float64)
+    start, cons = tr[0], tr[1 + info.total_chunks:].reshape(-1, 3)
+    cr, kbk = info.chunk_rows, info.k_block
+    remote = 0
+    for p, (shard, m, nn, need) in enumerate(tiles):
+        if need <= 0:
+            continue
+        remote += 1
+        row_end = min(int(need) * cr, S)       # the panel's last row group, K-block 0
+        paced_s = row_end * kbk * 2 / (gbps * 1e9)
+        assert (cons[p, 1] - start) / 1e8 >= paced_s, (p, shard, m, paced_s)
+    assert remote > 0
